@@ -1,0 +1,397 @@
+/*
+ * pkv_oracle.c -- TEST INFRASTRUCTURE, NOT PRODUCT CODE.
+ *
+ * A plain, slow, obviously correct host implementation of paged-KV-cache
+ * store and attention, in fp64.  It exists only so that tests, the smoke
+ * check and the benchmark's CPU-baseline leg can judge the GPU kernels.  It
+ * shares no code, header, table or helper with the GPU library and includes
+ * nothing from it; the product path never calls it.
+ *
+ * Pages it follows (titles as printed on the pages):
+ *   [NV2]  "Nano-vLLM Part 2: model internals, KV cache and tensor
+ *          parallelism" (seekfood.cn/news/749872)
+ *   [NVE]  "Nano-vLLM engine deep-dive: from 'it runs' to 'it runs well'"
+ *          (mhpq.cn/news/130328)
+ *   [LLM4] "LLM basics primer: from text to token, embedding, QKV and
+ *          Transformer, part 4" (CSDN; qwbw.cn/news/156881)
+ *
+ * Layouts (the pages name the dimensions Block / Layer / K-V / Token in
+ * [NV2] §05.2 but not their order; this is the reading taken):
+ *   k_cache, v_cache : bf16 bits [num_blocks][num_kv_heads][block_size][head_dim]
+ *                      (one array per layer and per K/V)
+ *   k, v (new)       : bf16 bits [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping     : int32 [num_tokens]; slot = block * block_size + offset,
+ *                      slot < 0 means "no token here" (padding)
+ *   q (decode)       : bf16 bits [num_seqs][num_q_heads][head_dim]
+ *   q (prefill)      : bf16 bits [total_new][num_q_heads][head_dim], prompts packed
+ *   block_tables     : int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens     : int32 [num_seqs], tokens in the cache AFTER the store
+ *   out              : double [rows][num_q_heads][head_dim]
+ *
+ * Parity pins for every function live in tests/ (see the test file for the
+ * list); none of them compares this file with itself.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+#include "pkv_oracle.h"
+
+/* A bf16 value is the upper 16 bits of an IEEE binary32; widen, then to double. */
+static double bf16_bits_to_double(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * KV-cache bytes: 2 (one K and one V) x layers x KV heads (not query heads)
+ * x head_dim x cached tokens x bytes per element.
+ * [LLM4] §17.3 (general formula, "2 means K and V", "num_kv_heads is the KV
+ * head count, not the Q head count") and §17.6 (cached_tokens is the sum of
+ * every request's cached tokens).
+ */
+uint64_t pko_kv_bytes(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                      int64_t cached_tokens, int32_t bytes_per_element)
+{
+    if (num_layers < 0 || num_kv_heads < 0 || head_dim < 0 || cached_tokens < 0 ||
+        bytes_per_element < 0)
+        return 0;
+    return (uint64_t)2 * (uint64_t)num_layers * (uint64_t)num_kv_heads *
+           (uint64_t)head_dim * (uint64_t)cached_tokens * (uint64_t)bytes_per_element;
+}
+
+/*
+ * Store: each new token's K and V go to the cache position its slot names.
+ * [NVE] §2.1 (decode appends the new token's K and V to the cache), §2.2
+ * (fixed-size blocks, managed "by block or by slot"); [NV2] §05.3 (a kernel
+ * writes new K/V into the cache).  A slot below zero is skipped.  Slots that
+ * repeat within one call, or that fall outside the pool, are rejected before
+ * anything is written.
+ */
+int pko_store(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
+              int32_t num_tokens, uint16_t *k_cache, uint16_t *v_cache,
+              int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size)
+{
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0)
+        return PKO_ERR_ARG;
+    if (num_tokens == 0)
+        return PKO_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+        return PKO_ERR_ARG;
+
+    int64_t num_slots = (int64_t)num_blocks * block_size;
+    unsigned char *seen = calloc((size_t)(num_slots > 0 ? num_slots : 1), 1);
+    if (!seen)
+        return PKO_ERR_ALLOC;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        int32_t slot = slot_mapping[i];
+        if (slot < 0)
+            continue;
+        if ((int64_t)slot >= num_slots) {
+            free(seen);
+            return PKO_ERR_RANGE;
+        }
+        if (seen[slot]) {
+            free(seen);
+            return PKO_ERR_DUPLICATE;
+        }
+        seen[slot] = 1;
+    }
+    free(seen);
+
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        int32_t slot = slot_mapping[i];
+        if (slot < 0)
+            continue;
+        int64_t block = slot / block_size;
+        int64_t offset = slot % block_size;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            for (int32_t x = 0; x < head_dim; ++x) {
+                int64_t src = ((int64_t)i * num_kv_heads + h) * head_dim + x;
+                int64_t dst = ((block * num_kv_heads + h) * block_size + offset) * head_dim + x;
+                k_cache[dst] = k[src];
+                v_cache[dst] = v[src];
+            }
+        }
+    }
+    return PKO_OK;
+}
+
+/*
+ * One query row against keys 0..n-1 of one sequence, read through its block
+ * table:  out = softmax(scale * q . K^T) V, the scaled dot-product attention
+ * of [NVE] §3 and [LLM4] §21.1, computed as its definition in fp64:
+ *   score_t = scale * sum_x q[x] * K_t[x]
+ *   M = max_t score_t          (the max subtraction of [NVE] §3.2)
+ *   w_t = exp(score_t - M),  Z = sum_t w_t
+ *   out[x] = sum_t w_t * V_t[x] / Z
+ * Token t of the sequence lives in physical block block_table[t / block_size]
+ * at offset t % block_size ([NVE] §2.2, [LLM4] §17.7 block table).  The K/V
+ * head is the query head's group: kv = h / (num_q_heads / num_kv_heads)
+ * ([LLM4] §21.1: grouped-query attention shares KV heads).  n == 0 gives 0.
+ */
+static void attend_one(const uint16_t *q_row, const uint16_t *k_cache,
+                       const uint16_t *v_cache, const int32_t *block_table,
+                       int32_t n, int32_t kv_head, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, double scale,
+                       double *scores, double *out_row)
+{
+    for (int32_t x = 0; x < head_dim; ++x)
+        out_row[x] = 0.0;
+    if (n <= 0)
+        return;
+
+    for (int32_t t = 0; t < n; ++t) {
+        int64_t block = block_table[t / block_size];
+        int64_t offset = t % block_size;
+        const uint16_t *key =
+            k_cache + ((block * num_kv_heads + kv_head) * block_size + offset) * head_dim;
+        double dot = 0.0;
+        for (int32_t x = 0; x < head_dim; ++x)
+            dot += bf16_bits_to_double(q_row[x]) * bf16_bits_to_double(key[x]);
+        scores[t] = scale * dot;
+    }
+
+    double m = scores[0];
+    for (int32_t t = 1; t < n; ++t)
+        if (scores[t] > m)
+            m = scores[t];
+
+    double z = 0.0;
+    for (int32_t t = 0; t < n; ++t) {
+        scores[t] = exp(scores[t] - m);
+        z += scores[t];
+    }
+
+    for (int32_t t = 0; t < n; ++t) {
+        int64_t block = block_table[t / block_size];
+        int64_t offset = t % block_size;
+        const uint16_t *value =
+            v_cache + ((block * num_kv_heads + kv_head) * block_size + offset) * head_dim;
+        for (int32_t x = 0; x < head_dim; ++x)
+            out_row[x] += scores[t] * bf16_bits_to_double(value[x]);
+    }
+    for (int32_t x = 0; x < head_dim; ++x)
+        out_row[x] /= z;
+}
+
+/* ---- a minimal static thread split over independent (sequence, kv head) units ---- */
+
+typedef struct {
+    int mode; /* 0 = decode, 1 = prefill */
+    const uint16_t *q, *k_cache, *v_cache;
+    const int32_t *block_tables, *context_lens, *cu_new_lens;
+    int32_t max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
+    double scale;
+    double *out;
+    int32_t max_context_len;
+    int nthreads, tid;
+    int status;
+} work_t;
+
+static void run_unit(work_t *w, int32_t s, int32_t kvh, double *scores)
+{
+    int32_t group = w->num_q_heads / w->num_kv_heads;
+    const int32_t *bt = w->block_tables + (int64_t)s * w->max_blocks_per_seq;
+    int32_t ctx = w->context_lens[s];
+    for (int32_t g = 0; g < group; ++g) {
+        int32_t h = kvh * group + g;
+        if (w->mode == 0) {
+            const uint16_t *q_row = w->q + ((int64_t)s * w->num_q_heads + h) * w->head_dim;
+            double *o = w->out + ((int64_t)s * w->num_q_heads + h) * w->head_dim;
+            attend_one(q_row, w->k_cache, w->v_cache, bt, ctx, kvh, w->num_kv_heads,
+                       w->head_dim, w->block_size, w->scale, scores, o);
+        } else {
+            /* Chunked causal prefill: prompt s has n new tokens after c cached
+             * ones (c = ctx - n); new token i sits at position c + i and sees
+             * keys 0..c+i inclusive -- it sees itself and what came before,
+             * never what follows ([NVE] §3.2 causal mask; [LLM4] §22 steps 6-8,
+             * where the middle token attends to the first and itself and the
+             * later token's weight is exactly 0). */
+            int32_t row0 = w->cu_new_lens[s];
+            int32_t n = w->cu_new_lens[s + 1] - row0;
+            int32_t c = ctx - n;
+            for (int32_t i = 0; i < n; ++i) {
+                const uint16_t *q_row =
+                    w->q + ((int64_t)(row0 + i) * w->num_q_heads + h) * w->head_dim;
+                double *o = w->out + ((int64_t)(row0 + i) * w->num_q_heads + h) * w->head_dim;
+                attend_one(q_row, w->k_cache, w->v_cache, bt, c + i + 1, kvh,
+                           w->num_kv_heads, w->head_dim, w->block_size, w->scale, scores, o);
+            }
+        }
+    }
+}
+
+static void *thread_main(void *arg)
+{
+    work_t *w = (work_t *)arg;
+    double *scores = malloc(sizeof(double) * (size_t)(w->max_context_len > 0 ? w->max_context_len : 1));
+    if (!scores) {
+        w->status = PKO_ERR_ALLOC;
+        return NULL;
+    }
+    int64_t units = (int64_t)w->num_seqs * w->num_kv_heads;
+    for (int64_t u = w->tid; u < units; u += w->nthreads)
+        run_unit(w, (int32_t)(u / w->num_kv_heads), (int32_t)(u % w->num_kv_heads), scores);
+    free(scores);
+    return NULL;
+}
+
+int pko_default_threads(void)
+{
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+static int run_threads(work_t *proto, int nthreads)
+{
+    if (nthreads <= 0)
+        nthreads = pko_default_threads();
+    int64_t units = (int64_t)proto->num_seqs * proto->num_kv_heads;
+    if (units < nthreads)
+        nthreads = units > 0 ? (int)units : 1;
+    work_t *ws = calloc((size_t)nthreads, sizeof(work_t));
+    pthread_t *th = calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!ws || !th) {
+        free(ws);
+        free(th);
+        return PKO_ERR_ALLOC;
+    }
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        ws[t] = *proto;
+        ws[t].nthreads = nthreads;
+        ws[t].tid = t;
+        ws[t].status = PKO_OK;
+        if (t == 0)
+            continue;
+        if (pthread_create(&th[t], NULL, thread_main, &ws[t]) != 0)
+            break;
+        started = t;
+    }
+    /* threads 1..started run in parallel; thread 0's share runs here, and any
+     * share whose thread failed to start runs here too */
+    thread_main(&ws[0]);
+    for (int t = started + 1; t < nthreads; ++t)
+        thread_main(&ws[t]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(th[t], NULL);
+    int status = PKO_OK;
+    for (int t = 0; t < nthreads; ++t)
+        if (ws[t].status != PKO_OK)
+            status = ws[t].status;
+    free(ws);
+    free(th);
+    return status;
+}
+
+static int check_common(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        const int32_t *block_tables, const int32_t *context_lens,
+                        int32_t num_blocks, int32_t *max_ctx_out)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+        return PKO_ERR_ARG;
+    if (num_q_heads % num_kv_heads != 0)
+        return PKO_ERR_ARG;
+    int32_t max_ctx = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int32_t ctx = context_lens[s];
+        if (ctx < 0 || (int64_t)ctx > (int64_t)max_blocks_per_seq * block_size)
+            return PKO_ERR_RANGE;
+        int32_t used = (ctx + block_size - 1) / block_size;
+        for (int32_t b = 0; b < used; ++b) {
+            int32_t id = block_tables[(int64_t)s * max_blocks_per_seq + b];
+            if (id < 0 || id >= num_blocks)
+                return PKO_ERR_RANGE;
+        }
+        if (ctx > max_ctx)
+            max_ctx = ctx;
+    }
+    *max_ctx_out = max_ctx;
+    return PKO_OK;
+}
+
+int pko_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+               int32_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
+               const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+               double *out, int nthreads)
+{
+    int32_t max_ctx = 0;
+    if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out))
+        return PKO_ERR_ARG;
+    int rc = check_common(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, block_tables, context_lens, num_blocks, &max_ctx);
+    if (rc != PKO_OK || num_seqs == 0)
+        return rc;
+    work_t w;
+    memset(&w, 0, sizeof w);
+    w.mode = 0;
+    w.q = q;
+    w.k_cache = k_cache;
+    w.v_cache = v_cache;
+    w.block_tables = block_tables;
+    w.context_lens = context_lens;
+    w.max_blocks_per_seq = max_blocks_per_seq;
+    w.num_seqs = num_seqs;
+    w.num_q_heads = num_q_heads;
+    w.num_kv_heads = num_kv_heads;
+    w.head_dim = head_dim;
+    w.block_size = block_size;
+    w.scale = (double)scale;
+    w.out = out;
+    w.max_context_len = max_ctx;
+    return run_threads(&w, nthreads);
+}
+
+int pko_prefill(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                int32_t num_blocks, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                const int32_t *cu_new_lens, const int32_t *context_lens, int32_t num_seqs,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size, float scale, double *out, int nthreads)
+{
+    int32_t max_ctx = 0;
+    if (num_seqs > 0 && (!q || !k_cache || !v_cache || !block_tables || !context_lens ||
+                         !cu_new_lens || !out))
+        return PKO_ERR_ARG;
+    int rc = check_common(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, block_tables, context_lens, num_blocks, &max_ctx);
+    if (rc != PKO_OK || num_seqs == 0)
+        return rc;
+    if (cu_new_lens[0] != 0)
+        return PKO_ERR_ARG;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int32_t n = cu_new_lens[s + 1] - cu_new_lens[s];
+        if (n < 0 || n > context_lens[s])
+            return PKO_ERR_ARG;
+    }
+    work_t w;
+    memset(&w, 0, sizeof w);
+    w.mode = 1;
+    w.q = q;
+    w.k_cache = k_cache;
+    w.v_cache = v_cache;
+    w.block_tables = block_tables;
+    w.context_lens = context_lens;
+    w.cu_new_lens = cu_new_lens;
+    w.max_blocks_per_seq = max_blocks_per_seq;
+    w.num_seqs = num_seqs;
+    w.num_q_heads = num_q_heads;
+    w.num_kv_heads = num_kv_heads;
+    w.head_dim = head_dim;
+    w.block_size = block_size;
+    w.scale = (double)scale;
+    w.out = out;
+    w.max_context_len = max_ctx;
+    return run_threads(&w, nthreads);
+}

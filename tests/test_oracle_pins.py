@@ -1,0 +1,10 @@
+"""The fp64 oracle against values, closed forms, library routines and
+invariants fixed outside it (CPU only)."""
+import pytest
+
+import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(orc, pin):
+    pin(orc)
