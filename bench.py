@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark: paged-KV decode step (store + split-KV decode attention) on one GPU.
+
+Workload (default): the Mistral-7B-style GQA batch -- 32 sequences x 4096
+cached tokens, 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks,
+32 independent layer pools (16 GiB of KV).  One step = for each of the 32
+layers: store the new token of every sequence (slot mapping), then decode
+attention over the whole cache.  Inputs are synthetic N(0,1) values rounded to
+bf16 and a seeded random physical-block permutation, resident in HBM before
+the timed region.
+
+Prints ONE JSON line.  ``value`` is the decode attention's KV read rate over
+the whole step (algorithmic KV bytes of all layers / step time), in GB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-iters", type=int, default=5)
+    return ap.parse_args()
+
+
+def decode_bytes(wl) -> int:
+    """Algorithmic bytes one decode launch must move: every cached K and V
+    element once, q in, out back, the live block-table entries and lengths."""
+    ctx = wl.context_lens.astype(np.int64)
+    kv = int(ctx.sum()) * 2 * wl.num_kv_heads * wl.head_dim * 2
+    qo = 2 * wl.num_seqs * wl.num_q_heads * wl.head_dim * 2
+    table = 4 * int(((ctx + wl.block_size - 1) // wl.block_size).sum()) + 4 * wl.num_seqs
+    return kv + qo + table
+
+
+def store_bytes(wl) -> int:
+    """Store: read and write each new token's K and V, plus its slot."""
+    live = int((wl.slot_mapping >= 0).sum())
+    return live * (2 * 2 * wl.num_kv_heads * wl.head_dim * 2) + 4 * wl.num_tokens
+
+
+def prefill_flops(wl) -> float:
+    """Causal pairs only: query i of prompt p sees c_p + i + 1 keys; 4 d flops
+    per (query head, key) pair (Q K^T and P V)."""
+    tot = 0
+    for p in range(wl.num_seqs):
+        n = int(wl.new_lens[p])
+        c = int(wl.context_lens[p]) - n
+        tot += n * c + n * (n + 1) // 2
+    return 4.0 * wl.head_dim * wl.num_q_heads * tot
+
+
+def cpu_baseline(wl, t, seconds):
+    """Time the fp64 oracle (as it stands) on whole layers of the same workload:
+    host copies of one layer's pools, store + decode, repeated until about
+    ``seconds`` of CPU time; tokens/s per layer = sequences / time per layer."""
+    import torch  # noqa: F401
+
+    import oracle
+    from paged_kv_cache_pools_amd import workloads as W
+
+    orc = oracle.get()
+    threads = orc.default_threads()
+    q = W.bf16_bits(t["q"][0])
+    kn = W.bf16_bits(t["k_new"][0])
+    vn = W.bf16_bits(t["v_new"][0])
+    layers_done, spent = 0, 0.0
+    while True:
+        kc = W.bf16_bits(t["k_caches"][layers_done % len(t["k_caches"])]).copy()
+        vc = W.bf16_bits(t["v_caches"][layers_done % len(t["v_caches"])]).copy()
+        t0 = time.perf_counter()
+        orc.store(kn, vn, wl.slot_mapping, kc, vc)
+        orc.decode(q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, nthreads=threads)
+        spent += time.perf_counter() - t0
+        layers_done += 1
+        del kc, vc
+        if spent >= seconds or layers_done >= 64:
+            break
+    per_layer = spent / layers_done
+    return {
+        "value": wl.num_seqs / per_layer, "unit": "tokens/s per layer", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{layers_done} whole layer(s) of the same batch (store + decode, "
+                  f"{wl.num_seqs} seqs x {wl.max_context_len} tokens), fp64 C oracle, "
+                  f"{per_layer * 1e3:.1f} ms per layer",
+        "kv_gbs": decode_bytes(wl) / per_layer / 1e9,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from paged_kv_cache_pools_amd import binding as B
+    from paged_kv_cache_pools_amd import workloads as W
+
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = args.layers
+    wl = W.mistral_gqa(seed=args.seed, num_layers=L)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+
+    def randn_bf16(shape):
+        return W._randn_bf16(torch, shape, gen, dev)
+
+    S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    t = {
+        "q": [randn_bf16((S, Hq, D)) for _ in range(L)],
+        "k_new": [randn_bf16((S, Hkv, D)) for _ in range(L)],
+        "v_new": [randn_bf16((S, Hkv, D)) for _ in range(L)],
+        "k_caches": [randn_bf16((wl.num_blocks, Hkv, 16, D)) for _ in range(L)],
+        "v_caches": [randn_bf16((wl.num_blocks, Hkv, 16, D)) for _ in range(L)],
+    }
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    ctx = torch.from_numpy(wl.context_lens).to(dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    outs = [torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    P = args.partition_tokens or B.pkv_decode_partition_tokens(S, Hkv, wl.max_context_len)
+    ws = torch.empty(max(16, B.pkv_decode_workspace_bytes(S, Hq, D, wl.max_context_len, P)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(L)]
+
+    def step(record=False):
+        for l in range(L):
+            B.pkv_store(t["k_new"][l], t["v_new"][l], slots, t["k_caches"][l], t["v_caches"][l])
+            if record:
+                ev[l][0].record(stream)
+            B.pkv_decode_attn(t["q"][l], t["k_caches"][l], t["v_caches"][l], bt, ctx, wl.scale,
+                              outs[l], max_context_len=wl.max_context_len, workspace=ws,
+                              partition_tokens=P)
+            if record:
+                ev[l][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dec_ms = []
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(record=True)
+        # per-launch decode durations of this step (read after the final sync)
+        dec_ms.append(list(ev))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(L)]
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    per_launch = [a.elapsed_time(b) for step_ev in dec_ms for a, b in step_ev]
+    dec_avg_ms = float(np.mean(per_launch))
+    ms_per_step = total_ms / args.steps
+
+    dbytes = decode_bytes(wl)
+    sbytes = store_bytes(wl)
+    kv_bytes_step = L * (dbytes + sbytes)
+    value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
+    achieved = dbytes / (dec_avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode attention KV GB/s and % of MI355X HBM peak; tokens/s per layer",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16, seeded random physical-block permutation",
+        "config": {"workload": "Mistral-7B-style GQA decode: 32 seqs x 4096 tokens, 32q/8kv "
+                               "heads, d 128, 16-token blocks, 32 layer pools, store + decode",
+                   "num_seqs": S, "context_len": int(wl.max_context_len), "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": 16, "layers": L,
+                   "partition_tokens": P},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
+        "decode_us_per_layer": round(dec_avg_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "pkv_decode_attn (split + reduce)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": dbytes},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(args, torch, B, W, dev)
+
+    if not args.no_cpu_baseline:
+        host = {"q": [t["q"][0]], "k_new": [t["k_new"][0]], "v_new": [t["v_new"][0]],
+                "k_caches": t["k_caches"][:2], "v_caches": t["v_caches"][:2]}
+        result["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args, torch, B, W, dev):
+    """Chunked causal prefill, 8 prompts x 2048 new tokens after U{0..4096}
+    cached, GQA 32/8, d 128: store of the new tokens, then MFMA attention."""
+    wl = W.chunked_prefill()
+    t = W.make_tensors(wl, device=dev, nan_fill=False)
+    out = torch.empty_like(t["q"])
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        B.pkv_prefill_attn(t["q"], t["k_caches"][0], t["v_caches"][0], t["block_tables"],
+                           t["cu_new_lens"], t["context_lens"], wl.scale, out,
+                           max_new_len=wl.max_new_len, max_context_len=wl.max_context_len)
+
+    def store():
+        B.pkv_store(t["k_new"], t["v_new"], t["slot_mapping"], t["k_caches"][0], t["v_caches"][0])
+
+    store()
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.prefill_iters):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        store()
+        b.record(stream)
+        run()
+        c.record(stream)
+        evs.append((a, b, c))
+    torch.cuda.synchronize()
+    st_ms = float(np.median([a.elapsed_time(b) for a, b, _ in evs]))
+    at_ms = float(np.median([b.elapsed_time(c) for _, b, c in evs]))
+    fl = prefill_flops(wl)
+    tf = fl / (at_ms * 1e-3) / 1e12
+    return {
+        "workload": "chunked causal prefill: 8 prompts x 2048 new tokens, cached U{0..4096}, "
+                    "32q/8kv, d 128",
+        "attn_ms": round(at_ms, 4), "attn_tflops": round(tf, 2),
+        "mfma_peak_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "causal_gflop": round(fl / 1e9, 2),
+        "store_ms": round(st_ms, 4),
+        "store_gbs": round(store_bytes(wl) / (st_ms * 1e-3) / 1e9, 2),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged-KV-cache store and attention on MI355X
+ * (gfx950).
+ *
+ * Pages this interface follows (titles as printed on the pages):
+ *   [NV2]  "Nano-vLLM Part 2: model internals, KV cache and tensor
+ *          parallelism" (seekfood.cn/news/749872)
+ *   [NVE]  the Nano-vLLM engine deep-dive that opens with "from 'it runs' to
+ *          'it runs well'" (mhpq.cn/news/130328)
+ *   [LLM4] "LLM basics primer: from text to token, embedding, QKV and
+ *          Transformer, part 4" (CSDN; qwbw.cn/news/156881)
+ *
+ * ---------------------------------------------------------------- layouts --
+ * The pages name the cache's dimensions (block, layer, K/V, token: [NV2]
+ * §05.2) but not their order.  This library takes, per layer:
+ *   k_cache, v_cache  bf16 [num_blocks][num_kv_heads][block_size][head_dim]
+ *                     contiguous; one (block, kv head) tile is one run of
+ *                     block_size * head_dim elements.  block_size is 16
+ *                     ("e.g. 16 tokens per block", [NVE] §2.2).
+ *   k, v (new tokens) bf16 [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping      int32 [num_tokens]; slot = physical_block * 16 + offset
+ *                     ([NVE] §2.2: the cache is managed by block or by slot).
+ *   q, out (decode)   bf16 [num_seqs][num_q_heads][head_dim]
+ *   q, out (prefill)  bf16 [total_new][num_q_heads][head_dim], prompts packed
+ *                     in order; prompt p owns rows cu_new_lens[p] ..
+ *                     cu_new_lens[p+1]-1.
+ *   block_tables      int32 [num_seqs][max_blocks_per_seq]: logical block i of
+ *                     sequence s lives in physical block block_tables[s][i]
+ *                     ([NVE] §2.2 block table; [LLM4] §17.7 logical -> physical
+ *                     mapping).  Entries past a sequence's last block are never
+ *                     read.  Sequences may share physical blocks (prefix
+ *                     sharing, [LLM4] §17.6-17.7).
+ *   context_lens      int32 [num_seqs]: cached tokens per sequence AFTER this
+ *                     step's store -- decode appends the new token, then
+ *                     attends over the whole cache including it ([NVE] §2.1).
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads): grouped-query
+ * attention with contiguous groups ([LLM4] §21.1, GQA shares KV heads).
+ *
+ * ------------------------------------------------------------ conventions --
+ * Ownership: the caller owns every buffer.  The library never allocates,
+ *   frees or synchronises; every call enqueues kernels on `stream` and
+ *   returns.  All pointers except `stream` are device pointers.
+ * Alignment: every device pointer must be 16-byte aligned.
+ * Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
+ *   num_kv_heads with a group size of 1, 2, 4 or 8.
+ * Errors: every call returns a pkv_status.  Argument errors are found on the
+ *   host before anything is launched; a launch failure returns PKV_ERR_HIP.
+ *   pkv_last_error() gives a one-line, thread-local description of the most
+ *   recent failure on the calling thread.
+ * Device-resident indices (slots, block ids, context lengths) are a caller
+ *   precondition: slots unique within a call and below num_blocks * 16, block
+ *   ids below num_blocks, context_lens at most max_blocks_per_seq * 16.  The
+ *   kernels never touch memory outside the pools when they are violated (an
+ *   out-of-range slot is not written, an out-of-range block is not read), but
+ *   the output for an offending sequence is then unspecified.
+ * Numerics: bf16 inputs, fp32 accumulation and softmax, bf16 output rounded
+ *   to nearest even.  Slots outside a sequence's live context never
+ *   influence its output, whatever bits they hold (NaN included).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL = 1,        /* a required pointer is null */
+    PKV_ERR_SHAPE = 2,       /* a size is negative or inconsistent */
+    PKV_ERR_UNSUPPORTED = 3, /* head_dim, block_size or group size not supported */
+    PKV_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+    PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+    PKV_ERR_HIP = 6          /* the HIP runtime reported an error */
+} pkv_status;
+
+/* One layer's K and V pools.  k and v are device pointers to bf16 arrays of
+ * [num_blocks][num_kv_heads][block_size][head_dim]. */
+typedef struct {
+    void *k;
+    void *v;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+} pkv_cache;
+
+/*
+ * pkv_store -- append new tokens' K and V to the paged cache.
+ * For every i < num_tokens with slot_mapping[i] >= 0:
+ *   cache.k[slot / 16][h][slot % 16][:] = k[i][h][:]   (and the same for v)
+ * for every KV head h.  A pure bit copy: stored bits equal the input bits.
+ * slot_mapping[i] < 0 skips token i (padding).  Follows [NVE] §2.1 (decode
+ * appends each new token's K and V to the cache) and [NV2] §05.3 (a kernel
+ * writes the new K/V into the cache).
+ * k, v: bf16 [num_tokens][cache.num_kv_heads][cache.head_dim], device.
+ * num_tokens == 0 is a no-op.
+ */
+int pkv_store(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+              pkv_cache cache, hipStream_t stream);
+
+/*
+ * pkv_decode_partition_tokens -- the split-KV partition length (tokens, a
+ * multiple of 16) that pkv_decode_attn uses when passed partition_tokens = 0.
+ * Chosen so that num_seqs * num_kv_heads * ceil(max_context_len / P) work
+ * units fill the GPU.  Returns 0 on invalid arguments.
+ */
+int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_context_len);
+
+/*
+ * pkv_decode_workspace_bytes -- device scratch pkv_decode_attn needs for the
+ * split-KV partials of num_seqs x num_q_heads rows at the given partition
+ * length.  partition_tokens = 0 sizes for what pkv_decode_partition_tokens
+ * picks with num_kv_heads = 1, which is an upper bound for every head count
+ * (fewer KV heads never give a longer partition).  0 when no partials are
+ * needed (every context fits one partition).
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ * pkv_decode_attn -- single-query attention of each sequence's new token over
+ * its cached tokens, read through its block table:
+ *   out[s][h][:] = softmax(scale * q[s][h] . K_s^T) V_s
+ * over keys 0 .. context_lens[s]-1 of KV head h / G ([NVE] §3 formula and
+ * decode shapes; [LLM4] §21.1 GQA).  The softmax subtracts the running
+ * maximum before exponentiating ([NVE] §3.2).  The keys are split into
+ * partitions of partition_tokens tokens (0 = pkv_decode_partition_tokens);
+ * each (sequence, KV head, partition) is one wavefront serving the whole
+ * query group, and a second pass merges the partitions' (max, sum, partial
+ * output) triples.  A sequence with context_lens[s] == 0 gets out = 0.
+ * max_context_len: host-side upper bound of context_lens (sizes the grid).
+ * workspace: device scratch of at least pkv_decode_workspace_bytes(num_seqs,
+ *   num_q_heads, head_dim, max_context_len, partition_tokens) bytes; may be
+ *   null when that is 0.  Its contents on entry do not matter.
+ */
+int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                    int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                    void *workspace, size_t workspace_bytes, int32_t partition_tokens,
+                    hipStream_t stream);
+
+/*
+ * pkv_prefill_attn -- chunked causal prefill over the paged cache.  Prompt p
+ * has n_p = cu_new_lens[p+1] - cu_new_lens[p] new tokens whose K/V are
+ * already stored after c_p = context_lens[p] - n_p cached ones.  New token i
+ * sits at position c_p + i and attends to keys 0 .. c_p + i inclusive: itself
+ * and everything before it, never a later token ([NVE] §3.2 causal mask;
+ * [LLM4] §22 steps 6-8).  Q K^T and P V run on the matrix cores (bf16 in, fp32
+ * accumulate); the softmax runs in fp32 and P is rounded to bf16 before P V.
+ * cu_new_lens: int32 [num_seqs + 1], device: cu_new_lens[0] == 0, non-decreasing,
+ *   cu_new_lens[num_seqs] == rows of q and out, and n_p <= context_lens[p]
+ *   (device-resident, so a caller precondition like the block ids).
+ * max_new_len, max_context_len: host-side upper bounds of n_p and
+ * context_lens (they size the grid).
+ */
+int pkv_prefill_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                     int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t max_new_len,
+                     int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                     hipStream_t stream);
+
+/*
+ * pkv_kv_bytes -- KV-cache bytes for `tokens` cached tokens:
+ *   2 (K and V) x layers x kv_heads x head_dim x tokens x bytes_per_elem
+ * ([LLM4] §17.3 and §17.6: KV heads, not query heads; tokens summed over
+ * requests).  Returns 0 for negative arguments.
+ */
+uint64_t pkv_kv_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim, int64_t tokens,
+                      int32_t bytes_per_elem);
+
+/* Static, human-readable name of a pkv_status value. */
+const char *pkv_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char *pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

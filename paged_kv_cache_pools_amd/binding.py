@@ -1,0 +1,220 @@
+"""ctypes binding of libpkv.so (the C ABI in include/pkv.h).
+
+Argument marshalling only: shape, dtype, device and contiguity checks, then the
+C call with raw device pointers and torch's current HIP stream.  Every step of
+the computation runs in the library's kernels; there is no fallback.  If the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpkv.so")
+
+PKV_OK = 0
+STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
+                4: "PKV_ERR_ALIGN", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_HIP"}
+
+# every symbol include/pkv.h declares
+EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
+            "pkv_decode_attn", "pkv_prefill_attn", "pkv_kv_bytes", "pkv_status_string",
+            "pkv_last_error"]
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        super().__init__(f"{what} failed: {STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+
+
+class PkvCache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32)]
+
+
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_lib_handle = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libpkv.so once; raise if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_pools_amd.build`"
+                           " (the HIP library is the only implementation; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    lib.pkv_store.restype = ctypes.c_int
+    lib.pkv_store.argtypes = [_P, _P, _P, _I32, PkvCache, _P]
+    lib.pkv_decode_partition_tokens.restype = _I32
+    lib.pkv_decode_partition_tokens.argtypes = [_I32, _I32, _I32]
+    lib.pkv_decode_workspace_bytes.restype = _SZ
+    lib.pkv_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
+    lib.pkv_decode_attn.restype = ctypes.c_int
+    lib.pkv_decode_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _I32, _I32, _I32, ctypes.c_float,
+                                    _P, _P, _SZ, _I32, _P]
+    lib.pkv_prefill_attn.restype = ctypes.c_int
+    lib.pkv_prefill_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
+                                     ctypes.c_float, _P, _P]
+    lib.pkv_kv_bytes.restype = ctypes.c_uint64
+    lib.pkv_kv_bytes.argtypes = [_I32, _I32, _I32, _I64, _I32]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_last_error.argtypes = []
+    _lib_handle = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != PKV_OK:
+        detail = load().pkv_last_error().decode()
+        raise PkvError(status, what, detail)
+
+
+def _stream(t, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _cache(k_cache, v_cache) -> PkvCache:
+    import torch
+
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} and v_cache {tuple(v_cache.shape)} differ")
+    nb, hkv, bs, d = k_cache.shape
+    return PkvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, hkv, d, bs)
+
+
+# ---------------------------------------------------------------------------
+# the three calls
+# ---------------------------------------------------------------------------
+
+def pkv_store(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """Scatter k/v ([T][Hkv][d] bf16) into the pools at slot_mapping ([T] int32)."""
+    import torch
+
+    lib = load()
+    cache = _cache(k_cache, v_cache)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    t = slot_mapping.shape[0]
+    want = (t, cache.num_kv_heads, cache.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want:
+        raise ValueError(f"k/v must be {want}, got {tuple(k.shape)} / {tuple(v.shape)}")
+    _check(lib.pkv_store(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), t, cache,
+                         _stream(k_cache, stream)), "pkv_store")
+
+
+def pkv_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len) -> int:
+    return int(load().pkv_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len))
+
+
+def pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                               partition_tokens=0) -> int:
+    return int(load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                 partition_tokens))
+
+
+def pkv_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                    max_context_len: Optional[int] = None, workspace=None, partition_tokens: int = 0,
+                    stream=None):
+    """out[s][h] = softmax(scale q[s][h] K^T) V over each sequence's paged cache.
+
+    q, out: [S][Hq][d] bf16; block_tables [S][max_blocks] int32; context_lens [S]
+    int32 (after the store).  ``max_context_len`` defaults to
+    ``max_blocks * 16`` (no host sync); pass the true maximum to size the grid
+    tightly.  ``workspace``: uint8 device tensor, allocated here when None.
+    """
+    import torch
+
+    lib = load()
+    cache = _cache(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    s, hq, d = q.shape
+    if tuple(out.shape) != (s, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables / context_lens do not match q's sequence count")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * cache.block_size
+    p = partition_tokens or pkv_decode_partition_tokens(s, cache.num_kv_heads, max_context_len)
+    need = pkv_decode_workspace_bytes(s, hq, d, max_context_len, p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib.pkv_decode_attn(q.data_ptr(), cache, block_tables.data_ptr(), max_blocks,
+                               context_lens.data_ptr(), s, int(max_context_len), hq,
+                               float(scale), out.data_ptr(), workspace.data_ptr(),
+                               workspace.numel(), int(p), _stream(q, stream)),
+           "pkv_decode_attn")
+    return out
+
+
+def pkv_prefill_attn(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens, scale, out,
+                     max_new_len: int, max_context_len: int, stream=None):
+    """Chunked causal prefill: q/out [total_new][Hq][d] bf16, prompts packed
+    by cu_new_lens ([S+1] int32); context_lens [S] int32 include the new tokens."""
+    import torch
+
+    lib = load()
+    cache = _cache(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(cu_new_lens, "cu_new_lens", torch.int32, 1)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    total, hq, d = q.shape
+    s = context_lens.shape[0]
+    if tuple(out.shape) != (total, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    if cu_new_lens.shape[0] != s + 1 or block_tables.shape[0] != s:
+        raise ValueError("cu_new_lens / block_tables do not match context_lens")
+    _check(lib.pkv_prefill_attn(q.data_ptr(), cache, block_tables.data_ptr(), block_tables.shape[1],
+                                cu_new_lens.data_ptr(), context_lens.data_ptr(), s,
+                                int(max_new_len), int(max_context_len), hq, float(scale),
+                                out.data_ptr(), _stream(q, stream)),
+           "pkv_prefill_attn")
+    return out
+
+
+def pkv_kv_bytes(layers, kv_heads, head_dim, tokens, bytes_per_elem) -> int:
+    return int(load().pkv_kv_bytes(layers, kv_heads, head_dim, tokens, bytes_per_elem))
+
+
+def pkv_status_string(status: int) -> str:
+    return load().pkv_status_string(status).decode()
+
+
+def pkv_last_error() -> str:
+    return load().pkv_last_error().decode()

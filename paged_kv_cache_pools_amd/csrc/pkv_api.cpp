@@ -1,0 +1,252 @@
+// pkv_api.cpp -- the exported C ABI of libpkv.so (declared in include/pkv.h).
+//
+// Host side only: argument validation (before anything is launched), launch
+// geometry, workspace sizing and error strings.  The arithmetic lives in the
+// kernels (store.hip, decode.hip, prefill.hip).
+#include "pkv.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return PKV_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int32_t kBlock = 16;
+
+int check_cache(const pkv_cache &c) {
+    if (c.num_blocks < 0 || c.num_kv_heads <= 0 || c.head_dim <= 0 || c.block_size <= 0)
+        return fail(PKV_ERR_SHAPE, "cache: num_blocks %d, num_kv_heads %d, head_dim %d, block_size %d",
+                    c.num_blocks, c.num_kv_heads, c.head_dim, c.block_size);
+    if (c.head_dim != 64 && c.head_dim != 128)
+        return fail(PKV_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are supported", c.head_dim);
+    if (c.block_size != kBlock)
+        return fail(PKV_ERR_UNSUPPORTED, "block_size %d: only 16 is supported", c.block_size);
+    if (c.num_blocks > 0 && (!c.k || !c.v)) return fail(PKV_ERR_NULL, "cache.k or cache.v is null");
+    if (!aligned16(c.k) || !aligned16(c.v))
+        return fail(PKV_ERR_ALIGN, "cache.k / cache.v must be 16-byte aligned");
+    return PKV_OK;
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+    if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+        return fail(PKV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                    num_q_heads, num_kv_heads);
+    const int32_t g = num_q_heads / num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(PKV_ERR_UNSUPPORTED, "group size %d: only 1, 2, 4 and 8 are supported", g);
+    return PKV_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+// Partition length for split-KV decode: aim for about 16 wavefronts per CU
+// (256 CUs) if every sequence had the longest context; never shorter than 4
+// blocks (the fixed cost of a unit is a q load and a cross-row merge) and
+// never longer than 64 blocks (so a long-context straggler is split enough).
+int32_t partition_for(int64_t units, int32_t max_context_len) {
+    constexpr int64_t kTargetWaves = 4096;
+    constexpr int32_t kMin = 64, kMax = 1024;
+    if (max_context_len <= 0) return kMin;
+    int64_t want = ((int64_t)max_context_len * units + kTargetWaves - 1) / kTargetWaves;
+    int32_t p = kMin;
+    while (p < kMax && p < want) p <<= 1;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pkv_status_string(int status) {
+    switch (status) {
+        case PKV_OK: return "PKV_OK";
+        case PKV_ERR_NULL: return "PKV_ERR_NULL: a required pointer is null";
+        case PKV_ERR_SHAPE: return "PKV_ERR_SHAPE: a size is negative or inconsistent";
+        case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED: head_dim, block_size or group size not supported";
+        case PKV_ERR_ALIGN: return "PKV_ERR_ALIGN: a device pointer is not 16-byte aligned";
+        case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
+        case PKV_ERR_HIP: return "PKV_ERR_HIP: the HIP runtime reported an error";
+        default: return "unknown pkv status";
+    }
+}
+
+const char *pkv_last_error(void) { return g_last_error; }
+
+uint64_t pkv_kv_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim, int64_t tokens,
+                      int32_t bytes_per_elem) {
+    if (layers < 0 || kv_heads < 0 || head_dim < 0 || tokens < 0 || bytes_per_elem < 0) return 0;
+    return 2ull * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim * (uint64_t)tokens *
+           (uint64_t)bytes_per_elem;
+}
+
+int pkv_store(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+              pkv_cache cache, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if (num_tokens < 0) return fail(PKV_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!k || !v || !slot_mapping) return fail(PKV_ERR_NULL, "k, v or slot_mapping is null");
+    if (!aligned16(k) || !aligned16(v))
+        return fail(PKV_ERR_ALIGN, "k / v must be 16-byte aligned");
+    const int64_t total = (int64_t)num_tokens * cache.num_kv_heads * (cache.head_dim / 8);
+    if (total > (int64_t)0x7f000000)
+        return fail(PKV_ERR_SHAPE, "store of %d tokens is too large for one call", num_tokens);
+    pkv::StoreArgs a{k, v, slot_mapping, num_tokens, cache.k, cache.v, cache.num_blocks,
+                     cache.num_kv_heads, cache.head_dim};
+    return hip_status(pkv::launch_store(a, stream), "pkv_store launch");
+}
+
+int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_context_len) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
+    return partition_for((int64_t)num_seqs * num_kv_heads, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+    if (partition_tokens < 0 || partition_tokens % kBlock != 0) return 0;
+    const int32_t p = partition_tokens ? partition_tokens
+                                       : pkv_decode_partition_tokens(num_seqs, 1, max_context_len);
+    const int32_t parts = ceil_div(max_context_len, p);
+    if (parts <= 1) return 0;
+    return (size_t)num_seqs * num_q_heads * parts * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                    int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                    void *workspace, size_t workspace_bytes, int32_t partition_tokens,
+                    hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
+    if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d, max_context_len %d, max_blocks_per_seq %d",
+                    num_seqs, max_context_len, max_blocks_per_seq);
+    if (num_seqs == 0) return ok();
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+        return fail(PKV_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq %d x 16",
+                    max_context_len, max_blocks_per_seq);
+    if (max_context_len > 0 && cache.num_blocks == 0)
+        return fail(PKV_ERR_SHAPE, "an empty pool cannot hold a context of %d tokens",
+                    max_context_len);
+    if (!q || !out || !context_lens || (max_blocks_per_seq > 0 && !block_tables))
+        return fail(PKV_ERR_NULL, "q, out, context_lens or block_tables is null");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
+    if (partition_tokens < 0 || partition_tokens % kBlock != 0)
+        return fail(PKV_ERR_SHAPE, "partition_tokens %d is not a non-negative multiple of 16",
+                    partition_tokens);
+    const int32_t p = partition_tokens
+                          ? partition_tokens
+                          : pkv_decode_partition_tokens(num_seqs, cache.num_kv_heads, max_context_len);
+    const int32_t parts = max_context_len > 0 ? ceil_div(max_context_len, p) : 1;
+    const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache.head_dim,
+                                                   max_context_len, p);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (need > 0 && !aligned16(workspace))
+        return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if ((int64_t)num_seqs * num_q_heads * parts > (int64_t)0x7fffffff / 256)
+        return fail(PKV_ERR_SHAPE, "too many partitions for one call");
+    if (num_seqs > 65535 || cache.num_kv_heads > 65535)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d / num_kv_heads %d exceed one launch's grid",
+                    num_seqs, cache.num_kv_heads);
+
+    pkv::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = cache.k;
+    a.v_cache = cache.v;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_context_len = max_context_len;
+    a.num_blocks = cache.num_blocks;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache.num_kv_heads;
+    a.head_dim = cache.head_dim;
+    a.partition_tokens = p;
+    a.max_parts = parts;
+    a.scale = scale;
+    a.out = out;
+    float *ws = static_cast<float *>(workspace);
+    a.ws_out = need ? ws : nullptr;
+    a.ws_ml = need ? ws + (size_t)num_seqs * num_q_heads * parts * cache.head_dim : nullptr;
+    return hip_status(pkv::launch_decode(a, stream), "pkv_decode_attn launch");
+}
+
+int pkv_prefill_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                     int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t max_new_len,
+                     int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                     hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
+    if (num_seqs < 0 || max_new_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d, max_new_len %d, max_context_len %d", num_seqs,
+                    max_new_len, max_context_len);
+    if (num_seqs == 0 || max_new_len == 0) return ok();
+    if (max_new_len > max_context_len)
+        return fail(PKV_ERR_SHAPE, "max_new_len %d exceeds max_context_len %d", max_new_len,
+                    max_context_len);
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+        return fail(PKV_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq %d x 16",
+                    max_context_len, max_blocks_per_seq);
+    if (cache.num_blocks == 0)
+        return fail(PKV_ERR_SHAPE, "an empty pool cannot hold a context of %d tokens",
+                    max_context_len);
+    if (!q || !out || !context_lens || !cu_new_lens || !block_tables)
+        return fail(PKV_ERR_NULL, "q, out, cu_new_lens, context_lens or block_tables is null");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
+    if (num_seqs > 65535 || cache.num_kv_heads > 65535)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d / num_kv_heads %d exceed one launch's grid",
+                    num_seqs, cache.num_kv_heads);
+    pkv::PrefillArgs a{};
+    a.q = q;
+    a.k_cache = cache.k;
+    a.v_cache = cache.v;
+    a.block_tables = block_tables;
+    a.cu_new_lens = cu_new_lens;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_new_len = max_new_len;
+    a.max_context_len = max_context_len;
+    a.num_blocks = cache.num_blocks;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache.num_kv_heads;
+    a.head_dim = cache.head_dim;
+    a.scale = scale;
+    a.out = out;
+    return hip_status(pkv::launch_prefill(a, stream), "pkv_prefill_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// pkv_internal.h -- kernel launchers behind the C ABI (host side, not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct StoreArgs {
+    const void *k, *v;
+    const int32_t *slots;
+    int32_t num_tokens;
+    void *k_cache, *v_cache;
+    int32_t num_blocks, num_kv_heads, head_dim;
+};
+hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q;
+    const void *k_cache, *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    int32_t max_blocks_per_seq, num_seqs, max_context_len;
+    int32_t num_blocks, num_q_heads, num_kv_heads, head_dim;
+    int32_t partition_tokens, max_parts;
+    float scale;
+    void *out;
+    float *ws_out;  // [num_seqs][num_q_heads][max_parts][head_dim]
+    float *ws_ml;   // [num_seqs][num_q_heads][max_parts][2]
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+struct PrefillArgs {
+    const void *q;
+    const void *k_cache, *v_cache;
+    const int32_t *block_tables;
+    const int32_t *cu_new_lens;
+    const int32_t *context_lens;
+    int32_t max_blocks_per_seq, num_seqs, max_new_len, max_context_len;
+    int32_t num_blocks, num_q_heads, num_kv_heads, head_dim;
+    float scale;
+    void *out;
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,148 @@
+"""Shared machinery of the GPU parity tests: run a workload through libpkv on
+the GPU and through the fp64 oracle on the host, on the same seeded inputs.
+
+The oracle always starts from the generator's pre-store cache and new K/V (host
+copies taken before the GPU store runs) and applies its own store, so no
+expected value comes from the GPU path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_cache_pools_amd import binding as B
+from paged_kv_cache_pools_amd import workloads as W
+
+MAX_ABS = 1e-2   # attention tolerance vs the fp64 oracle (bf16 in, fp32 accumulate, bf16 out)
+MEAN_ABS = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def bits(t):
+    return W.bf16_bits(t)
+
+
+def to_f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def compare(got, ref, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    """got: bf16 torch tensor (GPU), ref: float64 numpy.  Returns the stats."""
+    g = to_f64(got)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    floor = np.abs(torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy() - ref)
+    stats = dict(max=float(err.max()), mean=float(err.mean()), floor_mean=float(floor.mean()))
+    say(f"    {what}: max|err| {stats['max']:.3e} mean|err| {stats['mean']:.3e} "
+        f"(bf16 rounding floor mean {stats['floor_mean']:.3e})")
+    assert stats["max"] <= max_abs and stats["mean"] <= mean_abs, (what, stats)
+    return stats
+
+
+def orc():
+    return oracle.get()
+
+
+class Case:
+    """A workload with its tensors on the GPU plus host copies for the oracle."""
+
+    def __init__(self, wl, device="cuda", gen_device="cpu", seed=None, nan_fill=True, layers=1):
+        self.wl = wl
+        t = W.make_tensors(wl, device=gen_device, layers=layers, nan_fill=nan_fill, seed=seed)
+        self.host_src = gen_device == "cpu"
+        self.t = t
+        self.dev = {}
+        for k in ("q", "k_new", "v_new", "block_tables", "context_lens", "slot_mapping",
+                  "cu_new_lens"):
+            self.dev[k] = t[k].to(device)
+        self.dev["k_caches"] = [x.to(device) for x in t["k_caches"]]
+        self.dev["v_caches"] = [x.to(device) for x in t["v_caches"]]
+        if self.host_src:
+            # pre-store host copies for the oracle
+            self.h = {k: bits(t[k]) for k in ("q", "k_new", "v_new")}
+            self.h["kc"] = bits(t["k_caches"][0]).copy()
+            self.h["vc"] = bits(t["v_caches"][0]).copy()
+
+    # -- GPU side --------------------------------------------------------------
+    def gpu_store(self, layer=0):
+        d = self.dev
+        B.pkv_store(d["k_new"], d["v_new"], d["slot_mapping"], d["k_caches"][layer],
+                    d["v_caches"][layer])
+
+    def gpu_decode(self, layer=0, partition_tokens=0, max_context_len=None):
+        d = self.dev
+        out = torch.empty_like(d["q"])
+        B.pkv_decode_attn(d["q"], d["k_caches"][layer], d["v_caches"][layer], d["block_tables"],
+                          d["context_lens"], self.wl.scale, out,
+                          max_context_len=max_context_len or self.wl.max_context_len,
+                          partition_tokens=partition_tokens)
+        return out
+
+    def gpu_prefill(self, layer=0):
+        d = self.dev
+        out = torch.empty_like(d["q"])
+        B.pkv_prefill_attn(d["q"], d["k_caches"][layer], d["v_caches"][layer], d["block_tables"],
+                           d["cu_new_lens"], d["context_lens"], self.wl.scale, out,
+                           max_new_len=self.wl.max_new_len,
+                           max_context_len=self.wl.max_context_len)
+        return out
+
+    # -- oracle side (whole problem, host-generated inputs) ----------------------
+    def oracle_store(self):
+        h = self.h
+        orc().store(h["k_new"], h["v_new"], self.wl.slot_mapping, h["kc"], h["vc"])
+
+    def oracle_decode(self, nthreads=0):
+        h = self.h
+        return orc().decode(h["q"], h["kc"], h["vc"], self.wl.block_tables, self.wl.context_lens,
+                            self.wl.scale, nthreads=nthreads)
+
+    def oracle_prefill(self, nthreads=0):
+        h = self.h
+        return orc().prefill(h["q"], h["kc"], h["vc"], self.wl.block_tables, self.wl.cu_new_lens,
+                             self.wl.context_lens, self.wl.scale, nthreads=nthreads)
+
+
+def compact_for_oracle(wl, t, seqs, layer=0):
+    """Host inputs for the oracle restricted to the sequences ``seqs``: the
+    pre-store blocks they reference (renumbered), their block-table rows,
+    their new tokens' K/V and slots (renumbered), and their q rows.
+
+    ``t`` are the generator's tensors (any device), taken before the GPU store.
+    """
+    seqs = list(seqs)
+    bs = wl.block_size
+    rows = []
+    for s in seqs:
+        nb = -(-int(wl.context_lens[s]) // bs)
+        rows.append(wl.block_tables[s, :nb])
+    ids = np.unique(np.concatenate(rows))
+    remap = {int(b): i for i, b in enumerate(ids)}
+    width = max(len(r) for r in rows)
+    bt = np.full((len(seqs), max(width, 1)), -1, np.int32)
+    for i, r in enumerate(rows):
+        bt[i, : len(r)] = [remap[int(b)] for b in r]
+    idx = torch.from_numpy(ids.astype(np.int64)).to(t["k_caches"][layer].device)
+    kc = bits(t["k_caches"][layer].index_select(0, idx)).copy()
+    vc = bits(t["v_caches"][layer].index_select(0, idx)).copy()
+    cu = wl.cu_new_lens
+    tok = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs]).astype(np.int64)
+    slots = wl.slot_mapping[tok]
+    new_slots = np.array([remap[int(x) // bs] * bs + int(x) % bs if x >= 0 else -1 for x in slots],
+                         np.int32)
+    tok_t = torch.from_numpy(tok).to(t["k_new"].device)
+    k_new = bits(t["k_new"].index_select(0, tok_t))
+    v_new = bits(t["v_new"].index_select(0, tok_t))
+    ctx = wl.context_lens[seqs].astype(np.int32)
+    new_lens = wl.new_lens[seqs].astype(np.int32)
+    if wl.kind == "decode":
+        q = bits(t["q"].index_select(0, torch.tensor(seqs, device=t["q"].device)))
+    else:
+        q = bits(t["q"].index_select(0, tok_t))
+    return dict(kc=kc, vc=vc, bt=bt, ctx=ctx, new_lens=new_lens, slots=new_slots, k_new=k_new,
+                v_new=v_new, q=q, tok=tok)

@@ -1,0 +1,137 @@
+"""Host-side checks of libpkv.so: it loads, exports every symbol include/pkv.h
+declares, and its host-only logic (sizing, partitioning, argument validation
+before any launch) behaves.  No GPU: no call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_pools_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libpkv.so is not built (run python -m paged_kv_cache_pools_amd.build)")
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert set(names) == set(B.EXPORTED), names
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_kv_bytes_matches_pages(lib):
+    # LLM primer part 4, §17.3 and §23.2 lab 2 (tests/golden/kv_sizing.json)
+    import json
+
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "kv_sizing.json")))
+    for c in g["cases"] + [g["fp8_note"], g["counter_example"]]:
+        assert B.pkv_kv_bytes(c["layers"], c["kv_heads"], c["head_dim"], c["tokens"],
+                              c["bytes_per_element"]) == c["bytes"], c["cite"]
+    assert B.pkv_kv_bytes(-1, 8, 128, 4096, 2) == 0
+
+
+def test_status_strings(lib):
+    for s, name in B.STATUS_NAMES.items():
+        assert B.pkv_status_string(s).startswith(name)
+    assert "unknown" in B.pkv_status_string(99)
+
+
+def test_partition_heuristic(lib):
+    # the 32 x 4096 GQA batch: 256 (seq, kv head) units -> 256-token partitions
+    assert B.pkv_decode_partition_tokens(32, 8, 4096) == 256
+    for s, h, ctx in ((1, 1, 1), (2, 2, 37), (256, 8, 32768), (16, 32, 2048), (1, 1, 1 << 20)):
+        p = B.pkv_decode_partition_tokens(s, h, ctx)
+        assert p % 16 == 0 and 64 <= p <= 1024, (s, h, ctx, p)
+    assert B.pkv_decode_partition_tokens(-1, 8, 10) == 0
+    # fewer KV heads never give a longer partition: workspace(P=0) is an upper bound
+    for h in (1, 2, 8, 32):
+        assert B.pkv_decode_partition_tokens(32, h, 4096) >= B.pkv_decode_partition_tokens(32, 1, 4096)
+
+
+def test_workspace_bytes(lib):
+    assert B.pkv_decode_workspace_bytes(32, 32, 128, 4096, 256) == 32 * 32 * 16 * 130 * 4
+    assert B.pkv_decode_workspace_bytes(32, 32, 128, 256, 256) == 0   # one partition
+    assert B.pkv_decode_workspace_bytes(32, 32, 128, 257, 256) == 32 * 32 * 2 * 130 * 4
+    assert B.pkv_decode_workspace_bytes(0, 32, 128, 4096, 256) == 0
+    assert B.pkv_decode_workspace_bytes(4, 4, 64, 100, 24) == 0      # not a multiple of 16
+    p1 = B.pkv_decode_partition_tokens(32, 1, 4096)
+    assert B.pkv_decode_workspace_bytes(32, 32, 128, 4096, 0) == \
+        B.pkv_decode_workspace_bytes(32, 32, 128, 4096, p1)
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+def cache(nb=16, hkv=2, d=64, bs=16, k=FAKE, v=FAKE):
+    return B.PkvCache(k, v, nb, hkv, d, bs)
+
+
+def decode(lib, c=None, q=FAKE, out=FAKE, hq=4, s=2, max_ctx=37, max_blocks=3, ws=FAKE,
+           ws_bytes=1 << 30, part=0, bt=FAKE, ctx=FAKE):
+    return lib.pkv_decode_attn(q, c or cache(), bt, max_blocks, ctx, s, max_ctx, hq,
+                               ctypes.c_float(0.125), out, ws, ws_bytes, part, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(c=cache(d=96)), 3),
+    (dict(c=cache(bs=32)), 3),
+    (dict(hq=5), 2),                       # not a multiple of 2 kv heads
+    (dict(hq=6), 3),                       # group 3 unsupported
+    (dict(hq=2 * 16), 3),                  # group 16 unsupported
+    (dict(c=cache(hkv=3), hq=9), 3),       # group 3 unsupported
+    (dict(q=0), 1),
+    (dict(out=0), 1),
+    (dict(q=FAKE + 8), 4),
+    (dict(c=cache(k=FAKE + 2)), 4),
+    (dict(max_ctx=49), 2),                 # beyond max_blocks * 16
+    (dict(s=-1), 2),
+    (dict(ws=0, max_ctx=37, part=16), 5),  # needs partials, no workspace
+    (dict(ws_bytes=16, max_ctx=37, part=16), 5),
+    (dict(part=24), 2),
+    (dict(c=cache(nb=0)), 2),
+])
+def test_decode_rejects_before_launch(lib, kwargs, status):
+    assert decode(lib, **kwargs) == status
+    assert B.pkv_last_error() != ""
+
+
+def test_decode_empty_batch_is_ok(lib):
+    assert decode(lib, s=0) == 0
+
+
+def test_store_validation(lib):
+    st = lambda n, c=None, k=FAKE, v=FAKE, sl=FAKE: lib.pkv_store(k, v, sl, n, c or cache(), None)
+    assert st(0) == 0                         # no-op, nothing launched
+    assert st(-1) == 2
+    assert st(4, k=0) == 1
+    assert st(4, k=FAKE + 4) == 4
+    assert st(4, c=cache(d=80)) == 3
+    assert st(1 << 30, c=cache(hkv=64, d=128)) == 2
+
+
+def test_prefill_validation(lib):
+    pf = lambda **kw: lib.pkv_prefill_attn(
+        kw.get("q", FAKE), kw.get("c", cache()), FAKE, kw.get("max_blocks", 4), FAKE, FAKE,
+        kw.get("s", 2), kw.get("max_new", 16), kw.get("max_ctx", 40), kw.get("hq", 4),
+        ctypes.c_float(0.125), kw.get("out", FAKE), None)
+    assert pf(s=0) == 0 and pf(max_new=0) == 0
+    assert pf(max_new=50) == 2              # more new tokens than context
+    assert pf(max_ctx=80) == 2              # beyond max_blocks * 16
+    assert pf(q=0) == 1
+    assert pf(hq=5) == 2
+    assert pf(c=cache(d=32)) == 3

@@ -1,0 +1,257 @@
+"""GPU parity: libpkv's HIP kernels against the fp64 oracle on the same seeded
+inputs.  Store must be bit-exact; attention within max |err| 1e-2 and mean
+|err| 1e-3 of the oracle (bf16 in, fp32 accumulate, bf16 out).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import (Case, compact_for_oracle, compare, orc, say, bits, to_f64)
+from paged_kv_cache_pools_amd import binding as B
+from paged_kv_cache_pools_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+    say(f"[gpu] {torch.cuda.get_device_name(0)}")
+
+
+# ---------------------------------------------------------------------------
+# store
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "qwen_mha", "cont_batch", "chunked_prefill"])
+def test_store_bit_exact(name):
+    wl = W.CONFIGS[name]()
+    say(f"[gpu] store {name}: T={wl.num_tokens} pool={wl.num_blocks} blocks")
+    c = Case(wl)
+    c.gpu_store()
+    torch.cuda.synchronize()
+    c.oracle_store()
+    assert np.array_equal(bits(c.dev["k_caches"][0]), c.h["kc"])
+    assert np.array_equal(bits(c.dev["v_caches"][0]), c.h["vc"])
+
+
+def test_store_skips_negative_and_out_of_pool_slots():
+    wl = W.make_decode("store_skip", [20, 33, 7, 16], 4, 2, 128, 41, spare_blocks=2)
+    wl.slot_mapping[1] = -1
+    wl.slot_mapping[3] = wl.num_blocks * 16 + 5   # outside the pool: never written
+    say("[gpu] store with slot -1 and an out-of-pool slot")
+    c = Case(wl)
+    before = bits(c.dev["k_caches"][0]).copy()
+    c.gpu_store()
+    torch.cuda.synchronize()
+    after = bits(c.dev["k_caches"][0])
+    # exactly the two valid slots changed
+    for i, s in enumerate(wl.slot_mapping):
+        if 0 <= s < wl.num_blocks * 16:
+            assert np.array_equal(after[s // 16, :, s % 16], c.h["k_new"][i])
+    changed = np.argwhere(np.any(after != before, axis=(1, 3)))
+    valid = {(int(s) // 16, int(s) % 16) for s in wl.slot_mapping if 0 <= s < wl.num_blocks * 16}
+    assert {(int(b), int(o)) for b, o in changed} <= valid
+
+
+# ---------------------------------------------------------------------------
+# decode: whole problems checked element by element
+# ---------------------------------------------------------------------------
+
+def run_decode_full(wl, partition_tokens=0, max_context_len=None):
+    c = Case(wl)
+    say(f"[gpu] decode {wl.name}: S={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+        f"d={wl.head_dim} max_ctx={wl.max_context_len} P={partition_tokens or 'auto'}")
+    c.gpu_store()
+    out = c.gpu_decode(partition_tokens=partition_tokens, max_context_len=max_context_len)
+    torch.cuda.synchronize()
+    c.oracle_store()
+    ref = c.oracle_decode()
+    compare(out, ref, f"decode {wl.name}")
+    return c, out, ref
+
+
+def test_decode_tiny():
+    run_decode_full(W.tiny())
+
+
+def test_decode_qwen_mha():
+    run_decode_full(W.qwen_mha())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("part", [16, 64, 0])
+def test_decode_edge_lengths(d, g, part):
+    lens = [1, 15, 16, 17, 32, 63, 64, 65, 129, 0, 2]
+    wl = W.make_decode(f"edge_d{d}_g{g}", lens, 2 * g, 2, d, 100 + d + g, spare_blocks=3)
+    run_decode_full(wl, partition_tokens=part)
+
+
+def test_decode_single_token_exact():
+    """One cached token: out must equal the stored V bit for bit."""
+    wl = W.make_decode("ctx1", [1, 1, 1, 1], 8, 2, 128, 51, spare_blocks=1)
+    c = Case(wl)
+    c.gpu_store()
+    out = c.gpu_decode()
+    torch.cuda.synchronize()
+    got = bits(out)
+    for s in range(wl.num_seqs):
+        for h in range(wl.num_q_heads):
+            assert np.array_equal(got[s, h], c.h["v_new"][s, h // 4]), (s, h)
+
+
+def test_decode_empty_context_is_zero():
+    wl = W.make_decode("ctx0", [0, 40, 0], 4, 2, 64, 52, store=False)
+    c = Case(wl)
+    out = c.gpu_decode(partition_tokens=16)
+    torch.cuda.synchronize()
+    assert np.all(to_f64(out)[[0, 2]] == 0.0)
+    compare(out, c.oracle_decode(), "decode ctx0")
+
+
+@pytest.mark.parametrize("part", [16, 48, 256, 1024])
+def test_decode_partition_sizes(part):
+    wl = W.make_decode("parts", [300, 1000, 17, 2048], 16, 4, 128, 53)
+    run_decode_full(wl, partition_tokens=part)
+
+
+def test_decode_loose_max_context_len():
+    """A host bound larger than any context only adds empty partitions."""
+    wl = W.make_decode("loose", [100, 37], 8, 2, 128, 54)
+    wl.block_tables = np.concatenate([wl.block_tables, np.full((2, 30), -1, np.int32)], axis=1)
+    run_decode_full(wl, max_context_len=wl.max_blocks_per_seq * 16)
+
+
+def test_decode_prefix_shared_equals_copied():
+    """Sequences pointing at shared prefix blocks give bit-identical output to
+    the same sequences with the prefix copied into private blocks."""
+    lens = [64 + 20, 64 + 3, 64 + 50]
+    shared = W.make_decode("shared", lens, 8, 2, 128, 55, prefix_groups=[[0, 1, 2]],
+                           prefix_tokens=64, store=False)
+    c = Case(shared, nan_fill=True)
+    out_shared = c.gpu_decode()
+    # copy: give every sequence private prefix blocks holding the same bits
+    kc, vc = c.dev["k_caches"][0], c.dev["v_caches"][0]
+    nb = shared.num_blocks
+    pre = shared.block_tables[0, :4].copy()
+    kc2 = torch.cat([kc, kc[torch.from_numpy(np.concatenate([pre, pre])).long().cuda()]], 0)
+    vc2 = torch.cat([vc, vc[torch.from_numpy(np.concatenate([pre, pre])).long().cuda()]], 0)
+    bt2 = shared.block_tables.copy()
+    bt2[1, :4] = np.arange(nb, nb + 4)
+    bt2[2, :4] = np.arange(nb + 4, nb + 8)
+    out_copied = torch.empty_like(out_shared)
+    B.pkv_decode_attn(c.dev["q"], kc2.contiguous(), vc2.contiguous(),
+                      torch.from_numpy(bt2).cuda(), c.dev["context_lens"], shared.scale, out_copied,
+                      max_context_len=shared.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out_shared), bits(out_copied))
+    compare(out_shared, c.oracle_decode(), "decode shared prefix")
+
+
+def test_decode_block_permutation_bit_identical():
+    wl = W.make_decode("perm", [200, 45, 16], 8, 2, 128, 56, spare_blocks=5)
+    c = Case(wl)
+    c.gpu_store()
+    out = c.gpu_decode()
+    perm = np.random.default_rng(9).permutation(wl.num_blocks)
+    inv = torch.from_numpy(np.argsort(perm)).long().cuda()
+    kc2 = c.dev["k_caches"][0][inv].contiguous()   # new block perm[b] holds old block b
+    vc2 = c.dev["v_caches"][0][inv].contiguous()
+    bt2 = np.where(wl.block_tables >= 0, perm[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
+    out2 = torch.empty_like(out)
+    B.pkv_decode_attn(c.dev["q"], kc2, vc2, torch.from_numpy(bt2).cuda(), c.dev["context_lens"],
+                      wl.scale, out2, max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(out2))
+
+
+# ---------------------------------------------------------------------------
+# decode at full size, in the launch configuration the benchmark times
+# ---------------------------------------------------------------------------
+
+def run_decode_sampled(wl, seqs, layers=1):
+    say(f"[gpu] decode {wl.name} full size: S={wl.num_seqs} max_ctx={wl.max_context_len} "
+        f"pool={wl.num_blocks} blocks; oracle on seqs {list(seqs)}")
+    t = W.make_tensors(wl, device="cuda", layers=layers, nan_fill=True)
+    hosts = [compact_for_oracle(wl, t, seqs, layer=l) for l in range(layers)]
+    d = {k: t[k] for k in ("q", "k_new", "v_new", "block_tables", "context_lens", "slot_mapping")}
+    outs = []
+    for l in range(layers):
+        B.pkv_store(d["k_new"], d["v_new"], d["slot_mapping"], t["k_caches"][l], t["v_caches"][l])
+        out = torch.empty_like(d["q"])
+        B.pkv_decode_attn(d["q"], t["k_caches"][l], t["v_caches"][l], d["block_tables"],
+                          d["context_lens"], wl.scale, out, max_context_len=wl.max_context_len)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for l, h in enumerate(hosts):
+        orc().store(h["k_new"], h["v_new"], h["slots"], h["kc"], h["vc"])
+        ref = orc().decode(h["q"], h["kc"], h["vc"], h["bt"], h["ctx"], wl.scale)
+        compare(outs[l][list(seqs)], ref, f"decode {wl.name} layer {l}")
+    del t
+
+
+def test_decode_mistral_gqa_full_size():
+    run_decode_sampled(W.mistral_gqa(num_layers=2), [0, 9, 31], layers=2)
+
+
+def test_decode_cont_batch_full_size():
+    wl = W.cont_batch()
+    long_seq = int(np.argmax(wl.context_lens))
+    seqs = sorted({0, 1, 31, 32, 100, 200, 255, long_seq})
+    run_decode_sampled(wl, seqs)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+def test_prefill_small(d, g):
+    cached = [0, 37, 5, 300]
+    new = [70, 16, 1, 129]
+    wl = W.make_prefill(f"prefill_d{d}_g{g}", cached, new, 2 * g, 2, d, 200 + d + g, spare_blocks=2)
+    c = Case(wl)
+    say(f"[gpu] prefill {wl.name}: cached {cached} new {new}")
+    c.gpu_store()
+    out = c.gpu_prefill()
+    torch.cuda.synchronize()
+    c.oracle_store()
+    compare(out, c.oracle_prefill(), f"prefill {wl.name}")
+
+
+def test_prefill_chunked_full_size():
+    """The 8 x 2048-token chunked prefill; the oracle checks sampled query rows
+    (row i of prompt p is decode attention over keys 0 .. c_p + i)."""
+    wl = W.chunked_prefill()
+    say(f"[gpu] prefill {wl.name} full size: cached {list(wl.context_lens - wl.new_lens)}")
+    t = W.make_tensors(wl, device="cuda", nan_fill=True)
+    prompts = [0, 3, 7]
+    h = compact_for_oracle(wl, t, prompts)
+    d = t
+    B.pkv_store(d["k_new"], d["v_new"], d["slot_mapping"], d["k_caches"][0], d["v_caches"][0])
+    out = torch.empty_like(d["q"])
+    B.pkv_prefill_attn(d["q"], d["k_caches"][0], d["v_caches"][0], d["block_tables"],
+                       d["cu_new_lens"], d["context_lens"], wl.scale, out,
+                       max_new_len=wl.max_new_len, max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    orc().store(h["k_new"], h["v_new"], h["slots"], h["kc"], h["vc"])
+    rng = np.random.default_rng(0)
+    rows, ctxs, bts = [], [], []
+    cu = wl.cu_new_lens
+    for i, p in enumerate(prompts):
+        n = int(wl.new_lens[p])
+        c0 = int(wl.context_lens[p]) - n
+        picks = sorted(set([0, 1, 15, 16, 63, 64, n - 1]) | set(rng.integers(0, n, 9).tolist()))
+        for r in picks:
+            rows.append(cu[p] + r)
+            ctxs.append(c0 + r + 1)
+            bts.append(h["bt"][i])
+    rows = np.array(rows)
+    pos = np.searchsorted(h["tok"], rows)
+    q = h["q"][pos]
+    ref = orc().decode(q, h["kc"], h["vc"], np.stack(bts), np.array(ctxs, np.int32), wl.scale)
+    compare(out[torch.from_numpy(rows).cuda()], ref, "prefill chunked (sampled rows)")
