@@ -43,7 +43,25 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-iters", type=int, default=5)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB, three times: the
+    reference reading for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
 def decode_bytes(wl) -> int:
@@ -112,6 +130,9 @@ def cpu_baseline(wl, t, seconds):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU component)", file=sys.stderr)
@@ -205,11 +226,13 @@ def main():
                                "heads, d 128, 16-token blocks, 32 layer pools, store + decode",
                    "num_seqs": S, "context_len": int(wl.max_context_len), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": 16, "layers": L,
-                   "partition_tokens": P},
+                   "work_split": (f"single pass, {-P} waves per (seq, kv head)" if P < 0
+                                  else f"split-KV, {P}-token partitions + merge")},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
         "decode_us_per_layer": round(dec_avg_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": "pkv_decode_attn (split + reduce)",
+        "roofline": {"bound": "hbm", "kernel": ("pkv decode_fused_kernel" if P < 0
+                                               else "pkv decode_split_kernel + decode_reduce_kernel"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": dbytes},

@@ -105,21 +105,27 @@ int pkv_store(const void *k, const void *v, const int32_t *slot_mapping, int32_t
               pkv_cache cache, hipStream_t stream);
 
 /*
- * pkv_decode_partition_tokens -- the split-KV partition length (tokens, a
- * multiple of 16) that pkv_decode_attn uses when passed partition_tokens = 0.
- * Chosen so that num_seqs * num_kv_heads * ceil(max_context_len / P) work
- * units fill the GPU.  Returns 0 on invalid arguments.
+ * pkv_decode_partition_tokens -- the work split pkv_decode_attn uses when
+ * passed partition_tokens = 0:
+ *   -W (W in 1..8): the single-pass kernel, one workgroup of W wavefronts per
+ *      (sequence, KV head); the waves split the sequence's blocks evenly and
+ *      merge through LDS.  Chosen when there are at least 128 such units and
+ *      max_context_len <= 8192.
+ *   P > 0 (a multiple of 16): two-pass split-KV, one wavefront per (sequence,
+ *      KV head, P-token partition), partials merged by a second kernel; P is
+ *      chosen so that the partitions fill the GPU.
+ * Returns 0 on invalid arguments.
  */
 int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                     int32_t max_context_len);
 
 /*
  * pkv_decode_workspace_bytes -- device scratch pkv_decode_attn needs for the
- * split-KV partials of num_seqs x num_q_heads rows at the given partition
- * length.  partition_tokens = 0 sizes for what pkv_decode_partition_tokens
- * picks with num_kv_heads = 1, which is an upper bound for every head count
- * (fewer KV heads never give a longer partition).  0 when no partials are
- * needed (every context fits one partition).
+ * split-KV partials of num_seqs x num_q_heads rows with the given
+ * partition_tokens.  0 for the single-pass kernel (partition_tokens < 0) and
+ * when every context fits one partition.  partition_tokens = 0 sizes for the
+ * two-pass split with num_kv_heads = 1, an upper bound for every head count
+ * and for whichever kernel the automatic choice picks.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_tokens);
@@ -130,11 +136,12 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   out[s][h][:] = softmax(scale * q[s][h] . K_s^T) V_s
  * over keys 0 .. context_lens[s]-1 of KV head h / G ([NVE] §3 formula and
  * decode shapes; [LLM4] §21.1 GQA).  The softmax subtracts the running
- * maximum before exponentiating ([NVE] §3.2).  The keys are split into
- * partitions of partition_tokens tokens (0 = pkv_decode_partition_tokens);
- * each (sequence, KV head, partition) is one wavefront serving the whole
- * query group, and a second pass merges the partitions' (max, sum, partial
- * output) triples.  A sequence with context_lens[s] == 0 gets out = 0.
+ * maximum before exponentiating ([NVE] §3.2).  Every wavefront serves the
+ * whole query group of its KV head, so each cached K/V byte is read once.
+ * partition_tokens selects the work split (see pkv_decode_partition_tokens):
+ *   0 = automatic, P > 0 = two-pass split-KV with P-token partitions,
+ *   -W = single-pass with W waves per (sequence, KV head).
+ * A sequence with context_lens[s] == 0 gets out = 0.
  * max_context_len: host-side upper bound of context_lens (sizes the grid).
  * workspace: device scratch of at least pkv_decode_workspace_bytes(num_seqs,
  *   num_q_heads, head_dim, max_context_len, partition_tokens) bytes; may be

@@ -29,7 +29,7 @@
 //  * Softmax is online and in fp32 with exp2 (log2 e is folded into the
 //    scale): running max m, running sum l, accumulator rescaled by
 //    exp2(m_old - m_new) -- the max subtraction of the deep-dive's §3.2.
-//  * The next block's K and V are loaded while the current block computes.
+//  * K and V stream through registers two blocks ahead of the compute.
 //  * Partitions write (m, l, unnormalised acc) to the workspace and a second
 //    kernel merges them: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
 //    A sequence that fits in one partition is written directly.
@@ -37,238 +37,278 @@
 //    never by multiplying with a zero weight, so NaN bits there cannot leak.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 
-template <int D, int G>
-struct DecodeGeom {
-    static constexpr int LPR = D / 8;                     // lanes per token row
-    static constexpr int TPL = 64 / LPR;                  // tokens per wave-wide load (rows)
-    static constexpr int NL = kBlockTokens / TPL;         // loads per block per lane
-    static constexpr int NV = NL * G;                     // partial dots per lane per block
-    static constexpr int K = NV >= LPR ? NV / LPR : 1;    // whole scores a lane keeps
-    static constexpr int REP = NV >= LPR ? 1 : LPR / NV;  // lanes holding the same score
-    static constexpr int LPH = LPR / G;                   // lanes of a row holding one head
-    static_assert(D == 64 || D == 128, "head_dim");
-    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-    // score index i = g * NL + j (head g, load j) is kept by lane-in-row
-    // holder(i), register slot(i)
-    static constexpr int holder(int i) { return NV >= LPR ? i / K : i * REP; }
-    static constexpr int slot(int i) { return NV >= LPR ? i % K : 0; }
-};
+// DPP lane-permutation controls (GFX9 encoding).  Each of the first four is
+// an involution within a row of 16 lanes that pairs lanes differing in one bit
+// b and every lower bit: row_mirror (i <-> 15-i, b = 3), row_half_mirror
+// (i <-> i^7 within 8 lanes, b = 2), quad_perm [3,2,1,0] (i <-> i^3, b = 1),
+// quad_perm [1,0,3,2] (i <-> i^1, b = 0).  Their xor masks 15, 7, 3, 1 span
+// GF(2)^4, so applying a prefix of them sums over a coset of lanes: a butterfly.
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppQuadRev = 0x1B;
+constexpr int kDppQuadSwap = 0xB1;
+constexpr int kDppRowBcast = 0x150;  // + k: every lane of a row reads lane k of the row
 
-// Butterfly reduce-scatter of N values over the `Width` lanes of a row,
-// continuing as an all-reduce once one value is left.  Lane-in-row c keeps
-// indices [c*N/Width, (c+1)*N/Width) when N >= Width, else index c / (Width/N).
-template <int Width, int N>
-__device__ __forceinline__ void row_reduce_scatter(float (&v)[N], int c) {
-    constexpr int kMax = N;
-    int n = kMax;
-#pragma unroll
-    for (int delta = Width / 2; delta >= 1; delta >>= 1) {
-        if (n > 1) {
-            const bool upper = (c & delta) != 0;
-            const int h = n / 2;
-#pragma unroll
-            for (int k = 0; k < kMax / 2; ++k) {
-                if (k < h) {
-                    const float send = upper ? v[k] : v[h + k];
-                    const float keep = upper ? v[h + k] : v[k];
-                    v[k] = keep + __shfl_xor(send, delta);
-                }
-            }
-            n = h;
-        } else {
-            v[0] += __shfl_xor(v[0], delta);
-        }
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo * b.lo + a.hi * b.hi + c on two packed bf16 pairs (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Buffer resource for `bytes` bytes at `base` (raw, 32-bit elements; reads
+// past `bytes` return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// 2^x with the hardware instruction: exact at 0 (2^0 = 1), 0 at -inf, and
+// results below the normal range flush to 0 -- all that a softmax weight needs
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
     }
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+struct DecodeGeom {
+    static constexpr int LPR = D / 8;              // lanes per token row (16 B each)
+    static constexpr int LOG_LPR = ilog2(LPR);
+    static constexpr int TPL = 64 / LPR;           // token rows per wave (tokens per load)
+    static constexpr int NL = kBlockTokens / TPL;  // loads per block per lane
+    static constexpr int M = ilog2(G);             // butterfly steps that split heads
+    static constexpr int LPH = LPR / G;            // lanes of a row that end with one head
+    static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+    static_assert(M <= LOG_LPR, "group larger than a row");
+    // butterfly step k (0-based) of a row
+    static constexpr int ctrl(int k) {
+        return LPR == 16 ? (k == 0 ? kDppRowMirror
+                                   : k == 1 ? kDppHalfMirror : k == 2 ? kDppQuadRev : kDppQuadSwap)
+                         : (k == 0 ? kDppHalfMirror : k == 1 ? kDppQuadRev : kDppQuadSwap);
+    }
+};
+
+// Step k splitting N head positions of NL tokens each: keep the first half,
+// receive the partner's copy of it.  Lane c's list holds, at position p, head
+// g(c) ^ p (g(c) = the head the lane ends with); the partner flips bit k of the
+// head and every later one, so the partner's entry for my position q sits at
+// its position N-1-q -- a fixed register for every lane, hence no selects.
+template <int CTRL, int N, int NL, int TOTAL>
+__device__ __forceinline__ void head_split_step(float (&v)[TOTAL]) {
+#pragma unroll
+    for (int q = 0; q < N / 2; ++q)
+#pragma unroll
+        for (int j = 0; j < NL; ++j) v[q * NL + j] += dpp<CTRL>(v[(N - 1 - q) * NL + j]);
+}
+
+template <typename Geo, int K, int TOTAL>
+__device__ __forceinline__ void row_butterfly(float (&v)[TOTAL]) {
+    if constexpr (K < Geo::LOG_LPR) {
+        constexpr int CTRL = Geo::ctrl(K);
+        if constexpr (K < Geo::M) {
+            head_split_step<CTRL, ((TOTAL / Geo::NL) >> K), Geo::NL>(v);
+        } else {
+#pragma unroll
+            for (int j = 0; j < Geo::NL; ++j) v[j] += dpp<CTRL>(v[j]);
+        }
+        row_butterfly<Geo, K + 1>(v);
+    }
+}
+
+// Value of x held by lane `src` of this lane's token row.
+template <typename Geo, int SRC>
+__device__ __forceinline__ float row_bcast(float x, int row_base) {
+    if constexpr (Geo::LPR == 16) {
+        return dpp<kDppRowBcast + SRC>(x);
+    } else {
+        return __shfl(x, row_base + SRC);
+    }
+}
+
+// One wavefront's attention over tokens [t_begin, t_end) (t_begin < t_end,
+// t_begin a multiple of 16) of sequence s for the G query heads of KV head
+// kvh.  On return every lane holds, for each head g of the group, the wave's
+// running max mg[g] (log2 domain), weight sum lg[g] and the unnormalised
+// output acc[g][0..7] for head_dim elements 8c .. 8c+7 (c = lane % LPR).
+template <int D, int G>
+__device__ __forceinline__ void wave_attend(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
-    const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
-    int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_tokens,
-    int32_t max_parts, float scale_log2, uint16_t *__restrict__ out, float *__restrict__ ws_out,
-    float *__restrict__ ws_ml) {
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ bt, int32_t num_blocks,
+    int32_t num_q_heads, int32_t num_kv_heads, float scale_log2, int s, int kvh, int t_begin,
+    int t_end, float (&acc)[G][8], float (&mg)[G], float (&lg)[G]) {
     using Geo = DecodeGeom<D, G>;
-    constexpr int LPR = Geo::LPR, TPL = Geo::TPL, NL = Geo::NL, NV = Geo::NV, K = Geo::K;
-    constexpr int LPH = Geo::LPH, REP = Geo::REP;
+    constexpr int LPR = Geo::LPR, TPL = Geo::TPL, NL = Geo::NL, LPH = Geo::LPH;
     const float kNegInf = -INFINITY;
 
     const int lane = threadIdx.x & 63;
-    const int part = blockIdx.x * (blockDim.x >> 6) + wave_id_uniform();
-    const int kvh = blockIdx.y;
-    const int s = blockIdx.z;
     const int row = lane / LPR;
     const int c = lane % LPR;
     const int row_base = row * LPR;
-
-    int ctx = context_lens[s];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int my_head = c / LPH;  // the head whose scores this lane ends with
     const int h0 = kvh * G;
-    if (ctx <= 0) {
-        if (part == 0) {  // empty context: the output is defined as 0
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-                if (g % TPL == row) {
-                    uint4 z = {0u, 0u, 0u, 0u};
-                    reinterpret_cast<uint4 *>(out + ((size_t)s * num_q_heads + h0 + g) * D)[c] = z;
-                }
-        }
-        return;
-    }
-    const int t_begin = part * partition_tokens;
-    if (t_begin >= ctx) return;
-    const int t_end = min(t_begin + partition_tokens, ctx);
-    const int nparts = (ctx + partition_tokens - 1) / partition_tokens;
 
-    // this lane's 8 elements of each query head of the group
-    float qf[G][8];
+    // this lane's 8 elements (4 bf16 pairs) of each query head, in the lane's
+    // butterfly order: position p holds head my_head ^ p
+    uint4 qp[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const uint4 u = reinterpret_cast<const uint4 *>(q + ((size_t)s * num_q_heads + h0 + g) * D)[c];
-        unpack8(u, qf[g]);
+    for (int p = 0; p < G; ++p) {
+        const int h = h0 + (my_head ^ p);
+        qp[p] = reinterpret_cast<const uint4 *>(q + ((size_t)s * num_q_heads + h) * D)[c];
     }
 
-    float acc[G][8];
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int x = 0; x < 8; ++x) acc[g][x] = 0.f;
-    float m = kNegInf;  // running max of this row for head g(lane), log2 domain
-    float l = 0.f;      // running sum of this lane's own weights
+    float m = kNegInf;  // running max of this row's scores for my_head (log2 domain)
+    float l = 0.f;      // running sum of this row's weights for my_head
 
-    const int32_t *bt = block_tables + (size_t)s * max_blocks_per_seq;
     const size_t tile = (size_t)kBlockTokens * D;  // elements of one (block, head) tile
     const int b_begin = t_begin / kBlockTokens;
     const int b_end = (t_end + kBlockTokens - 1) / kBlockTokens;
 
-    auto tile_ptr = [&](const uint16_t *base, int b) -> const uint4 * {
+    // Tiles are read with buffer loads: a scalar descriptor per tile (base =
+    // the tile, size = one tile) plus a fixed per-lane offset, so the loads
+    // need no per-block vector address arithmetic, and a read can never leave
+    // the tile.
+    const uint32_t lane_off = lane * 16u;
+    auto load = [&](uint4 (&kb)[NL], uint4 (&vb)[NL], int b) {
         int pb = bt[b];
         // an out-of-range id is a caller error; read block 0 instead of faulting
         pb = ((unsigned)pb < (unsigned)num_blocks) ? pb : 0;
-        return reinterpret_cast<const uint4 *>(base + ((size_t)pb * num_kv_heads + kvh) * tile) +
-               lane;
+        const size_t off = ((size_t)pb * num_kv_heads + kvh) * tile;
+        const auto kr = tile_rsrc(k_cache + off, (uint32_t)(tile * 2));
+        const auto vr = tile_rsrc(v_cache + off, (uint32_t)(tile * 2));
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            kb[j] = buffer_load16(kr, lane_off + j * 1024u);
+            vb[j] = buffer_load16(vr, lane_off + j * 1024u);
+        }
     };
 
-    uint4 kcur[NL], vcur[NL];
-    {
-        const uint4 *kp = tile_ptr(k_cache, b_begin);
-        const uint4 *vp = tile_ptr(v_cache, b_begin);
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            kcur[j] = kp[j * 64];
-            vcur[j] = vp[j * 64];
-        }
-    }
-
-    for (int b = b_begin; b < b_end; ++b) {
-        uint4 knext[NL], vnext[NL];
-        if (b + 1 < b_end) {
-            const uint4 *kp = tile_ptr(k_cache, b + 1);
-            const uint4 *vp = tile_ptr(v_cache, b + 1);
-#pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                knext[j] = kp[j * 64];
-                vnext[j] = vp[j * 64];
-            }
-        }
+    auto process = [&](const uint4 (&kb)[NL], const uint4 (&vb)[NL], int b) {
         const int tb = b * kBlockTokens;
         const bool partial = tb + kBlockTokens > t_end;
-
-        // ---- scores: partial dot products, then the row butterfly
-        float v[NV];
+        // partial dot products: v[p * NL + j] = q(head at position p) . K(token j)
+        // over my 8 elements (bf16 pair dot products accumulate in fp32; bf16 x
+        // bf16 products are exact)
+        float v[G * NL];
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
-            float kf[8];
-            unpack8(kcur[j], kf);
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float d = 0.f;
-#pragma unroll
-                for (int x = 0; x < 8; ++x) d = fmaf(qf[g][x], kf[x], d);
-                v[g * NL + j] = d;
+            for (int p = 0; p < G; ++p) {
+                float d = dot2_bf16(qp[p].w, kb[j].w, 0.f);
+                d = dot2_bf16(qp[p].z, kb[j].z, d);
+                d = dot2_bf16(qp[p].y, kb[j].y, d);
+                d = dot2_bf16(qp[p].x, kb[j].x, d);
+                v[p * NL + j] = d;
             }
         }
-        row_reduce_scatter<LPR, NV>(v, c);
+        row_butterfly<Geo, 0>(v);  // v[j] = full score of (my_head, token j of this row)
 
-        float sc[K];
-        float bmax = kNegInf;
+        float sc[NL];
+        float bm = kNegInf;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            sc[k] = v[k] * scale_log2;
-            if (partial) {
-                const int i = (NV >= LPR) ? c * K + k : c / REP;
-                const int t = tb + (i % NL) * TPL + row;
-                sc[k] = (t < t_end) ? sc[k] : kNegInf;
-            }
-            bmax = fmaxf(bmax, sc[k]);
+        for (int j = 0; j < NL; ++j) {
+            sc[j] = v[j] * scale_log2;
+            if (partial) sc[j] = (tb + j * TPL + row < t_end) ? sc[j] : kNegInf;
+            bm = fmaxf(bm, sc[j]);
         }
-#pragma unroll
-        for (int d = 1; d < LPH; d <<= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, d));
-
-        const float m_new = fmaxf(m, bmax);
+        const float m_new = fmaxf(m, bm);
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // no live token yet
-        const float alpha = exp2f(m - m_use);
-        float p[K];
+        const float alpha = fast_exp2(m - m_use);
+        float pr[NL];
         float psum = 0.f;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            p[k] = exp2f(sc[k] - m_use);
-            psum += p[k];
+        for (int j = 0; j < NL; ++j) {
+            pr[j] = fast_exp2(sc[j] - m_use);
+            psum += pr[j];
         }
-        if (REP > 1 && (c % REP) != 0) psum = 0.f;  // a replica: counted once per head
         l = l * alpha + psum;
         m = m_new;
 
-        // ---- rescale the accumulators, then add P V for this row's tokens
+        // rescale only when some row's maximum moved (alpha != 1 somewhere)
+        if (!__all(alpha == 1.f)) {
+            static_for<G>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                const float a = row_bcast<Geo, g * LPH>(alpha, row_base);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float a = __shfl(alpha, row_base + g * LPH);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc[g][x] *= a;
+                for (int x = 0; x < 8; ++x) acc[g][x] *= a;
+            });
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             float vf[8];
-            unpack8(vcur[j], vf);
+            unpack8(vb[j], vf);
             if (partial) {
                 const bool live = tb + j * TPL + row < t_end;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) vf[x] = live ? vf[x] : 0.f;
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const int i = g * NL + j;
-                const float pg = __shfl(p[Geo::slot(i)], row_base + Geo::holder(i));
+            static_for<G>([&](auto gc) {
+                constexpr int g = decltype(gc)::value;
+                const float pg = row_bcast<Geo, g * LPH>(pr[j], row_base);
 #pragma unroll
                 for (int x = 0; x < 8; ++x) acc[g][x] = fmaf(pg, vf[x], acc[g][x]);
-            }
+            });
         }
+    };
 
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            kcur[j] = knext[j];
-            vcur[j] = vnext[j];
-        }
+    // stream the blocks through three register buffers, loading two blocks
+    // ahead of the one being computed.  The prefetches are unconditional (past
+    // the end they re-read the final block, an L2 hit), so the wait before each
+    // block covers only the loads issued before it.
+    const int b_last = b_end - 1;
+    uint4 k0[NL], v0[NL], k1[NL], v1[NL], k2[NL], v2[NL];
+    load(k0, v0, b_begin);
+    load(k1, v1, min(b_begin + 1, b_last));
+    for (int b = b_begin;;) {
+        load(k2, v2, min(b + 2, b_last));
+        process(k0, v0, b);
+        if (++b >= b_end) break;
+        load(k0, v0, min(b + 2, b_last));
+        process(k1, v1, b);
+        if (++b >= b_end) break;
+        load(k1, v1, min(b + 2, b_last));
+        process(k2, v2, b);
+        if (++b >= b_end) break;
     }
 
-    // ---- merge the rows: each row holds (m, l, acc) over its own tokens
-#pragma unroll
-    for (int d = 1; d < LPH; d <<= 1) l += __shfl_xor(l, d);
-    float mg[G], lg[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float mr = __shfl(m, row_base + g * LPH);
-        const float lr = __shfl(l, row_base + g * LPH);
+    // ---- merge the rows: row r holds (m, l, acc) over its own tokens
+    static_for<G>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const float mr = row_bcast<Geo, g * LPH>(m, row_base);
+        const float lr = row_bcast<Geo, g * LPH>(l, row_base);
         float M = mr;
 #pragma unroll
         for (int d = LPR; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
-        const float f = (mr == kNegInf) ? 0.f : exp2f(mr - M);
+        const float f = (mr == kNegInf) ? 0.f : fast_exp2(mr - M);
         float L = lr * f;
 #pragma unroll
         for (int d = LPR; d < 64; d <<= 1) L += __shfl_xor(L, d);
@@ -281,7 +321,57 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         }
         mg[g] = M;
         lg[g] = L;
+    });
+}
+
+// Zero output rows of a sequence with an empty context (defined as 0).
+template <int D, int G>
+__device__ __forceinline__ void write_zero_rows(uint16_t *out, int num_q_heads, int s, int kvh) {
+    constexpr int LPR = D / 8, TPL = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        if (g % TPL == lane / LPR) {
+            const uint4 z = {0u, 0u, 0u, 0u};
+            reinterpret_cast<uint4 *>(out + ((size_t)s * num_q_heads + kvh * G + g) * D)[lane % LPR] = z;
+        }
+}
+
+// Split-KV decode: one wavefront per (sequence, KV head, partition of
+// partition_tokens tokens).  A sequence that fits one partition is written
+// directly; otherwise each partition writes (m, l, acc) for the merge pass.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_split_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_tokens,
+    int32_t max_parts, float scale_log2, uint16_t *__restrict__ out, float *__restrict__ ws_out,
+    float *__restrict__ ws_ml) {
+    constexpr int LPR = D / 8, TPL = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int part = blockIdx.x * (blockDim.x >> 6) + wave_id_uniform();
+    const int kvh = blockIdx.y;
+    const int s = blockIdx.z;
+    const int row = lane / LPR;
+    const int c = lane % LPR;
+    const int h0 = kvh * G;
+
+    int ctx = context_lens[s];
+    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    if (ctx <= 0) {
+        if (part == 0) write_zero_rows<D, G>(out, num_q_heads, s, kvh);
+        return;
     }
+    const int t_begin = part * partition_tokens;
+    if (t_begin >= ctx) return;
+    const int t_end = min(t_begin + partition_tokens, ctx);
+    const int nparts = (ctx + partition_tokens - 1) / partition_tokens;
+
+    float acc[G][8], mg[G], lg[G];
+    wave_attend<D, G>(q, k_cache, v_cache, block_tables + (size_t)s * max_blocks_per_seq,
+                      num_blocks, num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
+                      acc, mg, lg);
 
     if (nparts == 1) {
 #pragma unroll
@@ -308,6 +398,87 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                 }
             }
         }
+    }
+}
+
+// Single-pass decode: one workgroup of W wavefronts per (sequence, KV head).
+// The sequence's blocks are split evenly among the waves; each wave runs
+// wave_attend over its share and the waves merge their (m, l, acc) through
+// LDS, so no workspace and no second kernel are needed.
+template <int D, int G>
+__global__ __launch_bounds__(512) void decode_fused_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, float scale_log2,
+    uint16_t *__restrict__ out) {
+    constexpr int LPR = D / 8, TPL = 64 / LPR;
+    extern __shared__ float smem[];  // [W][G][D] acc, then [W][G] m, then [W][G] l
+    const int W = blockDim.x >> 6;
+    const int w = wave_id_uniform();
+    const int lane = threadIdx.x & 63;
+    const int kvh = blockIdx.x;
+    const int s = blockIdx.y;
+    const int row = lane / LPR;
+    const int c = lane % LPR;
+
+    int ctx = context_lens[s];
+    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    if (ctx <= 0) {
+        if (w == 0) write_zero_rows<D, G>(out, num_q_heads, s, kvh);
+        return;  // uniform over the workgroup: no barrier is skipped
+    }
+    const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
+    const int b0 = (w * nb) / W, b1 = ((w + 1) * nb) / W;
+
+    float *lds_acc = smem;
+    float *lds_m = smem + W * G * D;
+    float *lds_l = lds_m + W * G;
+    if (b0 < b1) {
+        float acc[G][8], mg[G], lg[G];
+        wave_attend<D, G>(q, k_cache, v_cache, block_tables + (size_t)s * max_blocks_per_seq,
+                          num_blocks, num_q_heads, num_kv_heads, scale_log2, s, kvh,
+                          b0 * kBlockTokens, min(b1 * kBlockTokens, ctx), acc, mg, lg);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (g % TPL == row) {
+                float4 *dst = reinterpret_cast<float4 *>(lds_acc + (w * G + g) * D + c * 8);
+                dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+                dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
+            }
+        }
+        if (lane < G) {
+            // every lane holds every head's totals; lane g publishes head g
+            float mv = mg[0], lv = lg[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) {
+                mv = (lane == g) ? mg[g] : mv;
+                lv = (lane == g) ? lg[g] : lv;
+            }
+            lds_m[w * G + lane] = mv;
+            lds_l[w * G + lane] = lv;
+        }
+    } else if (lane < G) {  // no blocks for this wave: it contributes nothing
+        lds_m[w * G + lane] = -INFINITY;
+        lds_l[w * G + lane] = 0.f;
+    }
+    __syncthreads();
+
+    // merge: thread t produces output elements t, t + 64W, ... of the G x D tile
+    for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
+        const int g = e / D;
+        float M = -INFINITY;
+        for (int u = 0; u < W; ++u) M = fmaxf(M, lds_m[u * G + g]);
+        float num = 0.f, den = 0.f;
+        for (int u = 0; u < W; ++u) {
+            const float mu = lds_m[u * G + g];
+            if (mu == -INFINITY) continue;  // an idle wave (its acc slot is unwritten)
+            const float f = fast_exp2(mu - M);
+            num = fmaf(f, lds_acc[(u * G + g) * D + (e % D)], num);
+            den = fmaf(f, lds_l[u * G + g], den);
+        }
+        out[((size_t)s * num_q_heads + kvh * G + g) * D + (e % D)] =
+            (uint16_t)f32_to_bf16_rne(num / den);
     }
 }
 
@@ -341,7 +512,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     float L = 0.f;
     const float *po = ws_out + (size_t)row_id * max_parts * D + lane * E;
     for (int p = 0; p < nparts; ++p) {
-        const float w = exp2f(ml[p * 2] - M);
+        const float w = fast_exp2(ml[p * 2] - M);
         L = fmaf(w, ml[p * 2 + 1], L);
 #pragma unroll
         for (int e = 0; e < E; ++e) a[e] = fmaf(w, po[(size_t)p * D + e], a[e]);
@@ -354,9 +525,20 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
 
 template <int D, int G>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
+    const float scale_log2 = a.scale * 1.4426950408889634f;
+    if (a.fused_waves > 0) {
+        const int W = a.fused_waves;
+        const size_t lds = (size_t)W * G * (D + 2) * sizeof(float);
+        hipLaunchKernelGGL((decode_fused_kernel<D, G>), dim3(a.num_kv_heads, a.num_seqs),
+                           dim3(64 * W), lds, stream, (const uint16_t *)a.q,
+                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache,
+                           a.block_tables, a.context_lens, a.max_blocks_per_seq,
+                           a.max_context_len, a.num_blocks, a.num_q_heads, a.num_kv_heads,
+                           scale_log2, (uint16_t *)a.out);
+        return hipGetLastError();
+    }
     const int waves = a.max_parts >= 4 ? 4 : (a.max_parts >= 2 ? 2 : 1);
     dim3 grid((a.max_parts + waves - 1) / waves, a.num_kv_heads, a.num_seqs);
-    const float scale_log2 = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(64 * waves), 0, stream,
                        (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
                        (const uint16_t *)a.v_cache, a.block_tables, a.context_lens,

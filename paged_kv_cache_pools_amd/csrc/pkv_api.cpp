@@ -77,6 +77,21 @@ int32_t partition_for(int64_t units, int32_t max_context_len) {
     return p;
 }
 
+// Waves per workgroup for the single-pass kernel, or 0 when the two-pass
+// split is the better choice.  Single-pass needs enough (sequence, KV head)
+// units to fill the GPU by itself and contexts short enough that one
+// workgroup per unit is not a straggler; it then gives each unit enough waves
+// for about four per CU, at least one block per wave.
+int32_t fused_waves_for(int64_t units, int32_t max_context_len) {
+    constexpr int64_t kMinUnits = 128, kTargetWaves = 1024;
+    constexpr int32_t kMaxContext = 8192, kMaxWaves = 8;
+    if (units < kMinUnits || max_context_len <= 0 || max_context_len > kMaxContext) return 0;
+    int32_t w = (int32_t)((kTargetWaves + units - 1) / units);
+    w = w < 1 ? 1 : (w > kMaxWaves ? kMaxWaves : w);
+    const int32_t blocks = (max_context_len + kBlock - 1) / kBlock;
+    return w > blocks ? blocks : w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,15 +138,18 @@ int pkv_store(const void *k, const void *v, const int32_t *slot_mapping, int32_t
 int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                     int32_t max_context_len) {
     if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
-    return partition_for((int64_t)num_seqs * num_kv_heads, max_context_len);
+    const int64_t units = (int64_t)num_seqs * num_kv_heads;
+    const int32_t w = fused_waves_for(units, max_context_len);
+    if (w > 0) return -w;
+    return partition_for(units, max_context_len);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_context_len, int32_t partition_tokens) {
     if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-    if (partition_tokens < 0 || partition_tokens % kBlock != 0) return 0;
-    const int32_t p = partition_tokens ? partition_tokens
-                                       : pkv_decode_partition_tokens(num_seqs, 1, max_context_len);
+    if (partition_tokens < 0) return 0;  // single-pass: no partials
+    if (partition_tokens % kBlock != 0) return 0;
+    const int32_t p = partition_tokens ? partition_tokens : partition_for(num_seqs, max_context_len);
     const int32_t parts = ceil_div(max_context_len, p);
     if (parts <= 1) return 0;
     return (size_t)num_seqs * num_q_heads * parts * (size_t)(head_dim + 2) * sizeof(float);
@@ -159,15 +177,18 @@ int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
         return fail(PKV_ERR_NULL, "q, out, context_lens or block_tables is null");
     if (!aligned16(q) || !aligned16(out))
         return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
-    if (partition_tokens < 0 || partition_tokens % kBlock != 0)
-        return fail(PKV_ERR_SHAPE, "partition_tokens %d is not a non-negative multiple of 16",
+    if (partition_tokens < -8 || (partition_tokens > 0 && partition_tokens % kBlock != 0))
+        return fail(PKV_ERR_SHAPE,
+                    "partition_tokens %d is neither a positive multiple of 16, 0, nor -1..-8",
                     partition_tokens);
-    const int32_t p = partition_tokens
-                          ? partition_tokens
-                          : pkv_decode_partition_tokens(num_seqs, cache.num_kv_heads, max_context_len);
-    const int32_t parts = max_context_len > 0 ? ceil_div(max_context_len, p) : 1;
-    const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache.head_dim,
-                                                   max_context_len, p);
+    const int32_t choice =
+        partition_tokens ? partition_tokens
+                         : pkv_decode_partition_tokens(num_seqs, cache.num_kv_heads, max_context_len);
+    const int32_t fused = choice < 0 ? -choice : 0;
+    const int32_t p = choice > 0 ? choice : kBlock;
+    const int32_t parts = fused ? 1 : (max_context_len > 0 ? ceil_div(max_context_len, p) : 1);
+    const size_t need =
+        fused ? 0 : pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache.head_dim, max_context_len, p);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (need > 0 && !aligned16(workspace))
@@ -193,6 +214,7 @@ int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
     a.head_dim = cache.head_dim;
     a.partition_tokens = p;
     a.max_parts = parts;
+    a.fused_waves = fused;
     a.scale = scale;
     a.out = out;
     float *ws = static_cast<float *>(workspace);

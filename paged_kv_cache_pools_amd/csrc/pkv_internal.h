@@ -24,6 +24,7 @@ struct DecodeArgs {
     int32_t max_blocks_per_seq, num_seqs, max_context_len;
     int32_t num_blocks, num_q_heads, num_kv_heads, head_dim;
     int32_t partition_tokens, max_parts;
+    int32_t fused_waves;  // > 0: single-pass kernel with this many waves per (seq, kv head)
     float scale;
     void *out;
     float *ws_out;  // [num_seqs][num_q_heads][max_parts][head_dim]

@@ -43,12 +43,19 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 &a, const uint4 &b, 
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// fp32 -> bf16 (nearest even) for finite values (softmax weights in [0, 1]).
-__device__ __forceinline__ uint32_t pack2_bf16_finite(float lo, float hi) {
-    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-    a += 0x7fffu + ((a >> 16) & 1u);
-    b += 0x7fffu + ((b >> 16) & 1u);
-    return (a >> 16) | (b & 0xffff0000u);
+// Split two finite fp32 softmax weights into bf16 hi and lo parts with
+// p == hi + lo to about 2^-16 relative: hi is p truncated to bf16 (its upper
+// half), lo is the exact remainder p - hi rounded to bf16.  Using both in the
+// P V product keeps the weights' rounding far below the bf16 output rounding.
+__device__ __forceinline__ void split2_bf16(float p0, float p1, uint32_t &hi, uint32_t &lo) {
+    const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
+    hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // (b0 >> 16) | (b1 & 0xffff0000)
+    const float r0 = p0 - __uint_as_float(b0 & 0xffff0000u);
+    const float r1 = p1 - __uint_as_float(b1 & 0xffff0000u);
+    uint32_t c0 = __float_as_uint(r0), c1 = __float_as_uint(r1);
+    c0 += 0x7fffu + ((c0 >> 16) & 1u);
+    c1 += 0x7fffu + ((c1 >> 16) & 1u);
+    lo = __builtin_amdgcn_perm(c1, c0, 0x07060302u);
 }
 
 template <int D, int G>
@@ -216,7 +223,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
         // ---- online softmax per column; s[kt][nt][r] is key k0 + 16 kt + 4 a + r
         const bool need_mask = (k0 + KC > wave_min_pos) || (k0 + KC > ctx);
-        uint4 pb_frag[2][4];  // P^T as the B operand, per 32-key step and N-tile
+        uint4 ph[2][4], pl[2][4];  // P^T (hi and lo parts) as the B operand, per 32-key step and N-tile
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             float bm = kNegInf;
@@ -254,10 +261,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
             // the step's first 16, k-slot (a, 4..7) <- keys 16+4a..16+4a+3
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                pb_frag[kk][nt].x = pack2_bf16_finite(s[2 * kk][nt][0], s[2 * kk][nt][1]);
-                pb_frag[kk][nt].y = pack2_bf16_finite(s[2 * kk][nt][2], s[2 * kk][nt][3]);
-                pb_frag[kk][nt].z = pack2_bf16_finite(s[2 * kk + 1][nt][0], s[2 * kk + 1][nt][1]);
-                pb_frag[kk][nt].w = pack2_bf16_finite(s[2 * kk + 1][nt][2], s[2 * kk + 1][nt][3]);
+                split2_bf16(s[2 * kk][nt][0], s[2 * kk][nt][1], ph[kk][nt].x, pl[kk][nt].x);
+                split2_bf16(s[2 * kk][nt][2], s[2 * kk][nt][3], ph[kk][nt].y, pl[kk][nt].y);
+                split2_bf16(s[2 * kk + 1][nt][0], s[2 * kk + 1][nt][1], ph[kk][nt].z, pl[kk][nt].z);
+                split2_bf16(s[2 * kk + 1][nt][2], s[2 * kk + 1][nt][3], ph[kk][nt].w, pl[kk][nt].w);
             }
         }
 
@@ -271,7 +278,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(
                 const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (kk * 32 + 16 + a * 4) * 2);
                 const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) o[mt][nt] = mfma16x16x32(vf, pb_frag[kk][nt], o[mt][nt]);
+                for (int nt = 0; nt < 4; ++nt) {
+                    o[mt][nt] = mfma16x16x32(vf, ph[kk][nt], o[mt][nt]);
+                    o[mt][nt] = mfma16x16x32(vf, pl[kk][nt], o[mt][nt]);
+                }
             }
         }
     }

@@ -52,15 +52,24 @@ def test_status_strings(lib):
 
 
 def test_partition_heuristic(lib):
-    # the 32 x 4096 GQA batch: 256 (seq, kv head) units -> 256-token partitions
-    assert B.pkv_decode_partition_tokens(32, 8, 4096) == 256
-    for s, h, ctx in ((1, 1, 1), (2, 2, 37), (256, 8, 32768), (16, 32, 2048), (1, 1, 1 << 20)):
+    # the 32 x 4096 GQA batch: 256 (seq, kv head) units -> single pass, 4 waves each
+    assert B.pkv_decode_partition_tokens(32, 8, 4096) == -4
+    # many units with long contexts, or few units: two-pass split-KV
+    assert B.pkv_decode_partition_tokens(256, 8, 32768) == 1024
+    for s, h, ctx in ((1, 1, 1), (2, 2, 37), (256, 8, 32768), (16, 32, 2048), (1, 1, 1 << 20),
+                      (32, 8, 4096), (64, 8, 16)):
         p = B.pkv_decode_partition_tokens(s, h, ctx)
-        assert p % 16 == 0 and 64 <= p <= 1024, (s, h, ctx, p)
+        assert (p % 16 == 0 and 64 <= p <= 1024) or (-8 <= p <= -1), (s, h, ctx, p)
+        if p < 0:  # at least one block per wave
+            assert -p <= -(-ctx // 16)
     assert B.pkv_decode_partition_tokens(-1, 8, 10) == 0
-    # fewer KV heads never give a longer partition: workspace(P=0) is an upper bound
+    # fewer KV heads never give a longer two-pass partition: workspace(P=0) bounds every choice
     for h in (1, 2, 8, 32):
-        assert B.pkv_decode_partition_tokens(32, h, 4096) >= B.pkv_decode_partition_tokens(32, 1, 4096)
+        for ctx in (100, 4096, 20000):
+            p = B.pkv_decode_partition_tokens(32, h, ctx)
+            if p > 0:
+                assert B.pkv_decode_workspace_bytes(32, 32, 128, ctx, p) <= \
+                    B.pkv_decode_workspace_bytes(32, 32, 128, ctx, 0)
 
 
 def test_workspace_bytes(lib):
@@ -69,9 +78,8 @@ def test_workspace_bytes(lib):
     assert B.pkv_decode_workspace_bytes(32, 32, 128, 257, 256) == 32 * 32 * 2 * 130 * 4
     assert B.pkv_decode_workspace_bytes(0, 32, 128, 4096, 256) == 0
     assert B.pkv_decode_workspace_bytes(4, 4, 64, 100, 24) == 0      # not a multiple of 16
-    p1 = B.pkv_decode_partition_tokens(32, 1, 4096)
-    assert B.pkv_decode_workspace_bytes(32, 32, 128, 4096, 0) == \
-        B.pkv_decode_workspace_bytes(32, 32, 128, 4096, p1)
+    assert B.pkv_decode_workspace_bytes(32, 32, 128, 4096, -4) == 0  # single pass
+    assert B.pkv_decode_workspace_bytes(32, 32, 128, 4096, 0) == 32 * 32 * 64 * 130 * 4
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on these paths
@@ -103,6 +111,7 @@ def decode(lib, c=None, q=FAKE, out=FAKE, hq=4, s=2, max_ctx=37, max_blocks=3, w
     (dict(ws=0, max_ctx=37, part=16), 5),  # needs partials, no workspace
     (dict(ws_bytes=16, max_ctx=37, part=16), 5),
     (dict(part=24), 2),
+    (dict(part=-9), 2),
     (dict(c=cache(nb=0)), 2),
 ])
 def test_decode_rejects_before_launch(lib, kwargs, status):

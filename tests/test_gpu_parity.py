@@ -83,7 +83,7 @@ def test_decode_qwen_mha():
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
-@pytest.mark.parametrize("part", [16, 64, 0])
+@pytest.mark.parametrize("part", [16, 64, 0, -1, -3, -8])
 def test_decode_edge_lengths(d, g, part):
     lens = [1, 15, 16, 17, 32, 63, 64, 65, 129, 0, 2]
     wl = W.make_decode(f"edge_d{d}_g{g}", lens, 2 * g, 2, d, 100 + d + g, spare_blocks=3)
@@ -103,16 +103,17 @@ def test_decode_single_token_exact():
             assert np.array_equal(got[s, h], c.h["v_new"][s, h // 4]), (s, h)
 
 
-def test_decode_empty_context_is_zero():
+@pytest.mark.parametrize("part", [16, -2])
+def test_decode_empty_context_is_zero(part):
     wl = W.make_decode("ctx0", [0, 40, 0], 4, 2, 64, 52, store=False)
     c = Case(wl)
-    out = c.gpu_decode(partition_tokens=16)
+    out = c.gpu_decode(partition_tokens=part)
     torch.cuda.synchronize()
     assert np.all(to_f64(out)[[0, 2]] == 0.0)
     compare(out, c.oracle_decode(), "decode ctx0")
 
 
-@pytest.mark.parametrize("part", [16, 48, 256, 1024])
+@pytest.mark.parametrize("part", [16, 48, 256, 1024, -2, -8])
 def test_decode_partition_sizes(part):
     wl = W.make_decode("parts", [300, 1000, 17, 2048], 16, 4, 128, 53)
     run_decode_full(wl, partition_tokens=part)
@@ -194,6 +195,8 @@ def run_decode_sampled(wl, seqs, layers=1):
 
 
 def test_decode_mistral_gqa_full_size():
+    """32 x 4096 GQA batch: the automatic choice is the single-pass kernel."""
+    assert B.pkv_decode_partition_tokens(32, 8, 4096) < 0
     run_decode_sampled(W.mistral_gqa(num_layers=2), [0, 9, 31], layers=2)
 
 
