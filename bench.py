@@ -91,12 +91,40 @@ def prefill_flops(wl) -> float:
     return 4.0 * wl.head_dim * wl.num_q_heads * tot
 
 
-def cpu_baseline(wl, t, seconds):
-    """Time the fp64 oracle (as it stands) on whole layers of the same workload:
-    host copies of one layer's pools, store + decode, repeated until about
-    ``seconds`` of CPU time; tokens/s per layer = sequences / time per layer."""
-    import torch  # noqa: F401
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` as measured by rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by a plain-copy calibration) and recorded in a
+    ``traffic_record:`` line of a summary under profiles/.  The record lists
+    the sha256 of the kernel's source files when the counters were taken; if
+    any of them has changed since, the figure no longer describes this kernel
+    and None is returned."""
+    import glob
+    import hashlib
 
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path, encoding="utf-8"):
+            if not line.startswith("traffic_record:"):
+                continue
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("kernel") != kernel:
+                continue
+            same = all(
+                os.path.exists(os.path.join(ROOT, f)) and hashlib.sha256(
+                    open(os.path.join(ROOT, f), "rb").read()).hexdigest() == h
+                for f, h in rec["sources"].items())
+            return int(rec["bytes_per_launch"]) if same else None
+    return None
+
+
+def cpu_baseline(wl, t, seconds):
+    """Time the fp64 oracle (as it stands) on whole layers of the same workload.
+
+    Host copies of two layers' pools are taken once (outside the timing); each
+    timed unit is one layer's store + decode over all sequences, alternating
+    between the two copies.  The store rewrites the same slots with the same
+    bits, so every repetition does identical work.  Repeats until about
+    ``seconds`` of wall time inside the oracle; tokens/s per layer =
+    sequences / time per layer."""
     import oracle
     from paged_kv_cache_pools_amd import workloads as W
 
@@ -105,25 +133,24 @@ def cpu_baseline(wl, t, seconds):
     q = W.bf16_bits(t["q"][0])
     kn = W.bf16_bits(t["k_new"][0])
     vn = W.bf16_bits(t["v_new"][0])
+    pools = [(W.bf16_bits(k).copy(), W.bf16_bits(v).copy())
+             for k, v in zip(t["k_caches"], t["v_caches"])]
     layers_done, spent = 0, 0.0
-    while True:
-        kc = W.bf16_bits(t["k_caches"][layers_done % len(t["k_caches"])]).copy()
-        vc = W.bf16_bits(t["v_caches"][layers_done % len(t["v_caches"])]).copy()
+    while spent < seconds and layers_done < 4096:
+        kc, vc = pools[layers_done % len(pools)]
         t0 = time.perf_counter()
         orc.store(kn, vn, wl.slot_mapping, kc, vc)
         orc.decode(q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, nthreads=threads)
         spent += time.perf_counter() - t0
         layers_done += 1
-        del kc, vc
-        if spent >= seconds or layers_done >= 64:
-            break
     per_layer = spent / layers_done
     return {
         "value": wl.num_seqs / per_layer, "unit": "tokens/s per layer", "cores": threads,
         "kind": "oracle",
-        "sample": f"{layers_done} whole layer(s) of the same batch (store + decode, "
-                  f"{wl.num_seqs} seqs x {wl.max_context_len} tokens), fp64 C oracle, "
-                  f"{per_layer * 1e3:.1f} ms per layer",
+        "sample": f"{layers_done} layer(s) of the same batch (store + decode of all "
+                  f"{wl.num_seqs} seqs x {wl.max_context_len} tokens, alternating two layer "
+                  f"pools), fp64 C oracle on {threads} threads, {per_layer * 1e3:.1f} ms per "
+                  f"layer, {spent:.1f} s in total",
         "kv_gbs": decode_bytes(wl) / per_layer / 1e9,
     }
 
@@ -209,6 +236,8 @@ def main():
     kv_bytes_step = L * (dbytes + sbytes)
     value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
     achieved = dbytes / (dec_avg_ms * 1e-3) / 1e9
+    kernel = (f"decode_fused_kernel<{D},{Hq // Hkv}>" if P < 0
+              else f"decode_split_kernel<{D},{Hq // Hkv}>+decode_reduce_kernel<{D}>")
     result = {
         "metric": "decode attention KV GB/s and % of MI355X HBM peak; tokens/s per layer",
         "value": round(value, 2),
@@ -231,10 +260,10 @@ def main():
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
         "decode_us_per_layer": round(dec_avg_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": ("pkv decode_fused_kernel" if P < 0
-                                               else "pkv decode_split_kernel + decode_reduce_kernel"),
+        "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(kernel),
                      "algorithmic_bytes_per_launch": dbytes},
         "wall_s_timed": round(wall, 3),
     }
