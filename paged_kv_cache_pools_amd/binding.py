@@ -45,6 +45,10 @@ def load(path: str = LIB_PATH):
     global _lib_handle
     if _lib_handle is not None:
         return _lib_handle
+    # torch first: its HIP runtime (same soname as ROCm's) must be the one the
+    # process loads, so that libpkv launches on the runtime that owns torch's
+    # memory and streams.  Loading libpkv first pulls in a second copy.
+    import torch  # noqa: F401
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_cache_pools_amd.build`"
                            " (the HIP library is the only implementation; there is no fallback)")

