@@ -30,17 +30,25 @@ def to_f64(t):
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def compare(got, ref, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
-    """got: bf16 torch tensor (GPU), ref: float64 numpy.  Returns the stats."""
+def compare(got, ref, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS, plus_floor=False):
+    """got: bf16 torch tensor (GPU), ref: float64 numpy.  Returns the stats.
+
+    With ``plus_floor`` each element may also differ by its own bf16 rounding
+    (|bf16(ref) - ref|) on top of ``max_abs``: outputs of magnitude 4 or more
+    cannot be held to 1e-2 by any bf16 result (half an ulp there is 0.0156),
+    which only sharpened scales produce."""
     g = to_f64(got)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     err = np.abs(g - ref)
     floor = np.abs(torch.from_numpy(ref).to(torch.bfloat16).to(torch.float64).numpy() - ref)
-    stats = dict(max=float(err.max()), mean=float(err.mean()), floor_mean=float(floor.mean()))
+    stats = dict(max=float(err.max()), mean=float(err.mean()), floor_mean=float(floor.mean()),
+                 max_over_floor=float((err - floor).max()))
     say(f"    {what}: max|err| {stats['max']:.3e} mean|err| {stats['mean']:.3e} "
-        f"(bf16 rounding floor mean {stats['floor_mean']:.3e})")
-    assert stats["max"] <= max_abs and stats["mean"] <= mean_abs, (what, stats)
+        f"(bf16 rounding floor mean {stats['floor_mean']:.3e}; "
+        f"max beyond floor {stats['max_over_floor']:.3e})")
+    bound = max_abs + floor if plus_floor else max_abs
+    assert np.all(err <= bound) and stats["mean"] <= mean_abs, (what, stats)
     return stats
 
 

@@ -258,3 +258,37 @@ def test_prefill_chunked_full_size():
     q = h["q"][pos]
     ref = orc().decode(q, h["kc"], h["vc"], np.stack(bts), np.array(ctxs, np.int32), wl.scale)
     compare(out[torch.from_numpy(rows).cuda()], ref, "prefill chunked (sampled rows)")
+
+
+# ---------------------------------------------------------------------------
+# scale edge cases: zero (every visible key weighs the same) and negative
+# (prefill applies it by flipping q's sign bits).  Sharp scales push outputs
+# toward single V values, some of magnitude >= 4, so the bound adds each
+# element's own bf16 rounding to 1e-2.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
+def test_prefill_scale_edges(scale):
+    wl = W.make_prefill("prefill_scale", [0, 37, 130], [70, 16, 65], 8, 2, 128, 61,
+                        scale=scale, spare_blocks=1)
+    c = Case(wl)
+    say(f"[gpu] prefill scale {scale}")
+    c.gpu_store()
+    out = c.gpu_prefill()
+    torch.cuda.synchronize()
+    c.oracle_store()
+    compare(out, c.oracle_prefill(), f"prefill scale {scale}", plus_floor=True)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
+@pytest.mark.parametrize("part", [0, 32])
+def test_decode_scale_edges(scale, part):
+    wl = W.make_decode("decode_scale", [1, 40, 300, 17], 8, 2, 128, 62, scale=scale,
+                       spare_blocks=1)
+    c = Case(wl)
+    say(f"[gpu] decode scale {scale} P={part}")
+    c.gpu_store()
+    out = c.gpu_decode(partition_tokens=part)
+    torch.cuda.synchronize()
+    c.oracle_store()
+    compare(out, c.oracle_decode(), f"decode scale {scale}", plus_floor=True)
