@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
-"""Benchmark: paged-KV decode step (store + split-KV decode attention) on one GPU.
+"""Benchmark: paged-KV decode step (store + decode attention) on one GPU.
 
 Workload (default): the Mistral-7B-style GQA batch -- 32 sequences x 4096
 cached tokens, 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks,
 32 independent layer pools (16 GiB of KV).  One step = for each of the 32
 layers: store the new token of every sequence (slot mapping), then decode
-attention over the whole cache.  Inputs are synthetic N(0,1) values rounded to
-bf16 and a seeded random physical-block permutation, resident in HBM before
-the timed region.
+attention over the whole cache including it -- one pkv_store_decode_attn
+launch per layer (``--separate``: pkv_store then pkv_decode_attn).  Inputs are
+synthetic N(0,1) values rounded to bf16 and a seeded random physical-block
+permutation, resident in HBM before the timed region.
 
-Prints ONE JSON line.  ``value`` is the decode attention's KV read rate over
-the whole step (algorithmic KV bytes of all layers / step time), in GB/s.
+Prints ONE JSON line.  ``value`` is the step's algorithmic KV-cache traffic
+(decode reads plus the store's reads and writes, all layers) / step time, in
+GB/s.  ``roofline`` is the per-layer launch, timed with HIP events on the
+stream it runs on.  The chunked-prefill leg and the fp64 oracle on the host
+cores are reported beside it.
 """
 from __future__ import annotations
 
@@ -37,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--separate", action="store_true",
+                    help="time pkv_store + pkv_decode_attn as two launches per layer instead of "
+                         "the fused pkv_store_decode_attn")
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -196,48 +203,74 @@ def main():
     ws = torch.empty(max(16, B.pkv_decode_workspace_bytes(S, Hq, D, wl.max_context_len, P)),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(L)]
 
-    def step(record=False):
-        for l in range(L):
+    def launch(l):
+        if args.separate:
             B.pkv_store(t["k_new"][l], t["v_new"][l], slots, t["k_caches"][l], t["v_caches"][l])
-            if record:
-                ev[l][0].record(stream)
             B.pkv_decode_attn(t["q"][l], t["k_caches"][l], t["v_caches"][l], bt, ctx, wl.scale,
                               outs[l], max_context_len=wl.max_context_len, workspace=ws,
                               partition_tokens=P)
-            if record:
-                ev[l][1].record(stream)
+        else:
+            B.pkv_store_decode_attn(t["k_new"][l], t["v_new"][l], slots, t["q"][l],
+                                    t["k_caches"][l], t["v_caches"][l], bt, ctx, wl.scale,
+                                    outs[l], max_context_len=wl.max_context_len, workspace=ws,
+                                    partition_tokens=P)
+
+    def step():
+        for l in range(L):
+            launch(l)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # (1) the timed region: K steps, nothing but the launches between the two
+    # events (a HIP event pair around every launch costs several us of GPU
+    # time per layer, so per-launch timing has a pass of its own below)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dec_ms = []
     wall0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        step(record=True)
-        # per-launch decode durations of this step (read after the final sync)
-        dec_ms.append(list(ev))
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(L)]
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
-    per_launch = [a.elapsed_time(b) for step_ev in dec_ms for a, b in step_ev]
-    dec_avg_ms = float(np.mean(per_launch))
     ms_per_step = total_ms / args.steps
+
+    # (2) per-launch durations for the roofline: the same K steps again, each
+    # layer's launch(es) bracketed by HIP events on the stream they run on
+    pairs = []
+    for _ in range(args.steps):
+        for l in range(L):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if args.separate:  # time the decode launch only
+                B.pkv_store(t["k_new"][l], t["v_new"][l], slots, t["k_caches"][l],
+                            t["v_caches"][l])
+                a.record(stream)
+                B.pkv_decode_attn(t["q"][l], t["k_caches"][l], t["v_caches"][l], bt, ctx,
+                                  wl.scale, outs[l], max_context_len=wl.max_context_len,
+                                  workspace=ws, partition_tokens=P)
+            else:
+                a.record(stream)
+                launch(l)
+            b.record(stream)
+            pairs.append((a, b))
+    torch.cuda.synchronize()
+    per_launch = [a.elapsed_time(b) for a, b in pairs]
+    dec_avg_ms = float(np.mean(per_launch))
 
     dbytes = decode_bytes(wl)
     sbytes = store_bytes(wl)
     kv_bytes_step = L * (dbytes + sbytes)
     value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
-    achieved = dbytes / (dec_avg_ms * 1e-3) / 1e9
+    # the timed launch per layer: decode alone, or the fused store + decode
+    launch_bytes = dbytes if args.separate else dbytes + sbytes
+    achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
     kernel = (f"decode_fused_kernel<{D},{Hq // Hkv}>" if P < 0
               else f"decode_split_kernel<{D},{Hq // Hkv}>+decode_reduce_kernel<{D}>")
+    if not args.separate:
+        kernel += " (fused store)"
     result = {
         "metric": "decode attention KV GB/s and % of MI355X HBM peak; tokens/s per layer",
         "value": round(value, 2),
@@ -256,15 +289,17 @@ def main():
                    "num_seqs": S, "context_len": int(wl.max_context_len), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": 16, "layers": L,
                    "work_split": (f"single pass, {-P} waves per (seq, kv head)" if P < 0
-                                  else f"split-KV, {P}-token partitions + merge")},
+                                  else f"split-KV, {P}-token partitions + merge"),
+                   "launches_per_layer": ("pkv_store + pkv_decode_attn" if args.separate
+                                          else "pkv_store_decode_attn (store fused)")},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
-        "decode_us_per_layer": round(dec_avg_ms * 1e3, 2),
+        "decode_us_per_layer": round(dec_avg_ms * 1e3, 2),  # the timed launch (see kernel)
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(kernel),
-                     "algorithmic_bytes_per_launch": dbytes},
+                     "algorithmic_bytes_per_launch": launch_bytes},
         "wall_s_timed": round(wall, 3),
     }
 

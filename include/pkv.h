@@ -154,6 +154,32 @@ int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
                     hipStream_t stream);
 
 /*
+ * pkv_store_decode_attn -- one decode step of a layer in one launch: the
+ * store of each sequence's new token followed by decode attention over the
+ * cache including it.  Equivalent to
+ *   pkv_store(k, v, slot_mapping, num_seqs, cache, stream);
+ *   pkv_decode_attn(q, cache, ..., stream);
+ * ([NVE] §2.1: decode appends the new token's K and V, then attends over the
+ * whole cache including it), with one new token per sequence:
+ *   k, v          bf16 [num_seqs][cache.num_kv_heads][cache.head_dim], device
+ *   slot_mapping  int32 [num_seqs]: sequence s's token goes to slot
+ *                 slot_mapping[s] (< 0 skips the store)
+ * and every other argument as for pkv_decode_attn.  Within the launch the
+ * attention of sequence s takes its last position's K/V from k[s], v[s] when
+ * slot_mapping[s] is the slot the block table gives that position (the usual
+ * case), and from the cache otherwise.  Precondition, beyond pkv_decode_attn's:
+ * a stored slot is read in this call by no position other than its own
+ * sequence's last one (true whenever the slot lies in a block only its
+ * sequence references, as an appended token's slot does).
+ */
+int pkv_store_decode_attn(const void *k, const void *v, const int32_t *slot_mapping,
+                          const void *q, pkv_cache cache, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                          float scale, void *out, void *workspace, size_t workspace_bytes,
+                          int32_t partition_tokens, hipStream_t stream);
+
+/*
  * pkv_prefill_attn -- chunked causal prefill over the paged cache.  Prompt p
  * has n_p = cu_new_lens[p+1] - cu_new_lens[p] new tokens whose K/V are
  * already stored after c_p = context_lens[p] - n_p cached ones.  New token i

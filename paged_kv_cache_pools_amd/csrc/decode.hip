@@ -158,6 +158,18 @@ __device__ __forceinline__ float row_bcast(float x, int row_base) {
     }
 }
 
+// The new token of a fused store + decode, as seen by the one wavefront whose
+// span holds the sequence's last position: `src_k`/`src_v` point at the
+// token's K/V row for this KV head (null when nothing is stored), `dst_k`/
+// `dst_v` at its cache row (null when the slot is skipped), and `pos` is the
+// position whose cached K/V the row replaces in this wave's arithmetic (-1
+// when the slot is not that position's).
+struct NewToken {
+    const uint4 *src_k = nullptr, *src_v = nullptr;
+    uint4 *dst_k = nullptr, *dst_v = nullptr;
+    int pos = -1;
+};
+
 // One wavefront's attention over tokens [t_begin, t_end) (t_begin < t_end,
 // t_begin a multiple of 16) of sequence s for the G query heads of KV head
 // kvh.  On return every lane holds, for each head g of the group, the wave's
@@ -165,10 +177,10 @@ __device__ __forceinline__ float row_bcast(float x, int row_base) {
 // output acc[g][0..7] for head_dim elements 8c .. 8c+7 (c = lane % LPR).
 template <int D, int G>
 __device__ __forceinline__ void wave_attend(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ bt, int32_t num_blocks,
-    int32_t num_q_heads, int32_t num_kv_heads, float scale_log2, int s, int kvh, int t_begin,
-    int t_end, float (&acc)[G][8], float (&mg)[G], float (&lg)[G]) {
+    const uint16_t *__restrict__ q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const int32_t *__restrict__ bt, int32_t num_blocks, int32_t num_q_heads,
+    int32_t num_kv_heads, float scale_log2, int s, int kvh, int t_begin, int t_end,
+    const NewToken &nt, float (&acc)[G][8], float (&mg)[G], float (&lg)[G]) {
     using Geo = DecodeGeom<D, G>;
     constexpr int LPR = Geo::LPR, TPL = Geo::TPL, NL = Geo::NL, LPH = Geo::LPH;
     const float kNegInf = -INFINITY;
@@ -205,13 +217,18 @@ __device__ __forceinline__ void wave_attend(
     // need no per-block vector address arithmetic, and a read can never leave
     // the tile.
     const uint32_t lane_off = lane * 16u;
+    const int b_last = b_end - 1;
+    // Prefetches run up to two blocks past the span; those get an empty
+    // buffer range, so they still count as issued loads (the waits stay
+    // static) but fetch nothing and return zeros.
     auto load = [&](uint4 (&kb)[NL], uint4 (&vb)[NL], int b) {
-        int pb = bt[b];
+        int pb = bt[min(b, b_last)];
         // an out-of-range id is a caller error; read block 0 instead of faulting
         pb = ((unsigned)pb < (unsigned)num_blocks) ? pb : 0;
         const size_t off = ((size_t)pb * num_kv_heads + kvh) * tile;
-        const auto kr = tile_rsrc(k_cache + off, (uint32_t)(tile * 2));
-        const auto vr = tile_rsrc(v_cache + off, (uint32_t)(tile * 2));
+        const uint32_t bytes = b <= b_last ? (uint32_t)(tile * 2) : 0u;
+        const auto kr = tile_rsrc(k_cache + off, bytes);
+        const auto vr = tile_rsrc(v_cache + off, bytes);
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             kb[j] = buffer_load16(kr, lane_off + j * 1024u);
@@ -219,9 +236,42 @@ __device__ __forceinline__ void wave_attend(
         }
     };
 
-    auto process = [&](const uint4 (&kb)[NL], const uint4 (&vb)[NL], int b) {
+    // fused store: this wave holds the sequence's last position, so it writes
+    // the new token's row to its cache slot and, when that slot is the last
+    // position's, uses the row in place of what it loads from there (nothing
+    // in this launch reads the slot after the write)
+    // (uint4 is a struct: its selects are written per 32-bit word, which keeps
+    // everything in registers)
+    const int patch_block = nt.pos >= 0 ? nt.pos / kBlockTokens : -1;
+    const int patch_load = (nt.pos % kBlockTokens) / TPL;
+    const bool patch_row = row == (nt.pos % kBlockTokens) % TPL;
+    uint4 kn = make_uint4(0u, 0u, 0u, 0u), vn = kn;
+    if (nt.src_k != nullptr) {  // uniform: only the wave holding the last position
+        kn = nt.src_k[c];
+        vn = nt.src_v[c];
+        if (nt.dst_k != nullptr && row == 0) {
+            nt.dst_k[c] = kn;
+            nt.dst_v[c] = vn;
+        }
+    }
+    auto patch = [&](uint4 &x, const uint4 &y, bool here) {
+        x.x = here ? y.x : x.x;
+        x.y = here ? y.y : x.y;
+        x.z = here ? y.z : x.z;
+        x.w = here ? y.w : x.w;
+    };
+
+    auto process = [&](uint4 (&kb)[NL], uint4 (&vb)[NL], int b) {
         const int tb = b * kBlockTokens;
         const bool partial = tb + kBlockTokens > t_end;
+        if (b == patch_block) {
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                const bool here = j == patch_load && patch_row;
+                patch(kb[j], kn, here);
+                patch(vb[j], vn, here);
+            }
+        }
         // partial dot products: v[p * NL + j] = q(head at position p) . K(token j)
         // over my 8 elements (bf16 pair dot products accumulate in fp32; bf16 x
         // bf16 products are exact)
@@ -289,20 +339,19 @@ __device__ __forceinline__ void wave_attend(
 
     // stream the blocks through three register buffers, loading two blocks
     // ahead of the one being computed.  The prefetches are unconditional (past
-    // the end they re-read the final block, an L2 hit), so the wait before each
-    // block covers only the loads issued before it.
-    const int b_last = b_end - 1;
+    // the end they fetch nothing), so the wait before each block covers only
+    // the loads issued before it.
     uint4 k0[NL], v0[NL], k1[NL], v1[NL], k2[NL], v2[NL];
     load(k0, v0, b_begin);
-    load(k1, v1, min(b_begin + 1, b_last));
+    load(k1, v1, b_begin + 1);
     for (int b = b_begin;;) {
-        load(k2, v2, min(b + 2, b_last));
+        load(k2, v2, b + 2);
         process(k0, v0, b);
         if (++b >= b_end) break;
-        load(k0, v0, min(b + 2, b_last));
+        load(k0, v0, b + 2);
         process(k1, v1, b);
         if (++b >= b_end) break;
-        load(k1, v1, min(b + 2, b_last));
+        load(k1, v1, b + 2);
         process(k2, v2, b);
         if (++b >= b_end) break;
     }
@@ -344,17 +393,59 @@ __device__ __forceinline__ void write_zero_rows(uint16_t *out, int num_q_heads, 
         }
 }
 
+// The fused store's new token for (sequence s, KV head kvh) of a sequence
+// with ctx cached tokens (the new one included): its K/V rows, its cache row
+// when slots[s] names a slot in the pool, and the position it stands for when
+// that slot is where the block table puts position ctx - 1.  Empty when the
+// launch stores nothing (slots == null).
+template <int D>
+__device__ __forceinline__ NewToken new_token(const uint16_t *k_new, const uint16_t *v_new,
+                                              const int32_t *slots, uint16_t *k_cache,
+                                              uint16_t *v_cache, const int32_t *bt_row,
+                                              int32_t num_blocks, int32_t num_kv_heads, int s,
+                                              int kvh, int ctx) {
+    NewToken t;
+    if (slots == nullptr) return t;
+    const size_t src = ((size_t)s * num_kv_heads + kvh) * D;
+    t.src_k = reinterpret_cast<const uint4 *>(k_new + src);
+    t.src_v = reinterpret_cast<const uint4 *>(v_new + src);
+    const int slot = slots[s];
+    if (slot < 0 || slot / kBlockTokens >= num_blocks) return t;  // skipped: nothing written
+    const size_t dst =
+        (((size_t)(slot / kBlockTokens) * num_kv_heads + kvh) * kBlockTokens + slot % kBlockTokens) * D;
+    t.dst_k = reinterpret_cast<uint4 *>(k_cache + dst);
+    t.dst_v = reinterpret_cast<uint4 *>(v_cache + dst);
+    if (ctx > 0) {
+        const int last = ctx - 1;
+        if ((int64_t)bt_row[last / kBlockTokens] * kBlockTokens + last % kBlockTokens == slot)
+            t.pos = last;
+    }
+    return t;
+}
+
+// Write the new token's rows (fused store of a sequence with an empty context).
+template <int D>
+__device__ __forceinline__ void store_only(const NewToken &t) {
+    const int lane = threadIdx.x & 63;
+    if (t.dst_k != nullptr && lane < D / 8) {
+        t.dst_k[lane] = t.src_k[lane];
+        t.dst_v[lane] = t.src_v[lane];
+    }
+}
+
 // Split-KV decode: one wavefront per (sequence, KV head, partition of
 // partition_tokens tokens).  A sequence that fits one partition is written
 // directly; otherwise each partition writes (m, l, acc) for the merge pass.
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_split_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_tokens,
     int32_t max_parts, float scale_log2, uint16_t *__restrict__ out, float *__restrict__ ws_out,
-    float *__restrict__ ws_ml) {
+    float *__restrict__ ws_ml, const uint16_t *__restrict__ k_new,
+    const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, uint16_t *k_store,
+    uint16_t *v_store) {
     constexpr int LPR = D / 8, TPL = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int part = blockIdx.x * (blockDim.x >> 6) + wave_id_uniform();
@@ -366,19 +457,28 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
     int ctx = context_lens[s];
     ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;
     if (ctx <= 0) {
-        if (part == 0) write_zero_rows<D, G>(out, num_q_heads, s, kvh);
+        if (part == 0) {
+            write_zero_rows<D, G>(out, num_q_heads, s, kvh);
+            store_only<D>(new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks,
+                                       num_kv_heads, s, kvh, ctx));
+        }
         return;
     }
     const int t_begin = part * partition_tokens;
     if (t_begin >= ctx) return;
     const int t_end = min(t_begin + partition_tokens, ctx);
     const int nparts = (ctx + partition_tokens - 1) / partition_tokens;
+    // the partition holding the last position carries the fused store
+    NewToken nt;
+    if (t_end == ctx)
+        nt = new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks, num_kv_heads,
+                          s, kvh, ctx);
 
     float acc[G][8], mg[G], lg[G];
-    wave_attend<D, G>(q, k_cache, v_cache, block_tables + (size_t)s * max_blocks_per_seq,
-                      num_blocks, num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
-                      acc, mg, lg);
+    wave_attend<D, G>(q, k_cache, v_cache, bt_row, num_blocks, num_q_heads, num_kv_heads,
+                      scale_log2, s, kvh, t_begin, t_end, nt, acc, mg, lg);
 
     if (nparts == 1) {
 #pragma unroll
@@ -414,11 +514,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 // LDS, so no workspace and no second kernel are needed.
 template <int D, int G>
 __global__ __launch_bounds__(512) void decode_fused_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ q, const uint16_t *k_cache, const uint16_t *v_cache,
+    const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, float scale_log2,
-    uint16_t *__restrict__ out) {
+    uint16_t *__restrict__ out, const uint16_t *__restrict__ k_new,
+    const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, uint16_t *k_store,
+    uint16_t *v_store) {
     constexpr int LPR = D / 8, TPL = 64 / LPR;
     extern __shared__ float smem[];  // [W][G][D] acc, then [W][G] m, then [W][G] l
     const int W = blockDim.x >> 6;
@@ -431,21 +533,31 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
 
     int ctx = context_lens[s];
     ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;
     if (ctx <= 0) {
-        if (w == 0) write_zero_rows<D, G>(out, num_q_heads, s, kvh);
+        if (w == 0) {
+            write_zero_rows<D, G>(out, num_q_heads, s, kvh);
+            store_only<D>(new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks,
+                                       num_kv_heads, s, kvh, ctx));
+        }
         return;  // uniform over the workgroup: no barrier is skipped
     }
     const int nb = (ctx + kBlockTokens - 1) / kBlockTokens;
     const int b0 = (w * nb) / W, b1 = ((w + 1) * nb) / W;
+    // the wave holding the last block carries the fused store
+    NewToken nt;
+    if (b0 < b1 && b1 == nb)
+        nt = new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks, num_kv_heads,
+                          s, kvh, ctx);
 
     float *lds_acc = smem;
     float *lds_m = smem + W * G * D;
     float *lds_l = lds_m + W * G;
     if (b0 < b1) {
         float acc[G][8], mg[G], lg[G];
-        wave_attend<D, G>(q, k_cache, v_cache, block_tables + (size_t)s * max_blocks_per_seq,
-                          num_blocks, num_q_heads, num_kv_heads, scale_log2, s, kvh,
-                          b0 * kBlockTokens, min(b1 * kBlockTokens, ctx), acc, mg, lg);
+        wave_attend<D, G>(q, k_cache, v_cache, bt_row, num_blocks, num_q_heads, num_kv_heads,
+                          scale_log2, s, kvh, b0 * kBlockTokens, min(b1 * kBlockTokens, ctx), nt,
+                          acc, mg, lg);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (g % TPL == row) {
@@ -541,7 +653,9 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                            (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache,
                            a.block_tables, a.context_lens, a.max_blocks_per_seq,
                            a.max_context_len, a.num_blocks, a.num_q_heads, a.num_kv_heads,
-                           scale_log2, (uint16_t *)a.out);
+                           scale_log2, (uint16_t *)a.out, (const uint16_t *)a.k_new,
+                           (const uint16_t *)a.v_new, a.slots, (uint16_t *)a.k_store,
+                           (uint16_t *)a.v_store);
         return hipGetLastError();
     }
     const int waves = a.max_parts >= 4 ? 4 : (a.max_parts >= 2 ? 2 : 1);
@@ -551,7 +665,9 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                        (const uint16_t *)a.v_cache, a.block_tables, a.context_lens,
                        a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.num_q_heads,
                        a.num_kv_heads, a.partition_tokens, a.max_parts, scale_log2,
-                       (uint16_t *)a.out, a.ws_out, a.ws_ml);
+                       (uint16_t *)a.out, a.ws_out, a.ws_ml, (const uint16_t *)a.k_new,
+                       (const uint16_t *)a.v_new, a.slots, (uint16_t *)a.k_store,
+                       (uint16_t *)a.v_store);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1) return e;
     const int rows = a.num_seqs * a.num_q_heads;

@@ -155,11 +155,19 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
     return (size_t)num_seqs * num_q_heads * parts * (size_t)(head_dim + 2) * sizeof(float);
 }
 
-int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
-                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
-                    int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
-                    void *workspace, size_t workspace_bytes, int32_t partition_tokens,
-                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by pkv_decode_attn and pkv_store_decode_attn: validation, the work
+// split and the launch.  `fused` carries the store's k, v and slots (all null
+// for plain decode).
+int decode_call(const void *q, pkv_cache cache, const int32_t *block_tables,
+                int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                void *workspace, size_t workspace_bytes, int32_t partition_tokens,
+                hipStream_t stream, const void *k_new, const void *v_new, const int32_t *slots,
+                const char *what) {
     int rc = check_cache(cache);
     if (rc) return rc;
     if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
@@ -220,7 +228,45 @@ int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
     float *ws = static_cast<float *>(workspace);
     a.ws_out = need ? ws : nullptr;
     a.ws_ml = need ? ws + (size_t)num_seqs * num_q_heads * parts * cache.head_dim : nullptr;
-    return hip_status(pkv::launch_decode(a, stream), "pkv_decode_attn launch");
+    if (slots != nullptr) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.slots = slots;
+        a.k_store = cache.k;
+        a.v_store = cache.v;
+    }
+    return hip_status(pkv::launch_decode(a, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                    int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                    void *workspace, size_t workspace_bytes, int32_t partition_tokens,
+                    hipStream_t stream) {
+    return decode_call(q, cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       max_context_len, num_q_heads, scale, out, workspace, workspace_bytes,
+                       partition_tokens, stream, nullptr, nullptr, nullptr,
+                       "pkv_decode_attn launch");
+}
+
+int pkv_store_decode_attn(const void *k, const void *v, const int32_t *slot_mapping,
+                          const void *q, pkv_cache cache, const int32_t *block_tables,
+                          int32_t max_blocks_per_seq, const int32_t *context_lens,
+                          int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                          float scale, void *out, void *workspace, size_t workspace_bytes,
+                          int32_t partition_tokens, hipStream_t stream) {
+    if (num_seqs > 0 && (!k || !v || !slot_mapping))
+        return fail(PKV_ERR_NULL, "k, v or slot_mapping is null");
+    if (!aligned16(k) || !aligned16(v))
+        return fail(PKV_ERR_ALIGN, "k / v must be 16-byte aligned");
+    return decode_call(q, cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       max_context_len, num_q_heads, scale, out, workspace, workspace_bytes,
+                       partition_tokens, stream, k, v, slot_mapping,
+                       "pkv_store_decode_attn launch");
 }
 
 int pkv_prefill_attn(const void *q, pkv_cache cache, const int32_t *block_tables,

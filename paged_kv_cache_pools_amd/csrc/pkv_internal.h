@@ -29,6 +29,12 @@ struct DecodeArgs {
     void *out;
     float *ws_out;  // [num_seqs][num_q_heads][max_parts][head_dim]
     float *ws_ml;   // [num_seqs][num_q_heads][max_parts][2]
+    // fused store (all null for plain decode): one new token per sequence,
+    // k_new / v_new [num_seqs][num_kv_heads][head_dim] written at slots[s]
+    // into k_store / v_store (the same pools as k_cache / v_cache)
+    const void *k_new = nullptr, *v_new = nullptr;
+    const int32_t *slots = nullptr;
+    void *k_store = nullptr, *v_store = nullptr;
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

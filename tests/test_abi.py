@@ -144,3 +144,14 @@ def test_prefill_validation(lib):
     assert pf(q=0) == 1
     assert pf(hq=5) == 2
     assert pf(c=cache(d=32)) == 3
+
+
+def test_store_decode_validation(lib):
+    sd = lambda k=FAKE, v=FAKE, sl=FAKE, s=2, q=FAKE: lib.pkv_store_decode_attn(
+        k, v, sl, q, cache(), FAKE, 3, FAKE, s, 37, 4, ctypes.c_float(0.125), FAKE, FAKE, 1 << 30,
+        0, None)
+    assert sd(s=0) == 0                     # empty batch: nothing launched
+    assert sd(k=0) == 1 and sd(v=0) == 1 and sd(sl=0) == 1
+    assert sd(k=FAKE + 4) == 4
+    assert sd(q=0) == 1                     # the decode checks still apply
+    assert B.pkv_last_error() != ""

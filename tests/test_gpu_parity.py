@@ -292,3 +292,105 @@ def test_decode_scale_edges(scale, part):
     torch.cuda.synchronize()
     c.oracle_store()
     compare(out, c.oracle_decode(), f"decode scale {scale}", plus_floor=True)
+
+
+# ---------------------------------------------------------------------------
+# fused store + decode: bit-identical to pkv_store followed by pkv_decode_attn
+# (same arithmetic, the new token's K/V taken from registers instead of the
+# cache), and within tolerance of the oracle
+# ---------------------------------------------------------------------------
+
+def fused_vs_separate(wl, partition_tokens=0, slots=None, what=None, prep=None):
+    c = Case(wl)
+    if prep is not None:
+        prep(c)
+    d = c.dev
+    slot_t = d["slot_mapping"] if slots is None else torch.from_numpy(slots).cuda()
+    kc2 = [x.clone() for x in d["k_caches"]]
+    vc2 = [x.clone() for x in d["v_caches"]]
+    say(f"[gpu] fused store+decode {what or wl.name}: S={wl.num_seqs} G={wl.num_q_heads // wl.num_kv_heads} "
+        f"d={wl.head_dim} P={partition_tokens or 'auto'}")
+    # separate
+    B.pkv_store(d["k_new"], d["v_new"], slot_t, d["k_caches"][0], d["v_caches"][0])
+    out_sep = torch.empty_like(d["q"])
+    B.pkv_decode_attn(d["q"], d["k_caches"][0], d["v_caches"][0], d["block_tables"],
+                      d["context_lens"], wl.scale, out_sep, max_context_len=wl.max_context_len,
+                      partition_tokens=partition_tokens)
+    # fused
+    out_fused = torch.empty_like(d["q"])
+    B.pkv_store_decode_attn(d["k_new"], d["v_new"], slot_t, d["q"], kc2[0], vc2[0],
+                            d["block_tables"], d["context_lens"], wl.scale, out_fused,
+                            max_context_len=wl.max_context_len, partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc2[0]), bits(d["k_caches"][0])), "fused store differs (K)"
+    assert np.array_equal(bits(vc2[0]), bits(d["v_caches"][0])), "fused store differs (V)"
+    assert np.array_equal(bits(out_fused), bits(out_sep)), "fused attention differs"
+    return c, out_fused
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 4, 8])
+@pytest.mark.parametrize("part", [16, 64, 0, -1, -3])
+def test_fused_store_decode_matches_separate(d, g, part):
+    lens = [1, 15, 16, 17, 63, 64, 65, 129, 300]
+    wl = W.make_decode(f"fused_d{d}_g{g}", lens, 2 * g, 2, d, 300 + d + g, spare_blocks=2)
+    c, out = fused_vs_separate(wl, part)
+    c.oracle_store()
+    compare(out, c.oracle_decode(), f"fused store+decode d{d} g{g} P{part}")
+
+
+def test_fused_store_decode_skips_and_strays():
+    """slot -1 stores nothing and attends over the cache as it is; a slot in a
+    spare block is stored but is not the last position's, so attention reads
+    the cache there; a sequence with no context stores and outputs zero."""
+    wl = W.make_decode("fused_edges", [20, 33, 7, 0, 40], 8, 2, 128, 63, spare_blocks=2)
+    spare = sorted(set(range(wl.num_blocks)) - set(wl.used_blocks().tolist()))
+    assert len(spare) == 2
+    slots = wl.slot_mapping.copy()
+    slots[1] = -1
+    slots[2] = spare[0] * 16 + 3      # an unreferenced block: not position ctx-1's slot
+    slots[3] = spare[1] * 16 + 0      # ctx 0: store only
+
+    def cached_earlier(c):
+        # sequences 1 and 2 store nothing at their last position, so it must
+        # already hold a token: write one there (the generator left NaN)
+        for s in (1, 2):
+            slot = int(wl.slot_mapping[s])
+            for cache, host, src in ((c.dev["k_caches"][0], c.h["kc"], c.dev["k_new"]),
+                                     (c.dev["v_caches"][0], c.h["vc"], c.dev["v_new"])):
+                row = (src[s] * 0.5).to(torch.bfloat16)
+                cache[slot // 16, :, slot % 16] = row
+                host[slot // 16, :, slot % 16] = bits(row)
+
+    c, out = fused_vs_separate(wl, 0, slots=slots, what="edges", prep=cached_earlier)
+    assert np.all(to_f64(out)[3] == 0.0)
+    orc().store(c.h["k_new"], c.h["v_new"], slots, c.h["kc"], c.h["vc"])
+    compare(out, c.oracle_decode(), "fused store+decode edges")
+
+
+def test_fused_store_decode_mistral_full_size():
+    """The benchmark's launch: 32 x 4096 GQA, single-pass split, two layers;
+    the oracle checks sampled sequences."""
+    wl = W.mistral_gqa(num_layers=2)
+    seqs = [0, 13, 31]
+    say(f"[gpu] fused store+decode full size, oracle on seqs {seqs}")
+    t = W.make_tensors(wl, device="cuda", layers=2, nan_fill=True)
+    hosts = [compact_for_oracle(wl, t, seqs, layer=l) for l in range(2)]
+    outs = []
+    for l in range(2):
+        out = torch.empty_like(t["q"])
+        B.pkv_store_decode_attn(t["k_new"], t["v_new"], t["slot_mapping"], t["q"],
+                                t["k_caches"][l], t["v_caches"][l], t["block_tables"],
+                                t["context_lens"], wl.scale, out,
+                                max_context_len=wl.max_context_len)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for l, h in enumerate(hosts):
+        orc().store(h["k_new"], h["v_new"], h["slots"], h["kc"], h["vc"])
+        ref = orc().decode(h["q"], h["kc"], h["vc"], h["bt"], h["ctx"], wl.scale)
+        compare(outs[l][list(seqs)], ref, f"fused store+decode full size layer {l}")
+        # the stored token is in the cache
+        for i, s in enumerate(seqs):
+            slot = int(wl.slot_mapping[s])
+            got = bits(t["k_caches"][l][slot // 16, :, slot % 16])
+            assert np.array_equal(got, h["k_new"][i]), (l, s)
