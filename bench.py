@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the Qwen-style MHA and continuous-batch decode workloads")
     ap.add_argument("--prefill-iters", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -303,14 +305,72 @@ def main():
         "wall_s_timed": round(wall, 3),
     }
 
+    # the oracle's host copies of two layers are taken before the 16 GiB of
+    # pools are released for the other legs
+    host = None
+    if not args.no_cpu_baseline:
+        host = {"q": [t["q"][0].cpu()], "k_new": [t["k_new"][0].cpu()],
+                "v_new": [t["v_new"][0].cpu()],
+                "k_caches": [x.cpu() for x in t["k_caches"][:2]],
+                "v_caches": [x.cpu() for x in t["v_caches"][:2]]}
+    del t
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, torch, B, W, dev)
-
-    if not args.no_cpu_baseline:
-        host = {"q": [t["q"][0]], "k_new": [t["k_new"][0]], "v_new": [t["v_new"][0]],
-                "k_caches": t["k_caches"][:2], "v_caches": t["v_caches"][:2]}
+    if not args.no_other:
+        result["other_decode_workloads"] = [bench_other(torch, B, W, dev, name)
+                                            for name in ("qwen_mha", "cont_batch")]
+    if host is not None:
         result["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bench_other(torch, B, W, dev, name, iters=20):
+    """Store + decode (fused launch) on one of the other decode workloads: the
+    Qwen-style MHA batch (16 seqs, ctx U{128..2048}, 32 x 128 heads) or the
+    continuous batch (256 seqs in 8 groups of 32 sharing a 2048-token prefix
+    through identical block ids, lognormal tails).  Two pool copies alternate
+    so consecutive launches do not find each other's K/V in cache.  Reports
+    logical KV GB/s (every sequence's context) and, where blocks are shared,
+    the unique-block rate too."""
+    wl = W.CONFIGS[name]()
+    t = W.make_tensors(wl, device=dev, layers=2, nan_fill=False)
+    out = torch.empty_like(t["q"])
+    P = B.pkv_decode_partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.max_context_len)
+    ws = torch.empty(max(16, B.pkv_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
+                                                          wl.head_dim, wl.max_context_len, P)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(l):
+        B.pkv_store_decode_attn(t["k_new"], t["v_new"], t["slot_mapping"], t["q"],
+                                t["k_caches"][l], t["v_caches"][l], t["block_tables"],
+                                t["context_lens"], wl.scale, out,
+                                max_context_len=wl.max_context_len, workspace=ws,
+                                partition_tokens=P)
+
+    for l in (0, 1, 0, 1):
+        run(l)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(iters):
+        run(i & 1)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / iters
+    logical = decode_bytes(wl) + store_bytes(wl)
+    unique_tok = int(wl.used_blocks().shape[0]) * wl.block_size
+    res = {"workload": name, "num_seqs": wl.num_seqs, "max_context_len": wl.max_context_len,
+           "sum_context": int(wl.context_lens.sum()),
+           "work_split": (f"single pass, {-P} waves" if P < 0 else f"split-KV, P = {P} + merge"),
+           "us_per_launch": round(us, 2), "logical_kv_gbs": round(logical / us / 1e3, 1),
+           "tokens_per_s": round(wl.num_seqs / (us * 1e-6), 1)}
+    if wl.shared_blocks:
+        uniq = unique_tok * 2 * wl.num_kv_heads * wl.head_dim * 2
+        res["unique_kv_gbs"] = round(uniq / us / 1e3, 1)
+    del t
+    return res
 
 
 def bench_prefill(args, torch, B, W, dev):
