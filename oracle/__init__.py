@@ -58,6 +58,15 @@ def _bind(lib):
                                 _I32, ctypes.c_float, _P, ctypes.c_int]
     lib.pko_default_threads.restype = ctypes.c_int
     lib.pko_default_threads.argtypes = []
+    lib.pko_fp8_decode.restype = ctypes.c_double
+    lib.pko_fp8_decode.argtypes = [ctypes.c_uint8]
+    lib.pko_fp8_encode.restype = ctypes.c_uint8
+    lib.pko_fp8_encode.argtypes = [ctypes.c_float]
+    lib.pko_store_fp8.restype = ctypes.c_int
+    lib.pko_store_fp8.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32]
+    lib.pko_decode_fp8.restype = ctypes.c_int
+    lib.pko_decode_fp8.argtypes = [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32,
+                                   _I32, ctypes.c_float, _P]
     return lib
 
 
@@ -113,6 +122,54 @@ class Oracle:
                                  int(nthreads))
         if rc != OK:
             raise OracleError(rc, "decode")
+        return out
+
+    # -- FP8 (OCP E4M3, one fp32 scale per token and KV head) ------------------------
+    def fp8_decode(self, code: int) -> float:
+        return float(self.lib.pko_fp8_decode(int(code)))
+
+    def fp8_encode(self, y: float) -> int:
+        return int(self.lib.pko_fp8_encode(float(np.float32(y))))
+
+    def store_fp8(self, k, v, slot_mapping, k_codes, v_codes, k_scales, v_scales):
+        """In place: quantize k/v ([T][Hkv][d] uint16 bf16 bits) into the codes
+        ([NB][Hkv][bs][d] uint8) and scales ([NB][Hkv][bs] float32)."""
+        k = _u16(k)
+        v = _u16(v)
+        slots = _i32(slot_mapping)
+        for a, dt in ((k_codes, np.uint8), (v_codes, np.uint8), (k_scales, np.float32),
+                      (v_scales, np.float32)):
+            _check_inplace(a, dt)
+        nb, hkv, bs, d = k_codes.shape
+        assert v_codes.shape == k_codes.shape and k_scales.shape == (nb, hkv, bs)
+        assert v_scales.shape == k_scales.shape
+        t = slots.shape[0]
+        assert k.shape == (t, hkv, d) and v.shape == (t, hkv, d)
+        rc = self.lib.pko_store_fp8(_ptr(k), _ptr(v), _ptr(slots), t, _ptr(k_codes), _ptr(v_codes),
+                                    _ptr(k_scales), _ptr(v_scales), nb, hkv, d, bs)
+        if rc != OK:
+            raise OracleError(rc, "store_fp8")
+
+    def decode_fp8(self, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                   scale):
+        """q [S][Hq][d] uint16 -> out [S][Hq][d] float64 over the dequantized cache."""
+        q = _u16(q)
+        k_codes = np.ascontiguousarray(k_codes, np.uint8)
+        v_codes = np.ascontiguousarray(v_codes, np.uint8)
+        k_scales = np.ascontiguousarray(k_scales, np.float32)
+        v_scales = np.ascontiguousarray(v_scales, np.float32)
+        bt = _i32(block_tables)
+        ctx = _i32(context_lens)
+        nb, hkv, bs, d = k_codes.shape
+        s, hq, dq = q.shape
+        assert dq == d and v_codes.shape == k_codes.shape
+        assert bt.ndim == 2 and bt.shape[0] == s and ctx.shape == (s,)
+        out = np.zeros((s, hq, d), dtype=np.float64)
+        rc = self.lib.pko_decode_fp8(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales),
+                                     _ptr(v_scales), nb, _ptr(bt), bt.shape[1], _ptr(ctx), s, hq,
+                                     hkv, d, bs, float(np.float32(scale)), _ptr(out))
+        if rc != OK:
+            raise OracleError(rc, "decode_fp8")
         return out
 
     # -- prefill ----------------------------------------------------------------

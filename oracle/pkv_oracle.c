@@ -395,3 +395,231 @@ int pko_prefill(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_ca
     w.max_context_len = max_ctx;
     return run_threads(&w, nthreads);
 }
+
+
+/* ------------------------------------------------------------------------ */
+/* FP8 KV cache                                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [LLM4] §17.6 counts an FP8 KV cache at 1 byte per element and lists
+ * "whether to use an FP8 KV cache" among the memory levers; it fixes neither
+ * the 8-bit format nor the scaling.  Reading taken here: OCP FP8 E4M3 (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
+ * NaN; largest finite magnitude 448; subnormals m * 2^-9), with one fp32 scale
+ * per (token, KV head): scale = amax / 448 over the head's head_dim values
+ * (1 when they are all zero) and code = E4M3(x / scale) rounded to nearest,
+ * ties to even, after clamping x / scale to [-448, 448].  Both divisions are
+ * fp32 (correctly rounded), so the codes and scales are exact integers/bits
+ * to compare.  The cached value is decode(code) * scale.
+ */
+
+/* Value of an E4M3 code (NaN for the two NaN codes). */
+double pko_fp8_decode(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);              /* subnormal: (m / 8) * 2^-6 */
+    else
+        v = ldexp(8.0 + (double)m, e - 10);    /* (1 + m / 8) * 2^(e - 7) */
+    return sign ? -v : v;
+}
+
+/* Nearest E4M3 code to y (|y| <= 448 and finite), ties to the even code:
+ * the candidates are the two representable magnitudes around |y| on the
+ * grid whose spacing is that of |y|'s binade. */
+uint8_t pko_fp8_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs((double)y);
+    /* spacing of the grid containing a: 2^-9 below 2^-6, else 2^(e-3) */
+    int e;
+    double spacing;
+    if (a < ldexp(1.0, -6)) {
+        spacing = ldexp(1.0, -9);
+    } else {
+        frexp(a, &e);                          /* a in [2^(e-1), 2^e) */
+        spacing = ldexp(1.0, e - 1 - 3);
+    }
+    double lo = floor(a / spacing) * spacing;  /* exact: a / spacing has few bits */
+    double hi = lo + spacing;
+    double pick;
+    if (a - lo < hi - a)
+        pick = lo;
+    else if (a - lo > hi - a)
+        pick = hi;
+    else  /* tie: the candidate whose mantissa field is even */
+        pick = ((long long)(lo / spacing) % 2 == 0) ? lo : hi;
+    /* code of the picked magnitude (pick <= 448 because a <= 448) */
+    for (int c = 0; c < 0x7f; ++c)
+        if (pko_fp8_decode((uint8_t)c) == pick)
+            return (uint8_t)(sign | c);
+    return (uint8_t)(sign | 0x7e);             /* not reached */
+}
+
+static float bf16_bits_to_float(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Quantize one head row of head_dim bf16 values to codes + scale. */
+static void quantize_row(const uint16_t *x, int32_t head_dim, uint8_t *codes, float *scale_out)
+{
+    float amax = 0.0f;
+    for (int32_t i = 0; i < head_dim; ++i) {
+        float a = fabsf(bf16_bits_to_float(x[i]));
+        if (a > amax)
+            amax = a;
+    }
+    float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+    for (int32_t i = 0; i < head_dim; ++i) {
+        float y = bf16_bits_to_float(x[i]) / scale;
+        if (y > 448.0f)
+            y = 448.0f;
+        if (y < -448.0f)
+            y = -448.0f;
+        codes[i] = pko_fp8_encode(y);
+    }
+    *scale_out = scale;
+}
+
+/*
+ * Store into an FP8 cache: like pko_store, but each (token, KV head) row is
+ * quantized as described above.  codes: uint8 [num_blocks][num_kv_heads]
+ * [block_size][head_dim]; scales: float [num_blocks][num_kv_heads][block_size].
+ */
+int pko_store_fp8(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
+                  int32_t num_tokens, uint8_t *k_codes, uint8_t *v_codes, float *k_scales,
+                  float *v_scales, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size)
+{
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0)
+        return PKO_ERR_ARG;
+    if (num_tokens == 0)
+        return PKO_OK;
+    if (!k || !v || !slot_mapping || !k_codes || !v_codes || !k_scales || !v_scales)
+        return PKO_ERR_ARG;
+    int64_t num_slots = (int64_t)num_blocks * block_size;
+    unsigned char *seen = calloc((size_t)(num_slots > 0 ? num_slots : 1), 1);
+    if (!seen)
+        return PKO_ERR_ALLOC;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        int32_t slot = slot_mapping[i];
+        if (slot < 0)
+            continue;
+        if ((int64_t)slot >= num_slots || seen[slot]) {
+            free(seen);
+            return (int64_t)slot >= num_slots ? PKO_ERR_RANGE : PKO_ERR_DUPLICATE;
+        }
+        seen[slot] = 1;
+    }
+    free(seen);
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        int32_t slot = slot_mapping[i];
+        if (slot < 0)
+            continue;
+        int64_t block = slot / block_size, offset = slot % block_size;
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+            int64_t src = ((int64_t)i * num_kv_heads + h) * head_dim;
+            int64_t row = (block * num_kv_heads + h) * block_size + offset;
+            quantize_row(k + src, head_dim, k_codes + row * head_dim, k_scales + row);
+            quantize_row(v + src, head_dim, v_codes + row * head_dim, v_scales + row);
+        }
+    }
+    return PKO_OK;
+}
+
+/* Dequantize an FP8 cache into fp64 (value = decode(code) * scale). */
+static void dequantize(const uint8_t *codes, const float *scales, int64_t rows, int32_t head_dim,
+                       double *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t x = 0; x < head_dim; ++x)
+            out[r * head_dim + x] = pko_fp8_decode(codes[r * head_dim + x]) * (double)scales[r];
+}
+
+/*
+ * Decode attention over an FP8 cache: the scaled dot-product attention of
+ * pko_decode on the cached values decode(code) * scale, in fp64.  The cache
+ * is dequantized up front into fp64 arrays and attention runs on those.
+ */
+int pko_decode_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_codes,
+                   const float *k_scales, const float *v_scales, int32_t num_blocks,
+                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                   const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                   double *out)
+{
+    int32_t max_ctx = 0;
+    if (num_seqs > 0 && (!q || !k_codes || !v_codes || !k_scales || !v_scales ||
+                         !block_tables || !context_lens || !out))
+        return PKO_ERR_ARG;
+    int rc = check_common(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, block_tables, context_lens, num_blocks, &max_ctx);
+    if (rc != PKO_OK || num_seqs == 0)
+        return rc;
+    int64_t rows = (int64_t)num_blocks * num_kv_heads * block_size;
+    double *kd = malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * head_dim);
+    double *vd = malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * head_dim);
+    double *scores = malloc(sizeof(double) * (size_t)(max_ctx > 0 ? max_ctx : 1));
+    if (!kd || !vd || !scores) {
+        free(kd);
+        free(vd);
+        free(scores);
+        return PKO_ERR_ALLOC;
+    }
+    dequantize(k_codes, k_scales, rows, head_dim, kd);
+    dequantize(v_codes, v_scales, rows, head_dim, vd);
+    int32_t group = num_q_heads / num_kv_heads;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t *bt = block_tables + (int64_t)s * max_blocks_per_seq;
+        int32_t n = context_lens[s];
+        for (int32_t h = 0; h < num_q_heads; ++h) {
+            int32_t kvh = h / group;
+            const uint16_t *q_row = q + ((int64_t)s * num_q_heads + h) * head_dim;
+            double *o = out + ((int64_t)s * num_q_heads + h) * head_dim;
+            for (int32_t x = 0; x < head_dim; ++x)
+                o[x] = 0.0;
+            if (n <= 0)
+                continue;
+            for (int32_t t = 0; t < n; ++t) {
+                int64_t row = ((int64_t)bt[t / block_size] * num_kv_heads + kvh) * block_size +
+                              t % block_size;
+                double dot = 0.0;
+                for (int32_t x = 0; x < head_dim; ++x)
+                    dot += bf16_bits_to_double(q_row[x]) * kd[row * head_dim + x];
+                scores[t] = (double)scale * dot;
+            }
+            double m = scores[0];
+            for (int32_t t = 1; t < n; ++t)
+                if (scores[t] > m)
+                    m = scores[t];
+            double z = 0.0;
+            for (int32_t t = 0; t < n; ++t) {
+                scores[t] = exp(scores[t] - m);
+                z += scores[t];
+            }
+            for (int32_t t = 0; t < n; ++t) {
+                int64_t row = ((int64_t)bt[t / block_size] * num_kv_heads + kvh) * block_size +
+                              t % block_size;
+                for (int32_t x = 0; x < head_dim; ++x)
+                    o[x] += scores[t] * vd[row * head_dim + x];
+            }
+            for (int32_t x = 0; x < head_dim; ++x)
+                o[x] /= z;
+        }
+    }
+    free(kd);
+    free(vd);
+    free(scores);
+    return PKO_OK;
+}

@@ -47,6 +47,21 @@ int pko_prefill(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_ca
 
 int pko_default_threads(void);
 
+/* FP8 (OCP E4M3) cache with one fp32 scale per (token, KV head); see
+ * pkv_oracle.c for the quantization rule. */
+double pko_fp8_decode(uint8_t code);
+uint8_t pko_fp8_encode(float y);
+int pko_store_fp8(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapping,
+                  int32_t num_tokens, uint8_t *k_codes, uint8_t *v_codes, float *k_scales,
+                  float *v_scales, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size);
+int pko_decode_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_codes,
+                   const float *k_scales, const float *v_scales, int32_t num_blocks,
+                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                   const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                   double *out);
+
 #ifdef __cplusplus
 }
 #endif

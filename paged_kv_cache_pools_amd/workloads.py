@@ -328,6 +328,35 @@ def make_tensors(wl: Workload, device="cpu", layers: Optional[int] = None, nan_f
             **meta}
 
 
+def make_fp8_pools(wl: Workload, device="cpu", seed: Optional[int] = None, nan_fill: bool = True):
+    """Random FP8 (OCP E4M3) pools for one layer: codes drawn uniformly from the
+    finite codes (every byte but 0x7f and 0xff), scales drawn log-uniform in
+    [2^-3, 2^3).  With ``nan_fill`` every slot that holds no cached token (tails,
+    unreferenced blocks, the slots this step's store writes) gets the NaN code
+    and a NaN scale.  Returns (k_codes, v_codes, k_scales, v_scales) tensors:
+    uint8 [NB][Hkv][bs][d] and float32 [NB][Hkv][bs]."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed((wl.seed if seed is None else seed) + 7777)
+    shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    out = []
+    for _ in range(2):
+        c = torch.randint(0, 254, shape, generator=gen, device=device, dtype=torch.int32)
+        c = c + (c >= 0x7f).to(torch.int32)          # skip 0x7f: 0..0x7e, 0x80..0xfe
+        out.append(c.to(torch.uint8))
+    for _ in range(2):
+        e = torch.rand(shape[:3], generator=gen, device=device, dtype=torch.float32) * 6.0 - 3.0
+        out.append(torch.exp2(e))
+    if nan_fill:
+        dead = torch.from_numpy(~live_slot_mask(wl, pre_store=True)).to(device)
+        out[0].masked_fill_(dead[:, None, :, None], 0x7F)
+        out[1].masked_fill_(dead[:, None, :, None], 0x7F)
+        out[2].masked_fill_(dead[:, None, :], float("nan"))
+        out[3].masked_fill_(dead[:, None, :], float("nan"))
+    return tuple(out)
+
+
 def bf16_bits(t) -> np.ndarray:
     """Host numpy uint16 view of a bf16 torch tensor's bits."""
     import torch

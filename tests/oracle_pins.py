@@ -380,4 +380,135 @@ def pin_prefill_one_new_token_is_decode(orc):
     assert np.array_equal(pre, dec)
 
 
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) cache
+# ---------------------------------------------------------------------------
+
+def _torch_fp8_decode(codes):
+    t = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def pin_fp8_codec_spec_values(orc):
+    """The format's defining constants (OCP E4M3): 448 is the largest finite
+    magnitude, 2^-6 the smallest normal, 2^-9 the smallest subnormal, 1.0 is
+    0x38, S.1111.111 is NaN; every finite code survives decode -> encode."""
+    assert orc.fp8_decode(0x7E) == 448.0 and orc.fp8_decode(0xFE) == -448.0
+    assert orc.fp8_decode(0x08) == 2.0 ** -6 and orc.fp8_decode(0x01) == 2.0 ** -9
+    assert orc.fp8_decode(0x38) == 1.0 and orc.fp8_decode(0x00) == 0.0
+    assert math.isnan(orc.fp8_decode(0x7F)) and math.isnan(orc.fp8_decode(0xFF))
+    for c in list(range(0x7F)) + list(range(0x80, 0xFF)):
+        assert orc.fp8_encode(orc.fp8_decode(c)) == c, c
+
+
+def pin_fp8_codec_matches_torch(orc):
+    """Decode of all 256 codes and nearest-even encode of in-range values
+    (random, every midpoint between neighbouring codes, subnormals, +-0)
+    agree with torch's float8_e4m3fn."""
+    ref = _torch_fp8_decode(np.arange(256))
+    got = np.array([orc.fp8_decode(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    finite = np.sort(ref[(ref >= 0) & ~np.isnan(ref)])
+    mids = (finite[1:] + finite[:-1]) / 2
+    rng = np.random.default_rng(40)
+    ys = np.concatenate([finite, -finite, mids, -mids, rng.uniform(-448, 448, 3000),
+                         rng.standard_normal(2000) * 0.01, [0.0, -0.0, 447.99, -447.99]])
+    ys = ys.astype(np.float32)
+    tref = torch.from_numpy(ys).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.fp8_encode(float(y)) for y in ys], np.uint8)
+    bad = np.nonzero(got != tref)[0]
+    assert bad.size == 0, [(float(ys[i]), hex(got[i]), hex(tref[i])) for i in bad[:5]]
+
+
+def _fp8_store_case(seed=41):
+    wl = W.make_decode("pin_fp8_store", [5, 37, 16, 1], 4, 2, 64, seed, spare_blocks=3)
+    d = _setup(wl)
+    shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    codes = [np.full(shape, 0x7F, np.uint8), np.full(shape, 0x7F, np.uint8)]
+    scales = [np.full(shape[:3], np.nan, np.float32), np.full(shape[:3], np.nan, np.float32)]
+    return wl, d, codes, scales
+
+
+def pin_store_fp8_quantization(orc):
+    """Each stored (token, head) row: scale = fp32(amax / 448), the codes are
+    torch's float8_e4m3fn of fp32(x / scale), the amax element codes to +-448,
+    and decode * scale is within the round-to-nearest bound of x; slots not
+    written keep their bytes, slot -1 writes nothing."""
+    wl, d, (kc, vc), (ks, vs) = _fp8_store_case()
+    slots = wl.slot_mapping.copy()
+    slots[3] = -1
+    before = kc.copy()
+    orc.store_fp8(d["k"], d["v"], slots, kc, vc, ks, vs)
+    touched = np.zeros(kc.shape[:3], bool)
+    for i, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        b, o = slot // 16, slot % 16
+        for new, codes, scales in ((d["k"], kc, ks), (d["v"], vc, vs)):
+            x = torch.from_numpy(new[i].view(np.int16)).view(torch.bfloat16).float()  # [Hkv][d]
+            amax = x.abs().amax(dim=1)
+            sc = torch.where(amax > 0, amax / torch.tensor(448.0), torch.ones_like(amax))
+            assert np.array_equal(scales[b, :, o], sc.numpy())
+            y = (x / sc[:, None]).clamp(-448.0, 448.0)
+            ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes[b, :, o], ref)
+            top = x.abs().argmax(dim=1)
+            for h in range(x.shape[0]):
+                if amax[h] > 0:
+                    assert codes[b, h, o, top[h]] & 0x7F == 0x7E
+            deq = _torch_fp8_decode(codes[b, :, o]) * sc.numpy()[:, None].astype(np.float64)
+            err = np.abs(deq - x.numpy().astype(np.float64))
+            bound = 2.0 ** -4 * np.abs(x.numpy()) + 2.0 ** -10 * sc.numpy()[:, None]
+            assert np.all(err <= bound)
+        touched[b, :, o] = True
+    assert np.array_equal(kc[~touched], before[~touched])
+
+
+def _fp8_case(lens, hq, hkv, dim, seed, spare=2):
+    wl = W.make_decode("pin_fp8", lens, hq, hkv, dim, seed, spare_blocks=spare, store=False)
+    t = W.make_tensors(wl, device="cpu", nan_fill=True, layers=1)
+    kc, vc, ks, vs = (x.numpy() for x in W.make_fp8_pools(wl, nan_fill=True))
+    return wl, _bits(t["q"]), kc, vc, ks, vs
+
+
+def pin_decode_fp8_matches_sdpa(orc):
+    """Decode over an FP8 cache == torch fp64 SDPA on the dequantized values
+    (torch's float8_e4m3fn decode times the scale), GQA, ragged lengths; NaN
+    codes and scales in dead slots never reach the output."""
+    for hq, hkv, dim, lens, seed in ((8, 2, 64, [5, 37, 16, 17], 42), (4, 4, 128, [1, 33], 43)):
+        wl, q, kc, vc, ks, vs = _fp8_case(lens, hq, hkv, dim, seed)
+        out = orc.decode_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.context_lens, wl.scale)
+        assert np.all(np.isfinite(out))
+        kd = _torch_fp8_decode(kc) * ks[..., None].astype(np.float64)
+        vd = _torch_fp8_decode(vc) * vs[..., None].astype(np.float64)
+        q64 = _f64(q)
+        g = hq // hkv
+        for s in range(wl.num_seqs):
+            n = int(wl.context_lens[s])
+            k = np.repeat(_gather(kd, wl.block_tables[s], n), g, axis=0)
+            v = np.repeat(_gather(vd, wl.block_tables[s], n), g, axis=0)
+            ref = _sdpa(q64[s][:, None, :], k, v, wl.scale)[:, 0, :]
+            assert np.abs(out[s] - ref).max() <= 1e-12, (s, np.abs(out[s] - ref).max())
+
+
+def pin_decode_fp8_unit_scales_equal_bf16(orc):
+    """With every scale 1 the FP8 cache holds bf16-representable values, so
+    decode over it equals the bf16 decode over those values, bit for bit."""
+    wl, q, kc, vc, ks, vs = _fp8_case([20, 9], 4, 2, 64, 44, spare=0)
+    ks[:] = 1.0
+    vs[:] = 1.0
+    out = orc.decode_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.context_lens, wl.scale)
+    to_bits = lambda c: torch.from_numpy(_torch_fp8_decode(c)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+    kb = np.ascontiguousarray(to_bits(kc))
+    vb = np.ascontiguousarray(to_bits(vc))
+    live = W.live_slot_mask(wl, pre_store=False)
+    kb.transpose(0, 2, 1, 3)[~live] = 0  # dead slots (NaN codes): never read
+    vb.transpose(0, 2, 1, 3)[~live] = 0
+    ref = orc.decode(q, kb, vb, wl.block_tables, wl.context_lens, wl.scale)
+    assert np.array_equal(out, ref)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

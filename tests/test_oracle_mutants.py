@@ -38,6 +38,18 @@ MUTANTS = [
     ("kv_bytes_without_kv_factor", "return (uint64_t)2 * (uint64_t)num_layers", "return (uint64_t)1 * (uint64_t)num_layers"),
     ("ctx_zero_not_zero", "for (int32_t x = 0; x < head_dim; ++x)\n        out_row[x] = 0.0;\n    if (n <= 0)\n        return;",
      "for (int32_t x = 0; x < head_dim; ++x)\n        out_row[x] = 0.0;\n    if (n <= 0)\n        n = 1;"),
+    # FP8 cache
+    ("fp8_exponent_bias_off_by_one", "v = ldexp(8.0 + (double)m, e - 10);",
+     "v = ldexp(8.0 + (double)m, e - 9);"),
+    ("fp8_subnormals_as_normals", "v = ldexp((double)m, -9);", "v = ldexp(8.0 + (double)m, -10);"),
+    ("fp8_ties_up", "pick = ((long long)(lo / spacing) % 2 == 0) ? lo : hi;", "pick = hi;"),
+    ("fp8_truncating_encode", "if (a - lo < hi - a)\n        pick = lo;",
+     "if (1)\n        pick = lo;"),
+    ("fp8_scale_max_240", "amax / 448.0f", "amax / 240.0f"),
+    ("fp8_scale_not_applied", "* (double)scales[r];", "* 1.0;"),
+    ("fp8_v_stored_from_k", "quantize_row(v + src, head_dim, v_codes", "quantize_row(k + src, head_dim, v_codes"),
+    ("fp8_decode_v_from_k", "o[x] += scores[t] * vd[row * head_dim + x];",
+     "o[x] += scores[t] * kd[row * head_dim + x];"),
 ]
 
 
