@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8-cache leg of the decode workload")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the Qwen-style MHA and continuous-batch decode workloads")
     ap.add_argument("--prefill-iters", type=int, default=5)
@@ -315,6 +317,8 @@ def main():
                 "v_caches": [x.cpu() for x in t["v_caches"][:2]]}
     del t
     torch.cuda.empty_cache()
+    if not args.no_fp8:
+        result["fp8"] = bench_fp8(args, torch, B, W, dev)
     if not args.no_prefill:
         result["prefill"] = bench_prefill(args, torch, B, W, dev)
     if not args.no_other:
@@ -323,6 +327,91 @@ def main():
     if host is not None:
         result["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bench_fp8(args, torch, B, W, dev):
+    """The same decode step over FP8 caches (OCP E4M3 codes + one fp32 scale per
+    token and KV head): per layer, pkv_store_fp8 of the 32 new tokens then
+    pkv_decode_attn_fp8.  The pools hold random codes and scales (32 layers,
+    8.3 GB); timing as for the bf16 step (a timed region without per-launch
+    events, then a pass with events around each decode launch)."""
+    L = args.layers
+    wl = W.mistral_gqa(seed=args.seed, num_layers=L)
+    S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed + 1)
+    rb = lambda shape: W._randn_bf16(torch, shape, gen, dev)
+    q = [rb((S, Hq, D)) for _ in range(L)]
+    kn = [rb((S, Hkv, D)) for _ in range(L)]
+    vn = [rb((S, Hkv, D)) for _ in range(L)]
+    pools = [W.make_fp8_pools(wl, device=dev, seed=wl.seed + l, nan_fill=False) for l in range(L)]
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    ctx = torch.from_numpy(wl.context_lens).to(dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    outs = [torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    P = B.pkv_decode_partition_tokens_fp8(S, Hkv, wl.max_context_len)
+    ws = torch.empty(max(16, B.pkv_decode_workspace_bytes(S, Hq, D, wl.max_context_len, P)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def store(l):
+        B.pkv_store_fp8(kn[l], vn[l], slots, *pools[l])
+
+    def decode(l):
+        B.pkv_decode_attn_fp8(q[l], *pools[l], bt, ctx, wl.scale, outs[l],
+                              max_context_len=wl.max_context_len, workspace=ws,
+                              partition_tokens=P)
+
+    for _ in range(args.warmup):
+        for l in range(L):
+            store(l)
+            decode(l)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(args.steps):
+        for l in range(L):
+            store(l)
+            decode(l)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = a.elapsed_time(b) / args.steps
+    pairs = []
+    for _ in range(args.steps):
+        for l in range(L):
+            store(l)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            decode(l)
+            e1.record(stream)
+            pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([x.elapsed_time(y) for x, y in pairs]))
+    ctx64 = wl.context_lens.astype(np.int64)
+    # decode: codes + scales of every cached token, q in, out back, table, lengths
+    dec_bytes = (int(ctx64.sum()) * 2 * Hkv * (D + 4) + 2 * S * Hq * D * 2
+                 + 4 * int(((ctx64 + 15) // 16).sum()) + 4 * S)
+    # store: bf16 k/v in, codes + scales out, slots
+    st_bytes = S * 2 * Hkv * D * 2 + S * 2 * Hkv * (D + 4) + 4 * S
+    step_gbs = L * (dec_bytes + st_bytes) / (ms_per_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    del pools, q, kn, vn, outs
+    torch.cuda.empty_cache()
+    return {
+        "workload": "the same 32 seqs x 4096 tokens, 32q/8kv, d 128, 32 layers, over FP8 (E4M3 + "
+                    "fp32 scale per token and KV head) caches: pkv_store_fp8 + pkv_decode_attn_fp8",
+        "work_split": (f"single pass, {-P} waves per (seq, kv head)" if P < 0
+                       else f"split-KV, {P}-token partitions + merge"),
+        "ms_per_step": round(ms_per_step, 4),
+        "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
+        "kv_gbs": round(step_gbs, 2), "hbm_peak_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "decode_us_per_layer": round(dec_ms * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": f"decode_fused_kernel<{D},{Hq // Hkv},fp8>",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(f"decode_fused_kernel<{D},{Hq // Hkv},fp8>"),
+                     "algorithmic_bytes_per_launch": dec_bytes},
+    }
 
 
 def bench_other(torch, B, W, dev, name, iters=20):

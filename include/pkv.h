@@ -200,6 +200,62 @@ int pkv_prefill_attn(const void *q, pkv_cache cache, const int32_t *block_tables
                      hipStream_t stream);
 
 /*
+ * ---------------------------------------------------------------- FP8 ----
+ * An FP8 KV cache: [LLM4] §17.6 counts it at one byte per element (half of
+ * BF16) among the levers on KV memory, without fixing the format or the
+ * scaling.  This library uses OCP FP8 E4M3 codes (bias 7, largest finite
+ * magnitude 448, subnormals, 0x7f / 0xff = NaN) with one fp32 scale per
+ * (token, KV head):
+ *   scale = amax / 448 over the head's head_dim values (1 if all are zero)
+ *   code  = E4M3(x / scale), x / scale clamped to [-448, 448], rounded to
+ *           nearest, ties to even;  both divisions correctly rounded fp32
+ *   cached value = code_value * scale
+ * so a cached token costs 2 x head_dim + 8 bytes per KV head (K and V).
+ * Layout, per layer:
+ *   k, v              uint8 codes [num_blocks][num_kv_heads][block_size][head_dim]
+ *   k_scale, v_scale  fp32 [num_blocks][num_kv_heads][block_size]
+ * All four pointers 16-byte aligned.
+ */
+typedef struct {
+    void *k;
+    void *v;
+    float *k_scale;
+    float *v_scale;
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+} pkv_cache_fp8;
+
+/*
+ * pkv_store_fp8 -- pkv_store into an FP8 cache: each stored (token, KV head)
+ * row of k and v (bf16, as for pkv_store) is quantized as above; its codes and
+ * scale go to the slot's row.  slot_mapping[i] < 0 skips token i.
+ */
+int pkv_store_fp8(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                  pkv_cache_fp8 cache, hipStream_t stream);
+
+/*
+ * pkv_decode_partition_tokens_fp8 -- the automatic work split of
+ * pkv_decode_attn_fp8 (same encoding as pkv_decode_partition_tokens; the
+ * single-pass kernel gets up to twice the waves, for FP8's higher arithmetic
+ * per byte).  pkv_decode_workspace_bytes(..., 0) bounds its workspace too.
+ */
+int32_t pkv_decode_partition_tokens_fp8(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t max_context_len);
+
+/*
+ * pkv_decode_attn_fp8 -- pkv_decode_attn over an FP8 cache: the same
+ * attention on the cached values code_value * scale (bf16 q and out, fp32
+ * arithmetic).  Arguments and work split as for pkv_decode_attn.
+ */
+int pkv_decode_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                        int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                        void *workspace, size_t workspace_bytes, int32_t partition_tokens,
+                        hipStream_t stream);
+
+/*
  * pkv_kv_bytes -- KV-cache bytes for `tokens` cached tokens:
  *   2 (K and V) x layers x kv_heads x head_dim x tokens x bytes_per_elem
  * ([LLM4] §17.3 and §17.6: KV heads, not query heads; tokens summed over

@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_
 
 # every symbol include/pkv.h declares
 EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
-            "pkv_decode_attn", "pkv_store_decode_attn", "pkv_prefill_attn", "pkv_kv_bytes",
+            "pkv_decode_attn", "pkv_store_decode_attn", "pkv_prefill_attn", "pkv_store_fp8",
+            "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_kv_bytes",
             "pkv_status_string", "pkv_last_error"]
 
 
@@ -32,6 +33,13 @@ class PkvError(RuntimeError):
 
 class PkvCache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32)]
+
+
+class PkvCacheFp8(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32)]
 
@@ -57,6 +65,8 @@ def load(path: str = LIB_PATH):
     lib.pkv_store.argtypes = [_P, _P, _P, _I32, PkvCache, _P]
     lib.pkv_decode_partition_tokens.restype = _I32
     lib.pkv_decode_partition_tokens.argtypes = [_I32, _I32, _I32]
+    lib.pkv_decode_partition_tokens_fp8.restype = _I32
+    lib.pkv_decode_partition_tokens_fp8.argtypes = [_I32, _I32, _I32]
     lib.pkv_decode_workspace_bytes.restype = _SZ
     lib.pkv_decode_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32]
     lib.pkv_decode_attn.restype = ctypes.c_int
@@ -65,6 +75,11 @@ def load(path: str = LIB_PATH):
     lib.pkv_store_decode_attn.restype = ctypes.c_int
     lib.pkv_store_decode_attn.argtypes = [_P, _P, _P, _P, PkvCache, _P, _I32, _P, _I32, _I32, _I32,
                                           ctypes.c_float, _P, _P, _SZ, _I32, _P]
+    lib.pkv_store_fp8.restype = ctypes.c_int
+    lib.pkv_store_fp8.argtypes = [_P, _P, _P, _I32, PkvCacheFp8, _P]
+    lib.pkv_decode_attn_fp8.restype = ctypes.c_int
+    lib.pkv_decode_attn_fp8.argtypes = [_P, PkvCacheFp8, _P, _I32, _P, _I32, _I32, _I32,
+                                        ctypes.c_float, _P, _P, _SZ, _I32, _P]
     lib.pkv_prefill_attn.restype = ctypes.c_int
     lib.pkv_prefill_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                      ctypes.c_float, _P, _P]
@@ -118,8 +133,24 @@ def _cache(k_cache, v_cache) -> PkvCache:
     return PkvCache(k_cache.data_ptr(), v_cache.data_ptr(), nb, hkv, d, bs)
 
 
+def _cache_fp8(k_codes, v_codes, k_scale, v_scale) -> PkvCacheFp8:
+    import torch
+
+    _need(k_codes, "k_codes", torch.uint8, 4)
+    _need(v_codes, "v_codes", torch.uint8, 4)
+    _need(k_scale, "k_scale", torch.float32, 3)
+    _need(v_scale, "v_scale", torch.float32, 3)
+    if k_codes.shape != v_codes.shape or k_scale.shape != v_scale.shape or \
+            tuple(k_scale.shape) != tuple(k_codes.shape[:3]):
+        raise ValueError(f"codes {tuple(k_codes.shape)} / {tuple(v_codes.shape)} and scales "
+                         f"{tuple(k_scale.shape)} / {tuple(v_scale.shape)} do not match")
+    nb, hkv, bs, d = k_codes.shape
+    return PkvCacheFp8(k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(),
+                       v_scale.data_ptr(), nb, hkv, d, bs)
+
+
 # ---------------------------------------------------------------------------
-# the three calls
+# the calls
 # ---------------------------------------------------------------------------
 
 def pkv_store(k, v, slot_mapping, k_cache, v_cache, stream=None):
@@ -141,6 +172,10 @@ def pkv_store(k, v, slot_mapping, k_cache, v_cache, stream=None):
 
 def pkv_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len) -> int:
     return int(load().pkv_decode_partition_tokens(num_seqs, num_kv_heads, max_context_len))
+
+
+def pkv_decode_partition_tokens_fp8(num_seqs, num_kv_heads, max_context_len) -> int:
+    return int(load().pkv_decode_partition_tokens_fp8(num_seqs, num_kv_heads, max_context_len))
 
 
 def pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
@@ -255,6 +290,58 @@ def pkv_prefill_attn(q, k_cache, v_cache, block_tables, cu_new_lens, context_len
                                 int(max_new_len), int(max_context_len), hq, float(scale),
                                 out.data_ptr(), _stream(q, stream)),
            "pkv_prefill_attn")
+    return out
+
+
+def pkv_store_fp8(k, v, slot_mapping, k_codes, v_codes, k_scale, v_scale, stream=None):
+    """Quantize k/v ([T][Hkv][d] bf16) into an FP8 cache (E4M3 codes uint8
+    [NB][Hkv][16][d], fp32 scales [NB][Hkv][16]) at slot_mapping ([T] int32)."""
+    import torch
+
+    lib = load()
+    cache = _cache_fp8(k_codes, v_codes, k_scale, v_scale)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    t = slot_mapping.shape[0]
+    want = (t, cache.num_kv_heads, cache.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want:
+        raise ValueError(f"k/v must be {want}, got {tuple(k.shape)} / {tuple(v.shape)}")
+    _check(lib.pkv_store_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), t, cache,
+                             _stream(k_codes, stream)), "pkv_store_fp8")
+
+
+def pkv_decode_attn_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens, scale,
+                        out, max_context_len: Optional[int] = None, workspace=None,
+                        partition_tokens: int = 0, stream=None):
+    """pkv_decode_attn over an FP8 cache (see pkv_store_fp8 for its layout)."""
+    import torch
+
+    lib = load()
+    cache = _cache_fp8(k_codes, v_codes, k_scale, v_scale)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    s, hq, d = q.shape
+    if tuple(out.shape) != (s, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables / context_lens do not match q's sequence count")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * cache.block_size
+    p = partition_tokens or pkv_decode_partition_tokens_fp8(s, cache.num_kv_heads,
+                                                            max_context_len)
+    need = pkv_decode_workspace_bytes(s, hq, d, max_context_len, p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib.pkv_decode_attn_fp8(q.data_ptr(), cache, block_tables.data_ptr(), max_blocks,
+                                   context_lens.data_ptr(), s, int(max_context_len), hq,
+                                   float(scale), out.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel(), int(p), _stream(q, stream)),
+           "pkv_decode_attn_fp8")
     return out
 
 

@@ -89,6 +89,43 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kNontemporal));
 }
 
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kNontemporal));
+}
+
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+
+// Eight OCP E4M3 codes (bytes of u, in order) to four packed bf16 pairs:
+// every E4M3 value, subnormals included, is exactly a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+
+__device__ __forceinline__ uint4 fp8x8_to_bf16(const uint2 &u) {
+    return make_uint4(fp8x2_to_bf16<false>(u.x), fp8x2_to_bf16<true>(u.x),
+                      fp8x2_to_bf16<false>(u.y), fp8x2_to_bf16<true>(u.y));
+}
+
+// Eight OCP E4M3 codes to fp32.
+__device__ __forceinline__ void fp8x8_to_f32(const uint2 &u, float (&f)[8]) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.x, true);
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, false);
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)u.y, true);
+    f[0] = a.x;
+    f[1] = a.y;
+    f[2] = b.x;
+    f[3] = b.y;
+    f[4] = c.x;
+    f[5] = c.y;
+    f[6] = d.x;
+    f[7] = d.y;
+}
+
 // 2^x with the hardware instruction: exact at 0 (2^0 = 1), 0 at -inf, and
 // results below the normal range flush to 0 -- all that a softmax weight needs
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -175,13 +212,22 @@ struct NewToken {
 // kvh.  On return every lane holds, for each head g of the group, the wave's
 // running max mg[g] (log2 domain), weight sum lg[g] and the unnormalised
 // output acc[g][0..7] for head_dim elements 8c .. 8c+7 (c = lane % LPR).
-template <int D, int G>
+//
+// FP8 = true reads an FP8 cache (OCP E4M3 codes, one fp32 scale per token and
+// KV head in k_scale / v_scale [block][kv head][16]).  The lane layout is the
+// bf16 one -- 8 elements per lane per load, 8-byte loads of 512 bytes per
+// instruction -- and the K codes become bf16 pairs for the same dot products;
+// a token's K scale multiplies its scores, its V scale its weights.
+template <int D, int G, bool FP8 = false>
 __device__ __forceinline__ void wave_attend(
-    const uint16_t *__restrict__ q, const uint16_t *k_cache, const uint16_t *v_cache,
-    const int32_t *__restrict__ bt, int32_t num_blocks, int32_t num_q_heads,
-    int32_t num_kv_heads, float scale_log2, int s, int kvh, int t_begin, int t_end,
-    const NewToken &nt, float (&acc)[G][8], float (&mg)[G], float (&lg)[G]) {
+    const uint16_t *__restrict__ q, const void *k_cache, const void *v_cache,
+    const float *k_scale, const float *v_scale, const int32_t *__restrict__ bt,
+    int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, float scale_log2, int s,
+    int kvh, int t_begin, int t_end, const NewToken &nt, float (&acc)[G][8], float (&mg)[G],
+    float (&lg)[G]) {
     using Geo = DecodeGeom<D, G>;
+    using Tile = typename std::conditional<FP8, uint2, uint4>::type;  // one lane's 8 elements
+    constexpr uint32_t EB = FP8 ? 1 : 2;                               // bytes per element
     constexpr int LPR = Geo::LPR, TPL = Geo::TPL, NL = Geo::NL, LPH = Geo::LPH;
     const float kNegInf = -INFINITY;
 
@@ -208,7 +254,7 @@ __device__ __forceinline__ void wave_attend(
     float m = kNegInf;  // running max of this row's scores for my_head (log2 domain)
     float l = 0.f;      // running sum of this row's weights for my_head
 
-    const size_t tile = (size_t)kBlockTokens * D;  // elements of one (block, head) tile
+    const size_t tile = (size_t)kBlockTokens * D * EB;  // bytes of one (block, head) tile
     const int b_begin = t_begin / kBlockTokens;
     const int b_end = (t_end + kBlockTokens - 1) / kBlockTokens;
 
@@ -216,23 +262,39 @@ __device__ __forceinline__ void wave_attend(
     // the tile, size = one tile) plus a fixed per-lane offset, so the loads
     // need no per-block vector address arithmetic, and a read can never leave
     // the tile.
-    const uint32_t lane_off = lane * 16u;
+    const uint32_t lane_off = lane * 8u * EB;
     const int b_last = b_end - 1;
     // Prefetches run up to two blocks past the span; those get an empty
     // buffer range, so they still count as issued loads (the waits stay
-    // static) but fetch nothing and return zeros.
-    auto load = [&](uint4 (&kb)[NL], uint4 (&vb)[NL], int b) {
+    // static) but fetch nothing and return zeros.  Token row r of load j is
+    // token j * TPL + r of the block; with FP8 its two scales come along.
+    auto load = [&](Tile (&kb)[NL], Tile (&vb)[NL], float (&ks)[NL], float (&vs)[NL], int b) {
         int pb = bt[min(b, b_last)];
         // an out-of-range id is a caller error; read block 0 instead of faulting
         pb = ((unsigned)pb < (unsigned)num_blocks) ? pb : 0;
-        const size_t off = ((size_t)pb * num_kv_heads + kvh) * tile;
-        const uint32_t bytes = b <= b_last ? (uint32_t)(tile * 2) : 0u;
-        const auto kr = tile_rsrc(k_cache + off, bytes);
-        const auto vr = tile_rsrc(v_cache + off, bytes);
+        const size_t unit = (size_t)pb * num_kv_heads + kvh;
+        const uint32_t bytes = b <= b_last ? (uint32_t)tile : 0u;
+        const auto kr = tile_rsrc(static_cast<const char *>(k_cache) + unit * tile, bytes);
+        const auto vr = tile_rsrc(static_cast<const char *>(v_cache) + unit * tile, bytes);
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
-            kb[j] = buffer_load16(kr, lane_off + j * 1024u);
-            vb[j] = buffer_load16(vr, lane_off + j * 1024u);
+            if constexpr (FP8) {
+                kb[j] = buffer_load8(kr, lane_off + j * 512u);
+                vb[j] = buffer_load8(vr, lane_off + j * 512u);
+            } else {
+                kb[j] = buffer_load16(kr, lane_off + j * 1024u);
+                vb[j] = buffer_load16(vr, lane_off + j * 1024u);
+            }
+        }
+        if constexpr (FP8) {
+            const uint32_t sbytes = b <= b_last ? kBlockTokens * 4u : 0u;
+            const auto ksr = tile_rsrc(k_scale + unit * kBlockTokens, sbytes);
+            const auto vsr = tile_rsrc(v_scale + unit * kBlockTokens, sbytes);
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                ks[j] = buffer_load_f32(ksr, (j * TPL + row) * 4u);
+                vs[j] = buffer_load_f32(vsr, (j * TPL + row) * 4u);
+            }
         }
     };
 
@@ -261,15 +323,24 @@ __device__ __forceinline__ void wave_attend(
         x.w = here ? y.w : x.w;
     };
 
-    auto process = [&](uint4 (&kb)[NL], uint4 (&vb)[NL], int b) {
+    auto process = [&](Tile (&kt)[NL], Tile (&vt)[NL], const float (&ks)[NL],
+                       const float (&vs)[NL], int b) {
         const int tb = b * kBlockTokens;
         const bool partial = tb + kBlockTokens > t_end;
-        if (b == patch_block) {
+        uint4 kb[NL];  // K as bf16 pairs
+        if constexpr (FP8) {
 #pragma unroll
-            for (int j = 0; j < NL; ++j) {
-                const bool here = j == patch_load && patch_row;
-                patch(kb[j], kn, here);
-                patch(vb[j], vn, here);
+            for (int j = 0; j < NL; ++j) kb[j] = fp8x8_to_bf16(kt[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NL; ++j) kb[j] = kt[j];
+            if (b == patch_block) {
+#pragma unroll
+                for (int j = 0; j < NL; ++j) {
+                    const bool here = j == patch_load && patch_row;
+                    patch(kb[j], kn, here);
+                    patch(vt[j], vn, here);
+                }
             }
         }
         // partial dot products: v[p * NL + j] = q(head at position p) . K(token j)
@@ -293,7 +364,7 @@ __device__ __forceinline__ void wave_attend(
         float bm = kNegInf;
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
-            sc[j] = v[j] * scale_log2;
+            sc[j] = (FP8 ? v[j] * ks[j] : v[j]) * scale_log2;
             if (partial) sc[j] = (tb + j * TPL + row < t_end) ? sc[j] : kNegInf;
             bm = fmaxf(bm, sc[j]);
         }
@@ -322,15 +393,22 @@ __device__ __forceinline__ void wave_attend(
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             float vf[8];
-            unpack8(vb[j], vf);
-            if (partial) {
+            float pj = pr[j];  // the weight, times the token's V scale for FP8
+            if constexpr (FP8) {
+                fp8x8_to_f32(vt[j], vf);
+                pj *= vs[j];
+            } else {
+                unpack8(vt[j], vf);
+            }
+            if (partial) {  // rows past the end: NaN codes, scales or bits stay out
                 const bool live = tb + j * TPL + row < t_end;
 #pragma unroll
                 for (int x = 0; x < 8; ++x) vf[x] = live ? vf[x] : 0.f;
+                pj = live ? pj : 0.f;
             }
             static_for<G>([&](auto gc) {
                 constexpr int g = decltype(gc)::value;
-                const float pg = row_bcast<Geo, g * LPH>(pr[j], row_base);
+                const float pg = row_bcast<Geo, g * LPH>(pj, row_base);
 #pragma unroll
                 for (int x = 0; x < 8; ++x) acc[g][x] = fmaf(pg, vf[x], acc[g][x]);
             });
@@ -341,18 +419,19 @@ __device__ __forceinline__ void wave_attend(
     // ahead of the one being computed.  The prefetches are unconditional (past
     // the end they fetch nothing), so the wait before each block covers only
     // the loads issued before it.
-    uint4 k0[NL], v0[NL], k1[NL], v1[NL], k2[NL], v2[NL];
-    load(k0, v0, b_begin);
-    load(k1, v1, b_begin + 1);
+    Tile k0[NL], v0[NL], k1[NL], v1[NL], k2[NL], v2[NL];
+    float ks0[NL], vs0[NL], ks1[NL], vs1[NL], ks2[NL], vs2[NL];  // FP8 scales (else unused)
+    load(k0, v0, ks0, vs0, b_begin);
+    load(k1, v1, ks1, vs1, b_begin + 1);
     for (int b = b_begin;;) {
-        load(k2, v2, b + 2);
-        process(k0, v0, b);
+        load(k2, v2, ks2, vs2, b + 2);
+        process(k0, v0, ks0, vs0, b);
         if (++b >= b_end) break;
-        load(k0, v0, b + 2);
-        process(k1, v1, b);
+        load(k0, v0, ks0, vs0, b + 2);
+        process(k1, v1, ks1, vs1, b);
         if (++b >= b_end) break;
-        load(k1, v1, b + 2);
-        process(k2, v2, b);
+        load(k1, v1, ks1, vs1, b + 2);
+        process(k2, v2, ks2, vs2, b);
         if (++b >= b_end) break;
     }
 
@@ -436,10 +515,10 @@ __device__ __forceinline__ void store_only(const NewToken &t) {
 // Split-KV decode: one wavefront per (sequence, KV head, partition of
 // partition_tokens tokens).  A sequence that fits one partition is written
 // directly; otherwise each partition writes (m, l, acc) for the merge pass.
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ __launch_bounds__(256) void decode_split_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *k_cache, const uint16_t *v_cache,
-    const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ q, const void *k_cache, const void *v_cache,
+    const float *k_scale, const float *v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, int32_t partition_tokens,
     int32_t max_parts, float scale_log2, uint16_t *__restrict__ out, float *__restrict__ ws_out,
@@ -477,8 +556,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                           s, kvh, ctx);
 
     float acc[G][8], mg[G], lg[G];
-    wave_attend<D, G>(q, k_cache, v_cache, bt_row, num_blocks, num_q_heads, num_kv_heads,
-                      scale_log2, s, kvh, t_begin, t_end, nt, acc, mg, lg);
+    wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
+                           num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end, nt, acc,
+                           mg, lg);
 
     if (nparts == 1) {
 #pragma unroll
@@ -512,10 +592,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 // The sequence's blocks are split evenly among the waves; each wave runs
 // wave_attend over its share and the waves merge their (m, l, acc) through
 // LDS, so no workspace and no second kernel are needed.
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ __launch_bounds__(512) void decode_fused_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *k_cache, const uint16_t *v_cache,
-    const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ q, const void *k_cache, const void *v_cache,
+    const float *k_scale, const float *v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, float scale_log2,
     uint16_t *__restrict__ out, const uint16_t *__restrict__ k_new,
@@ -555,9 +635,9 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
     float *lds_l = lds_m + W * G;
     if (b0 < b1) {
         float acc[G][8], mg[G], lg[G];
-        wave_attend<D, G>(q, k_cache, v_cache, bt_row, num_blocks, num_q_heads, num_kv_heads,
-                          scale_log2, s, kvh, b0 * kBlockTokens, min(b1 * kBlockTokens, ctx), nt,
-                          acc, mg, lg);
+        wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
+                               num_q_heads, num_kv_heads, scale_log2, s, kvh, b0 * kBlockTokens,
+                               min(b1 * kBlockTokens, ctx), nt, acc, mg, lg);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (g % TPL == row) {
@@ -642,16 +722,15 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     for (int e = 0; e < E; ++e) o[e] = (uint16_t)f32_to_bf16_rne(a[e] * inv);
 }
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const float scale_log2 = a.scale * 1.4426950408889634f;
     if (a.fused_waves > 0) {
         const int W = a.fused_waves;
         const size_t lds = (size_t)W * G * (D + 2) * sizeof(float);
-        hipLaunchKernelGGL((decode_fused_kernel<D, G>), dim3(a.num_kv_heads, a.num_seqs),
-                           dim3(64 * W), lds, stream, (const uint16_t *)a.q,
-                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache,
-                           a.block_tables, a.context_lens, a.max_blocks_per_seq,
+        hipLaunchKernelGGL((decode_fused_kernel<D, G, FP8>), dim3(a.num_kv_heads, a.num_seqs),
+                           dim3(64 * W), lds, stream, (const uint16_t *)a.q, a.k_cache, a.v_cache,
+                           a.k_scale, a.v_scale, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                            a.max_context_len, a.num_blocks, a.num_q_heads, a.num_kv_heads,
                            scale_log2, (uint16_t *)a.out, (const uint16_t *)a.k_new,
                            (const uint16_t *)a.v_new, a.slots, (uint16_t *)a.k_store,
@@ -660,9 +739,9 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     }
     const int waves = a.max_parts >= 4 ? 4 : (a.max_parts >= 2 ? 2 : 1);
     dim3 grid((a.max_parts + waves - 1) / waves, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(64 * waves), 0, stream,
-                       (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
-                       (const uint16_t *)a.v_cache, a.block_tables, a.context_lens,
+    hipLaunchKernelGGL((decode_split_kernel<D, G, FP8>), grid, dim3(64 * waves), 0, stream,
+                       (const uint16_t *)a.q, a.k_cache, a.v_cache, a.k_scale, a.v_scale,
+                       a.block_tables, a.context_lens,
                        a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.num_q_heads,
                        a.num_kv_heads, a.partition_tokens, a.max_parts, scale_log2,
                        (uint16_t *)a.out, a.ws_out, a.ws_ml, (const uint16_t *)a.k_new,
@@ -678,20 +757,24 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FP8>
 static hipError_t launch_decode_d(const DecodeArgs &a, hipStream_t stream) {
     switch (a.num_q_heads / a.num_kv_heads) {
-        case 1: return launch_decode_t<D, 1>(a, stream);
-        case 2: return launch_decode_t<D, 2>(a, stream);
-        case 4: return launch_decode_t<D, 4>(a, stream);
-        case 8: return launch_decode_t<D, 8>(a, stream);
+        case 1: return launch_decode_t<D, 1, FP8>(a, stream);
+        case 2: return launch_decode_t<D, 2, FP8>(a, stream);
+        case 4: return launch_decode_t<D, 4, FP8>(a, stream);
+        case 8: return launch_decode_t<D, 8, FP8>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     if (a.num_seqs == 0) return hipSuccess;
-    return a.head_dim == 64 ? launch_decode_d<64>(a, stream) : launch_decode_d<128>(a, stream);
+    if (a.fp8)
+        return a.head_dim == 64 ? launch_decode_d<64, true>(a, stream)
+                                : launch_decode_d<128, true>(a, stream);
+    return a.head_dim == 64 ? launch_decode_d<64, false>(a, stream)
+                            : launch_decode_d<128, false>(a, stream);
 }
 
 }  // namespace pkv

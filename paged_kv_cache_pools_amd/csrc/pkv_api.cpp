@@ -46,6 +46,35 @@ int check_cache(const pkv_cache &c) {
     return PKV_OK;
 }
 
+// One layer's pools as the launchers see them (bf16, or FP8 codes + scales).
+struct CacheDesc {
+    void *k, *v;
+    float *k_scale, *v_scale;
+    int32_t num_blocks, num_kv_heads, head_dim, block_size;
+    bool fp8;
+};
+
+CacheDesc desc_of(const pkv_cache &c) {
+    return CacheDesc{c.k, c.v, nullptr, nullptr, c.num_blocks, c.num_kv_heads, c.head_dim,
+                     c.block_size, false};
+}
+
+CacheDesc desc_of(const pkv_cache_fp8 &c) {
+    return CacheDesc{c.k, c.v, c.k_scale, c.v_scale, c.num_blocks, c.num_kv_heads, c.head_dim,
+                     c.block_size, true};
+}
+
+int check_cache(const CacheDesc &c) {
+    pkv_cache plain{c.k, c.v, c.num_blocks, c.num_kv_heads, c.head_dim, c.block_size};
+    int rc = check_cache(plain);
+    if (rc || !c.fp8) return rc;
+    if (c.num_blocks > 0 && (!c.k_scale || !c.v_scale))
+        return fail(PKV_ERR_NULL, "cache.k_scale or cache.v_scale is null");
+    if (!aligned16(c.k_scale) || !aligned16(c.v_scale))
+        return fail(PKV_ERR_ALIGN, "cache.k_scale / cache.v_scale must be 16-byte aligned");
+    return PKV_OK;
+}
+
 int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
     if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
         return fail(PKV_ERR_SHAPE, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
@@ -81,9 +110,11 @@ int32_t partition_for(int64_t units, int32_t max_context_len) {
 // split is the better choice.  Single-pass needs enough (sequence, KV head)
 // units to fill the GPU by itself and contexts short enough that one
 // workgroup per unit is not a straggler; it then gives each unit enough waves
-// for about four per CU, at least one block per wave.
-int32_t fused_waves_for(int64_t units, int32_t max_context_len) {
-    constexpr int64_t kMinUnits = 128, kTargetWaves = 1024;
+// for kTargetWaves in all (1024 = four per CU for bf16; the FP8 path, with
+// twice the arithmetic per byte, runs best at 2048 = two per SIMD), at least
+// one block per wave.
+int32_t fused_waves_for(int64_t units, int32_t max_context_len, int64_t kTargetWaves) {
+    constexpr int64_t kMinUnits = 128;
     constexpr int32_t kMaxContext = 8192, kMaxWaves = 8;
     if (units < kMinUnits || max_context_len <= 0 || max_context_len > kMaxContext) return 0;
     int32_t w = (int32_t)((kTargetWaves + units - 1) / units);
@@ -135,13 +166,30 @@ int pkv_store(const void *k, const void *v, const int32_t *slot_mapping, int32_t
     return hip_status(pkv::launch_store(a, stream), "pkv_store launch");
 }
 
-int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
-                                    int32_t max_context_len) {
+}  // extern "C"
+
+namespace {
+
+int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, bool fp8) {
     if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
     const int64_t units = (int64_t)num_seqs * num_kv_heads;
-    const int32_t w = fused_waves_for(units, max_context_len);
+    const int32_t w = fused_waves_for(units, max_context_len, fp8 ? 2048 : 1024);
     if (w > 0) return -w;
     return partition_for(units, max_context_len);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_context_len) {
+    return auto_split(num_seqs, num_kv_heads, max_context_len, false);
+}
+
+int32_t pkv_decode_partition_tokens_fp8(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t max_context_len) {
+    return auto_split(num_seqs, num_kv_heads, max_context_len, true);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -162,7 +210,7 @@ namespace {
 // Shared by pkv_decode_attn and pkv_store_decode_attn: validation, the work
 // split and the launch.  `fused` carries the store's k, v and slots (all null
 // for plain decode).
-int decode_call(const void *q, pkv_cache cache, const int32_t *block_tables,
+int decode_call(const void *q, const CacheDesc &cache, const int32_t *block_tables,
                 int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
                 int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
                 void *workspace, size_t workspace_bytes, int32_t partition_tokens,
@@ -191,7 +239,7 @@ int decode_call(const void *q, pkv_cache cache, const int32_t *block_tables,
                     partition_tokens);
     const int32_t choice =
         partition_tokens ? partition_tokens
-                         : pkv_decode_partition_tokens(num_seqs, cache.num_kv_heads, max_context_len);
+                         : auto_split(num_seqs, cache.num_kv_heads, max_context_len, cache.fp8);
     const int32_t fused = choice < 0 ? -choice : 0;
     const int32_t p = choice > 0 ? choice : kBlock;
     const int32_t parts = fused ? 1 : (max_context_len > 0 ? ceil_div(max_context_len, p) : 1);
@@ -228,6 +276,9 @@ int decode_call(const void *q, pkv_cache cache, const int32_t *block_tables,
     float *ws = static_cast<float *>(workspace);
     a.ws_out = need ? ws : nullptr;
     a.ws_ml = need ? ws + (size_t)num_seqs * num_q_heads * parts * cache.head_dim : nullptr;
+    a.fp8 = cache.fp8;
+    a.k_scale = cache.k_scale;
+    a.v_scale = cache.v_scale;
     if (slots != nullptr) {
         a.k_new = k_new;
         a.v_new = v_new;
@@ -247,9 +298,9 @@ int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
                     int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
                     void *workspace, size_t workspace_bytes, int32_t partition_tokens,
                     hipStream_t stream) {
-    return decode_call(q, cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       max_context_len, num_q_heads, scale, out, workspace, workspace_bytes,
-                       partition_tokens, stream, nullptr, nullptr, nullptr,
+    return decode_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                       workspace_bytes, partition_tokens, stream, nullptr, nullptr, nullptr,
                        "pkv_decode_attn launch");
 }
 
@@ -263,10 +314,38 @@ int pkv_store_decode_attn(const void *k, const void *v, const int32_t *slot_mapp
         return fail(PKV_ERR_NULL, "k, v or slot_mapping is null");
     if (!aligned16(k) || !aligned16(v))
         return fail(PKV_ERR_ALIGN, "k / v must be 16-byte aligned");
-    return decode_call(q, cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       max_context_len, num_q_heads, scale, out, workspace, workspace_bytes,
-                       partition_tokens, stream, k, v, slot_mapping,
+    return decode_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                       workspace_bytes, partition_tokens, stream, k, v, slot_mapping,
                        "pkv_store_decode_attn launch");
+}
+
+int pkv_decode_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                        int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                        void *workspace, size_t workspace_bytes, int32_t partition_tokens,
+                        hipStream_t stream) {
+    return decode_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                       workspace_bytes, partition_tokens, stream, nullptr, nullptr, nullptr,
+                       "pkv_decode_attn_fp8 launch");
+}
+
+int pkv_store_fp8(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,
+                  pkv_cache_fp8 cache, hipStream_t stream) {
+    int rc = check_cache(desc_of(cache));
+    if (rc) return rc;
+    if (num_tokens < 0) return fail(PKV_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!k || !v || !slot_mapping) return fail(PKV_ERR_NULL, "k, v or slot_mapping is null");
+    if (!aligned16(k) || !aligned16(v))
+        return fail(PKV_ERR_ALIGN, "k / v must be 16-byte aligned");
+    const int64_t threads = (int64_t)num_tokens * cache.num_kv_heads * (cache.head_dim / 8);
+    if (threads > (int64_t)0x7f000000)
+        return fail(PKV_ERR_SHAPE, "store of %d tokens is too large for one call", num_tokens);
+    pkv::StoreFp8Args a{k, v, slot_mapping, num_tokens, cache.k, cache.v, cache.k_scale,
+                        cache.v_scale, cache.num_blocks, cache.num_kv_heads, cache.head_dim};
+    return hip_status(pkv::launch_store_fp8(a, stream), "pkv_store_fp8 launch");
 }
 
 int pkv_prefill_attn(const void *q, pkv_cache cache, const int32_t *block_tables,

@@ -16,6 +16,16 @@ struct StoreArgs {
 };
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream);
 
+struct StoreFp8Args {
+    const void *k, *v;  // bf16 [num_tokens][num_kv_heads][head_dim]
+    const int32_t *slots;
+    int32_t num_tokens;
+    void *k_cache, *v_cache;    // fp8 codes [num_blocks][num_kv_heads][16][head_dim]
+    float *k_scale, *v_scale;   // fp32 [num_blocks][num_kv_heads][16]
+    int32_t num_blocks, num_kv_heads, head_dim;
+};
+hipError_t launch_store_fp8(const StoreFp8Args &a, hipStream_t stream);
+
 struct DecodeArgs {
     const void *q;
     const void *k_cache, *v_cache;
@@ -35,6 +45,10 @@ struct DecodeArgs {
     const void *k_new = nullptr, *v_new = nullptr;
     const int32_t *slots = nullptr;
     void *k_store = nullptr, *v_store = nullptr;
+    // FP8 cache: k_cache / v_cache hold E4M3 codes, these their fp32 scales
+    // [num_blocks][num_kv_heads][16]
+    bool fp8 = false;
+    const float *k_scale = nullptr, *v_scale = nullptr;
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

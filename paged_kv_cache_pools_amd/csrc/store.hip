@@ -51,6 +51,89 @@ __global__ __launch_bounds__(256) void store_kernel(const uint4 *__restrict__ k,
     }
 }
 
+// ---- FP8 cache: OCP E4M3 codes with one fp32 scale per (token, KV head) ----
+//
+// The LLM primer (part 4, §17.6) counts an FP8 KV cache at one byte per
+// element.  Each (token, KV head) row of head_dim values is quantized on its
+// own: scale = amax / 448 (448 = the largest finite E4M3 magnitude; 1 when
+// the row is all zero) and code = E4M3(x / scale), rounded to nearest even,
+// with x / scale clamped to [-448, 448] first so the conversion never
+// saturates.  Both divisions are correctly rounded fp32.  A group of D/8
+// lanes owns a row (8 values per lane, one 16-byte load); the row's amax is
+// an all-reduce over the group.
+
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
+}
+
+// Quantize this lane's 8 values of a row whose group is LPR lanes wide; every
+// lane of the wave must call it (it shuffles across the group).
+template <int LPR>
+__device__ __forceinline__ uint2 quantize8(const uint4 &u, float &scale) {
+    float f[8];
+    unpack8(u, f);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(__fdiv_rn(f[i], scale), -448.f), 448.f);
+    return make_uint2(fp8x4(y[0], y[1], y[2], y[3]), fp8x4(y[4], y[5], y[6], y[7]));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void store_fp8_kernel(
+    const uint4 *__restrict__ k, const uint4 *__restrict__ v, const int32_t *__restrict__ slots,
+    int32_t num_tokens, uint2 *__restrict__ kc, uint2 *__restrict__ vc, float *__restrict__ ks,
+    float *__restrict__ vs, int32_t num_blocks, int32_t num_kv_heads) {
+    constexpr int LPR = D / 8;  // lanes per (token, head) row
+    const int32_t rows = num_tokens * num_kv_heads;
+    const int32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+    const int32_t row = gid / LPR;
+    const int c = threadIdx.x % LPR;
+    const bool in_range = row < rows;  // no early exit: the whole group shuffles
+    const int32_t r = in_range ? row : 0;
+    const int32_t t = r / num_kv_heads, h = r % num_kv_heads;
+    const uint4 kk = k[(size_t)r * LPR + c];
+    const uint4 vv = v[(size_t)r * LPR + c];
+    const int32_t slot = slots[t];
+    float ksc, vsc;
+    const uint2 kq = quantize8<LPR>(kk, ksc);
+    const uint2 vq = quantize8<LPR>(vv, vsc);
+    // slot < 0 is a padding token; a block past the pool is never written
+    if (!in_range || slot < 0 || slot / kBlockTokens >= num_blocks) return;
+    const size_t dst_row = ((size_t)(slot / kBlockTokens) * num_kv_heads + h) * kBlockTokens +
+                           slot % kBlockTokens;
+    kc[dst_row * LPR + c] = kq;
+    vc[dst_row * LPR + c] = vq;
+    if (c == 0) {
+        ks[dst_row] = ksc;
+        vs[dst_row] = vsc;
+    }
+}
+
+hipError_t launch_store_fp8(const StoreFp8Args &a, hipStream_t stream) {
+    if (a.num_tokens == 0) return hipSuccess;
+    const int64_t threads_total = (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / 8);
+    const int threads = 256;
+    const unsigned blocks = (unsigned)((threads_total + threads - 1) / threads);
+    if (a.head_dim == 64)
+        hipLaunchKernelGGL(store_fp8_kernel<64>, dim3(blocks), dim3(threads), 0, stream,
+                           (const uint4 *)a.k, (const uint4 *)a.v, a.slots, a.num_tokens,
+                           (uint2 *)a.k_cache, (uint2 *)a.v_cache, a.k_scale, a.v_scale,
+                           a.num_blocks, a.num_kv_heads);
+    else
+        hipLaunchKernelGGL(store_fp8_kernel<128>, dim3(blocks), dim3(threads), 0, stream,
+                           (const uint4 *)a.k, (const uint4 *)a.v, a.slots, a.num_tokens,
+                           (uint2 *)a.k_cache, (uint2 *)a.v_cache, a.k_scale, a.v_scale,
+                           a.num_blocks, a.num_kv_heads);
+    return hipGetLastError();
+}
+
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream) {
     if (a.num_tokens == 0) return hipSuccess;
     const int chunks = a.head_dim / 8;

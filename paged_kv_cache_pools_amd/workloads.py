@@ -331,7 +331,9 @@ def make_tensors(wl: Workload, device="cpu", layers: Optional[int] = None, nan_f
 def make_fp8_pools(wl: Workload, device="cpu", seed: Optional[int] = None, nan_fill: bool = True):
     """Random FP8 (OCP E4M3) pools for one layer: codes drawn uniformly from the
     finite codes (every byte but 0x7f and 0xff), scales drawn log-uniform in
-    [2^-3, 2^3).  With ``nan_fill`` every slot that holds no cached token (tails,
+    [2^-7.5, 2^-6.5), so a row's largest magnitude (448 x scale) lies between
+    about 2.5 and 5, as for N(0,1) data.  With ``nan_fill`` every slot that holds
+    no cached token (tails,
     unreferenced blocks, the slots this step's store writes) gets the NaN code
     and a NaN scale.  Returns (k_codes, v_codes, k_scales, v_scales) tensors:
     uint8 [NB][Hkv][bs][d] and float32 [NB][Hkv][bs]."""
@@ -346,7 +348,7 @@ def make_fp8_pools(wl: Workload, device="cpu", seed: Optional[int] = None, nan_f
         c = c + (c >= 0x7f).to(torch.int32)          # skip 0x7f: 0..0x7e, 0x80..0xfe
         out.append(c.to(torch.uint8))
     for _ in range(2):
-        e = torch.rand(shape[:3], generator=gen, device=device, dtype=torch.float32) * 6.0 - 3.0
+        e = torch.rand(shape[:3], generator=gen, device=device, dtype=torch.float32) - 7.5
         out.append(torch.exp2(e))
     if nan_fill:
         dead = torch.from_numpy(~live_slot_mask(wl, pre_store=True)).to(device)

@@ -155,3 +155,28 @@ def test_store_decode_validation(lib):
     assert sd(k=FAKE + 4) == 4
     assert sd(q=0) == 1                     # the decode checks still apply
     assert B.pkv_last_error() != ""
+
+
+def test_fp8_validation(lib):
+    c8 = lambda ks=FAKE, vs=FAKE, d=64: B.PkvCacheFp8(FAKE, FAKE, ks, vs, 16, 2, d, 16)
+    st = lambda c, n=4: lib.pkv_store_fp8(FAKE, FAKE, FAKE, n, c, None)
+    assert st(c8(), 0) == 0
+    assert st(c8(ks=0)) == 1
+    assert st(c8(vs=FAKE + 4)) == 4
+    assert st(c8(d=96)) == 3
+    dec = lambda c: lib.pkv_decode_attn_fp8(FAKE, c, FAKE, 3, FAKE, 2, 37, 4,
+                                            ctypes.c_float(0.125), FAKE, FAKE, 1 << 30, 0, None)
+    assert dec(c8(ks=0)) == 1
+    assert dec(c8(vs=FAKE + 8)) == 4
+    assert B.pkv_last_error() != ""
+
+
+def test_fp8_partition_heuristic(lib):
+    # the 32 x 4096 GQA batch: single pass with 8 waves (twice the bf16 choice)
+    assert B.pkv_decode_partition_tokens_fp8(32, 8, 4096) == -8
+    for s, h, ctx in ((1, 1, 1), (2, 2, 37), (256, 8, 32768), (16, 32, 2048), (64, 8, 16)):
+        p = B.pkv_decode_partition_tokens_fp8(s, h, ctx)
+        assert (p % 16 == 0 and 64 <= p <= 1024) or (-8 <= p <= -1), (s, h, ctx, p)
+        if p > 0:  # the P = 0 workspace bound covers the FP8 choice too
+            assert B.pkv_decode_workspace_bytes(s, 4 * h, 128, ctx, p) <= \
+                B.pkv_decode_workspace_bytes(s, 4 * h, 128, ctx, 0)

@@ -394,3 +394,107 @@ def test_fused_store_decode_mistral_full_size():
             slot = int(wl.slot_mapping[s])
             got = bits(t["k_caches"][l][slot // 16, :, slot % 16])
             assert np.array_equal(got, h["k_new"][i]), (l, s)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3, one fp32 scale per token and KV head) cache.  Dequantized
+# values (code x scale) are not bf16 values, so even a one-token context
+# rounds on output, and single-key rows reach magnitudes near 5: the
+# attention bound adds each element's own bf16 rounding to 1e-2.
+# ---------------------------------------------------------------------------
+
+def fp8_case(wl, nan_fill=True):
+    """Host and device FP8 pools for one layer (random codes and scales)."""
+    pools = W.make_fp8_pools(wl, device="cpu", nan_fill=nan_fill)
+    host = [x.numpy().copy() for x in pools]
+    dev = [x.cuda() for x in pools]
+    return host, dev
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen_mha", "chunked_prefill"])
+def test_store_fp8_bit_exact(name):
+    wl = W.CONFIGS[name]()
+    say(f"[gpu] store fp8 {name}: T={wl.num_tokens}")
+    c = Case(wl)
+    host, dev = fp8_case(wl)
+    slot_t = c.dev["slot_mapping"]
+    B.pkv_store_fp8(c.dev["k_new"], c.dev["v_new"], slot_t, *dev)
+    torch.cuda.synchronize()
+    orc().store_fp8(c.h["k_new"], c.h["v_new"], wl.slot_mapping, *host)
+    for got, ref, what in zip(dev, host, ("k codes", "v codes", "k scales", "v scales")):
+        g = got.cpu().numpy()
+        assert np.array_equal(g.view(np.uint8), ref.view(np.uint8)), what
+
+
+def test_store_fp8_skips_and_d64():
+    wl = W.make_decode("fp8_skip", [20, 33, 7, 16], 4, 2, 64, 71, spare_blocks=2)
+    slots = wl.slot_mapping.copy()
+    slots[1] = -1
+    slots[3] = wl.num_blocks * 16 + 2      # outside the pool: never written
+    c = Case(wl)
+    host, dev = fp8_case(wl)
+    B.pkv_store_fp8(c.dev["k_new"], c.dev["v_new"], torch.from_numpy(slots).cuda(), *dev)
+    torch.cuda.synchronize()
+    slots_oracle = slots.copy()
+    slots_oracle[3] = -1                   # the oracle rejects out-of-pool slots
+    orc().store_fp8(c.h["k_new"], c.h["v_new"], slots_oracle, *host)
+    for got, ref in zip(dev, host):
+        assert np.array_equal(got.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 4, 8])
+@pytest.mark.parametrize("part", [16, 64, 0, -1, -3])
+def test_decode_fp8_edge_lengths(d, g, part):
+    lens = [1, 15, 16, 17, 63, 64, 65, 129, 0, 300]
+    wl = W.make_decode(f"fp8_d{d}_g{g}", lens, 2 * g, 2, d, 400 + d + g, spare_blocks=2,
+                       store=False)
+    c = Case(wl)
+    host, dev = fp8_case(wl)
+    say(f"[gpu] decode fp8 d={d} G={g} P={part}")
+    out = torch.empty_like(c.dev["q"])
+    B.pkv_decode_attn_fp8(c.dev["q"], *dev, c.dev["block_tables"], c.dev["context_lens"],
+                          wl.scale, out, max_context_len=wl.max_context_len, partition_tokens=part)
+    torch.cuda.synchronize()
+    ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
+    compare(out, ref, f"decode fp8 d{d} g{g} P{part}", plus_floor=True)
+
+
+def test_store_then_decode_fp8():
+    """A decode step on an FP8 cache: quantizing store of the new tokens, then
+    attention over the cache including them, against the oracle doing both."""
+    wl = W.make_decode("fp8_step", [5, 37, 200, 1, 64], 8, 2, 128, 72, spare_blocks=1)
+    c = Case(wl)
+    host, dev = fp8_case(wl)
+    B.pkv_store_fp8(c.dev["k_new"], c.dev["v_new"], c.dev["slot_mapping"], *dev)
+    out = torch.empty_like(c.dev["q"])
+    B.pkv_decode_attn_fp8(c.dev["q"], *dev, c.dev["block_tables"], c.dev["context_lens"],
+                          wl.scale, out, max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    orc().store_fp8(c.h["k_new"], c.h["v_new"], wl.slot_mapping, *host)
+    ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
+    compare(out, ref, "store + decode fp8", plus_floor=True)
+
+
+def test_decode_fp8_mistral_full_size():
+    """32 x 4096 GQA over FP8 pools in the benchmark's launch configuration;
+    the oracle checks sampled sequences on compacted copies."""
+    wl = W.mistral_gqa(num_layers=1)
+    seqs = [0, 17, 31]
+    say(f"[gpu] decode fp8 full size, oracle on seqs {seqs}")
+    t = W.make_tensors(wl, device="cuda", layers=1, nan_fill=False)
+    pools = W.make_fp8_pools(wl, device="cuda", nan_fill=True)
+    B.pkv_store_fp8(t["k_new"], t["v_new"], t["slot_mapping"], *pools)
+    out = torch.empty_like(t["q"])
+    B.pkv_decode_attn_fp8(t["q"], *pools, t["block_tables"], t["context_lens"], wl.scale, out,
+                          max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    rows = [wl.block_tables[s, : (int(wl.context_lens[s]) + 15) // 16] for s in seqs]
+    ids = np.unique(np.concatenate(rows))
+    remap = {int(b): i for i, b in enumerate(ids)}
+    idx = torch.from_numpy(ids.astype(np.int64)).cuda()
+    host = [p.index_select(0, idx).cpu().numpy() for p in pools]
+    bt = np.stack([[remap[int(b)] for b in r] for r in rows]).astype(np.int32)
+    q = bits(t["q"][seqs])
+    ref = orc().decode_fp8(q, *host, bt, wl.context_lens[seqs], wl.scale)
+    compare(out[seqs], ref, "decode fp8 full size", plus_floor=True)
