@@ -58,6 +58,8 @@ def _bind(lib):
                                 _I32, ctypes.c_float, _P, ctypes.c_int]
     lib.pko_default_threads.restype = ctypes.c_int
     lib.pko_default_threads.argtypes = []
+    lib.pko_rope.restype = ctypes.c_int
+    lib.pko_rope.argtypes = [_P, _P, _I32, _I32, _I32, _P, _I32, _P]
     lib.pko_fp8_decode.restype = ctypes.c_double
     lib.pko_fp8_decode.argtypes = [ctypes.c_uint8]
     lib.pko_fp8_encode.restype = ctypes.c_uint8
@@ -122,6 +124,21 @@ class Oracle:
                                  int(nthreads))
         if rc != OK:
             raise OracleError(rc, "decode")
+        return out
+
+    # -- rotary position embedding ------------------------------------------------------
+    def rope(self, x, positions, cos_sin):
+        """x [n][H][d] uint16 bf16 bits rotated at positions [n] with the fp32
+        table cos_sin [P][d] -> new uint16 array."""
+        x = _u16(x)
+        pos = _i32(positions)
+        cs = np.ascontiguousarray(cos_sin, np.float32)
+        n, h, d = x.shape
+        assert pos.shape == (n,) and cs.ndim == 2 and cs.shape[1] == d
+        out = np.empty_like(x)
+        rc = self.lib.pko_rope(_ptr(x), _ptr(pos), n, h, d, _ptr(cs), cs.shape[0], _ptr(out))
+        if rc != OK:
+            raise OracleError(rc, "rope")
         return out
 
     # -- FP8 (OCP E4M3, one fp32 scale per token and KV head) ------------------------

@@ -623,3 +623,66 @@ int pko_decode_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_c
     free(scores);
     return PKO_OK;
 }
+
+
+/* ------------------------------------------------------------------------ */
+/* Rotary position embedding                                                */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 of a float, round to nearest, ties to even (NaN stays NaN). */
+static uint16_t float_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+/*
+ * Rotary position embedding of rows of head_dim bf16 values, [NVE] §3.2 (RoPE
+ * puts position into Q and K before attention) and [LLM4] §21.2 / §22 step 4
+ * (no position vector is added; Q and K are rotated inside attention).  The
+ * pages fix no formula; the reading taken is the rotation of element pairs
+ * (i, i + d/2) by the angle whose cosine and sine the caller tabulates per
+ * position:
+ *   y[i]       = x[i] * c_i - x[i + d/2] * s_i
+ *   y[i + d/2] = x[i + d/2] * c_i + x[i] * s_i,   i < d/2,
+ *   c_i = cos_sin[p][i],  s_i = cos_sin[p][d/2 + i]   (fp32 table [positions][d])
+ * every product and sum in fp32 (no fused multiply-add), the result rounded
+ * to bf16 -- as a model materializes rotated q and k before attention.
+ * rows: num_rows x heads rows of head_dim; positions[r] is row r's position.
+ */
+int pko_rope(const uint16_t *x, const int32_t *positions, int32_t num_rows, int32_t heads,
+             int32_t head_dim, const float *cos_sin, int32_t max_positions, uint16_t *out)
+{
+    if (num_rows < 0 || heads <= 0 || head_dim <= 0 || head_dim % 2 || max_positions <= 0)
+        return PKO_ERR_ARG;
+    int32_t half = head_dim / 2;
+    for (int32_t r = 0; r < num_rows; ++r) {
+        int32_t p = positions[r];
+        if (p < 0 || p >= max_positions)
+            return PKO_ERR_RANGE;
+        const float *c = cos_sin + (int64_t)p * head_dim;
+        const float *sn = c + half;
+        for (int32_t h = 0; h < heads; ++h) {
+            const uint16_t *xr = x + ((int64_t)r * heads + h) * head_dim;
+            uint16_t *yr = out + ((int64_t)r * heads + h) * head_dim;
+            for (int32_t i = 0; i < half; ++i) {
+                float x1 = bf16_bits_to_float(xr[i]);
+                float x2 = bf16_bits_to_float(xr[i + half]);
+                float a = x1 * c[i];
+                float b = x2 * sn[i];
+                float y1 = a - b;
+                float e = x2 * c[i];
+                float f = x1 * sn[i];
+                float y2 = e + f;
+                yr[i] = float_to_bf16_rne(y1);
+                yr[i + half] = float_to_bf16_rne(y2);
+            }
+        }
+    }
+    return PKO_OK;
+}

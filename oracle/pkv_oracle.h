@@ -55,6 +55,10 @@ int pko_store_fp8(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapp
                   int32_t num_tokens, uint8_t *k_codes, uint8_t *v_codes, float *k_scales,
                   float *v_scales, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                   int32_t block_size);
+/* Rotary position embedding of bf16 rows (see pkv_oracle.c for the formula). */
+int pko_rope(const uint16_t *x, const int32_t *positions, int32_t num_rows, int32_t heads,
+             int32_t head_dim, const float *cos_sin, int32_t max_positions, uint16_t *out);
+
 int pko_decode_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_codes,
                    const float *k_scales, const float *v_scales, int32_t num_blocks,
                    const int32_t *block_tables, int32_t max_blocks_per_seq,

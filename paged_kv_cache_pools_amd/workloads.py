@@ -359,6 +359,16 @@ def make_fp8_pools(wl: Workload, device="cpu", seed: Optional[int] = None, nan_f
     return tuple(out)
 
 
+def rope_table(max_positions: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """fp32 [max_positions][head_dim] table of cos (first half) and sin (second
+    half) of position * base^(-2i / head_dim), i < head_dim / 2, computed in
+    fp64 and rounded once: the caller-side input of the rotary embedding."""
+    half = head_dim // 2
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / head_dim)
+    ang = np.arange(max_positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
 def bf16_bits(t) -> np.ndarray:
     """Host numpy uint16 view of a bf16 torch tensor's bits."""
     import torch

@@ -511,4 +511,65 @@ def pin_decode_fp8_unit_scales_equal_bf16(orc):
     assert np.array_equal(out, ref)
 
 
+# ---------------------------------------------------------------------------
+# rotary position embedding
+# ---------------------------------------------------------------------------
+
+def _rope_inputs(n=6, heads=3, dim=64, seed=50, max_pos=4096):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(n, heads, dim, generator=g).to(torch.bfloat16)
+    pos = np.array([0, 1, 17, 255, 4095, 1000][:n], np.int32)
+    return _bits(x), pos, W.rope_table(max_pos, dim)
+
+
+def pin_rope_matches_torch_rotate_half(orc):
+    """The rotation equals torch's fp32 x * cos + rotate_half(x) * sin (the
+    rotate-half layout: element i pairs with i + d/2), rounded to bf16, bit for
+    bit, for d 64 and 128 and positions up to 4095."""
+    for dim in (64, 128):
+        x, pos, table = _rope_inputs(dim=dim)
+        got = orc.rope(x, pos, table)
+        xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
+        cs = torch.from_numpy(table[pos])                       # [n][d]
+        half = dim // 2
+        cos = torch.cat([cs[:, :half], cs[:, :half]], dim=1)[:, None, :]
+        sin = torch.cat([cs[:, half:], cs[:, half:]], dim=1)[:, None, :]
+        rot = torch.cat([-xt[..., half:], xt[..., :half]], dim=-1)
+        ref = (xt * cos + rot * sin).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, ref), dim
+
+
+def pin_rope_special_angles(orc):
+    """A zero angle leaves the row unchanged; a quarter turn maps (x1, x2) to
+    (-x2, x1) exactly."""
+    x, _, _ = _rope_inputs(dim=64)
+    table = np.zeros((2, 64), np.float32)
+    table[0, :32] = 1.0                    # cos 1, sin 0
+    table[1, 32:] = 1.0                    # cos 0, sin 1
+    same = orc.rope(x, np.zeros(len(x), np.int32), table)
+    assert np.array_equal(same, x)
+    quarter = orc.rope(x, np.ones(len(x), np.int32), table)
+    neg = x[..., 32:] ^ np.uint16(0x8000)
+    assert np.array_equal(quarter[..., :32], neg) and np.array_equal(quarter[..., 32:], x[..., :32])
+
+
+def pin_rope_relative_position(orc):
+    """Rotated scores depend on the distance between positions only: q at m and
+    k at n score like q at m + t and k at n + t (up to the bf16 rounding of
+    the rotated rows)."""
+    g = torch.Generator().manual_seed(51)
+    q = _bits(torch.randn(1, 1, 128, generator=g).to(torch.bfloat16))
+    k = _bits(torch.randn(1, 1, 128, generator=g).to(torch.bfloat16))
+    table = W.rope_table(8192, 128)
+    def score(m, n):
+        a = _f64(orc.rope(q, np.array([m], np.int32), table))
+        b = _f64(orc.rope(k, np.array([n], np.int32), table))
+        return float((a * b).sum())
+    for m, n, t in ((5, 2, 100), (300, 299, 4000), (0, 0, 7000), (1000, 10, 3)):
+        s0, s1 = score(m, n), score(m + t, n + t)
+        assert abs(s0 - s1) <= 0.05 + 0.01 * abs(s0), (m, n, t, s0, s1)
+    # and a different distance really changes the score
+    assert abs(score(5, 2) - score(5, 40)) > 0.05
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -50,6 +50,12 @@ MUTANTS = [
     ("fp8_v_stored_from_k", "quantize_row(v + src, head_dim, v_codes", "quantize_row(k + src, head_dim, v_codes"),
     ("fp8_decode_v_from_k", "o[x] += scores[t] * vd[row * head_dim + x];",
      "o[x] += scores[t] * kd[row * head_dim + x];"),
+    # rotary position embedding
+    ("rope_rotates_backwards", "float y1 = a - b;", "float y1 = a + b;"),
+    ("rope_interleaved_pairs", "float x2 = bf16_bits_to_float(xr[i + half]);",
+     "float x2 = bf16_bits_to_float(xr[(i + 1) % head_dim]);"),
+    ("rope_cos_sin_swapped", "const float *sn = c + half;", "const float *sn = c; c = c + half;"),
+    ("rope_truncates", "u += 0x7fffu + lsb;", "u += 0u * lsb;"),
 ]
 
 
