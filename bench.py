@@ -53,6 +53,8 @@ def parse():
                     help="skip the FP8-cache leg of the decode workload")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the Qwen-style MHA and continuous-batch decode workloads")
+    ap.add_argument("--no-rope", action="store_true",
+                    help="skip the step with the rotary embedding fused in")
     ap.add_argument("--prefill-iters", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -264,6 +266,35 @@ def main():
     per_launch = [a.elapsed_time(b) for a, b in pairs]
     dec_avg_ms = float(np.mean(per_launch))
 
+    # (3) the same step with the rotary embedding fused in (q and the new k
+    # rotated at position ctx - 1 by an fp32 cos/sin table of 4096 x 128)
+    rope = None
+    if not args.no_rope and not args.separate:
+        table = torch.from_numpy(W.rope_table(wl.max_context_len, D)).to(dev)
+
+        def rope_step():
+            for l in range(L):
+                B.pkv_store_decode_attn_rope(t["k_new"][l], t["v_new"][l], slots, t["q"][l],
+                                             table, t["k_caches"][l], t["v_caches"][l], bt, ctx,
+                                             wl.scale, outs[l], max_context_len=wl.max_context_len,
+                                             workspace=ws, partition_tokens=P)
+
+        for _ in range(args.warmup):
+            rope_step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            rope_step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        rope_ms = a.elapsed_time(b) / args.steps
+        rope = {"launch": "pkv_store_decode_attn_rope", "ms_per_step": round(rope_ms, 4),
+                "tokens_per_s_per_layer": round(S * L / (rope_ms * 1e-3), 1),
+                "GB_s": round(L * (decode_bytes(wl) + store_bytes(wl)) / (rope_ms * 1e-3) / 1e9,
+                              2),
+                "step_time_vs_plain": round(rope_ms / ms_per_step, 4)}
+
     dbytes = decode_bytes(wl)
     sbytes = store_bytes(wl)
     kv_bytes_step = L * (dbytes + sbytes)
@@ -306,6 +337,8 @@ def main():
                      "algorithmic_bytes_per_launch": launch_bytes},
         "wall_s_timed": round(wall, 3),
     }
+    if rope is not None:
+        result["rope"] = rope
 
     # the oracle's host copies of two layers are taken before the 16 GiB of
     # pools are released for the other legs

@@ -180,6 +180,34 @@ int pkv_store_decode_attn(const void *k, const void *v, const int32_t *slot_mapp
                           int32_t partition_tokens, hipStream_t stream);
 
 /*
+ * pkv_store_decode_attn_rope -- pkv_store_decode_attn with the rotary
+ * position embedding fused in: each sequence's q and new-token k are rotated
+ * at the sequence's last position p = context_lens[s] - 1 before they are used
+ * (k also before it is stored), as a model does before attention ([NVE] §3.2:
+ * RoPE embeds position into Q and K, and efficient engines fuse it into the
+ * attention kernel; [LLM4] §21.2: RoPE rotates Q/K inside attention).  For
+ * every head row x and i < d/2, with c_i = cos_sin[p][i], s_i =
+ * cos_sin[p][d/2 + i]:
+ *   y[i]       = x[i] c_i - x[i + d/2] s_i
+ *   y[i + d/2] = x[i + d/2] c_i + x[i] s_i
+ * each product and sum rounded in fp32 (no fused multiply-add), y rounded to
+ * bf16 (nearest even).  The cached K before this step must already be
+ * rotated (at each token's own position).
+ *   cos_sin        fp32 [max_positions][head_dim], device, 16-byte aligned
+ *   max_positions  rows of the table; must be >= max_context_len (positions
+ *                  are clamped into the table; an empty context rotates its
+ *                  stored token at position 0)
+ * Every other argument as for pkv_store_decode_attn.
+ */
+int pkv_store_decode_attn_rope(const void *k, const void *v, const int32_t *slot_mapping,
+                               const void *q, const float *cos_sin, int32_t max_positions,
+                               pkv_cache cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                               float scale, void *out, void *workspace, size_t workspace_bytes,
+                               int32_t partition_tokens, hipStream_t stream);
+
+/*
  * pkv_prefill_attn -- chunked causal prefill over the paged cache.  Prompt p
  * has n_p = cu_new_lens[p+1] - cu_new_lens[p] new tokens whose K/V are
  * already stored after c_p = context_lens[p] - n_p cached ones.  New token i

@@ -9,10 +9,12 @@ workload generator used by the tests and the benchmark.
 from .binding import (PkvError, load, pkv_decode_attn, pkv_decode_partition_tokens,  # noqa: F401
                       pkv_decode_workspace_bytes, pkv_kv_bytes, pkv_last_error,
                       pkv_prefill_attn, pkv_status_string, pkv_store, pkv_store_decode_attn,
+                      pkv_store_decode_attn_rope,
                       pkv_store_fp8, pkv_decode_attn_fp8,
                       pkv_decode_partition_tokens_fp8)
 
-__all__ = ["pkv_store", "pkv_decode_attn", "pkv_store_decode_attn", "pkv_prefill_attn",
+__all__ = ["pkv_store", "pkv_decode_attn", "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
+           "pkv_prefill_attn",
            "pkv_store_fp8", "pkv_decode_attn_fp8", "pkv_decode_partition_tokens_fp8", "pkv_kv_bytes",
            "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_status_string",
            "pkv_last_error", "PkvError", "load"]

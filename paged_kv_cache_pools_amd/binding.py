@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_
 
 # every symbol include/pkv.h declares
 EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
-            "pkv_decode_attn", "pkv_store_decode_attn", "pkv_prefill_attn", "pkv_store_fp8",
+            "pkv_decode_attn", "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
+            "pkv_prefill_attn", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_kv_bytes",
             "pkv_status_string", "pkv_last_error"]
 
@@ -75,6 +76,10 @@ def load(path: str = LIB_PATH):
     lib.pkv_store_decode_attn.restype = ctypes.c_int
     lib.pkv_store_decode_attn.argtypes = [_P, _P, _P, _P, PkvCache, _P, _I32, _P, _I32, _I32, _I32,
                                           ctypes.c_float, _P, _P, _SZ, _I32, _P]
+    lib.pkv_store_decode_attn_rope.restype = ctypes.c_int
+    lib.pkv_store_decode_attn_rope.argtypes = [_P, _P, _P, _P, _P, _I32, PkvCache, _P, _I32, _P,
+                                               _I32, _I32, _I32, ctypes.c_float, _P, _P, _SZ,
+                                               _I32, _P]
     lib.pkv_store_fp8.restype = ctypes.c_int
     lib.pkv_store_fp8.argtypes = [_P, _P, _P, _I32, PkvCacheFp8, _P]
     lib.pkv_decode_attn_fp8.restype = ctypes.c_int
@@ -263,6 +268,49 @@ def pkv_store_decode_attn(k, v, slot_mapping, q, k_cache, v_cache, block_tables,
                                      float(scale), out.data_ptr(), workspace.data_ptr(),
                                      workspace.numel(), int(p), _stream(q, stream)),
            "pkv_store_decode_attn")
+    return out
+
+
+def pkv_store_decode_attn_rope(k, v, slot_mapping, q, cos_sin, k_cache, v_cache, block_tables,
+                               context_lens, scale, out, max_context_len: Optional[int] = None,
+                               workspace=None, partition_tokens: int = 0, stream=None):
+    """pkv_store_decode_attn with q and the new k rotated at each sequence's
+    last position by the fp32 table cos_sin [P][d] (cos, then sin)."""
+    import torch
+
+    lib = load()
+    cache = _cache(k_cache, v_cache)
+    for t, name, dt, nd in ((q, "q", torch.bfloat16, 3), (out, "out", torch.bfloat16, 3),
+                            (k, "k", torch.bfloat16, 3), (v, "v", torch.bfloat16, 3),
+                            (slot_mapping, "slot_mapping", torch.int32, 1),
+                            (cos_sin, "cos_sin", torch.float32, 2),
+                            (block_tables, "block_tables", torch.int32, 2),
+                            (context_lens, "context_lens", torch.int32, 1)):
+        _need(t, name, dt, nd)
+    s, hq, d = q.shape
+    if tuple(out.shape) != (s, hq, d) or d != cache.head_dim or cos_sin.shape[1] != d:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, cos_sin "
+                         f"{tuple(cos_sin.shape)}, head_dim {cache.head_dim}")
+    want = (s, cache.num_kv_heads, cache.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want or slot_mapping.shape[0] != s:
+        raise ValueError(f"k/v must be {want} and slot_mapping [{s}]")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables / context_lens do not match q's sequence count")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * cache.block_size
+    p = partition_tokens or pkv_decode_partition_tokens(s, cache.num_kv_heads, max_context_len)
+    need = pkv_decode_workspace_bytes(s, hq, d, max_context_len, p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib.pkv_store_decode_attn_rope(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                          q.data_ptr(), cos_sin.data_ptr(), cos_sin.shape[0],
+                                          cache, block_tables.data_ptr(), max_blocks,
+                                          context_lens.data_ptr(), s, int(max_context_len), hq,
+                                          float(scale), out.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), int(p), _stream(q, stream)),
+           "pkv_store_decode_attn_rope")
     return out
 
 

@@ -207,6 +207,46 @@ struct NewToken {
     int pos = -1;
 };
 
+// Rotary position embedding of a sequence's new token: the fp32 table row
+// (cos for elements i < d/2, then sin) of its position, or null for none.
+struct Rope {
+    const float *row = nullptr;
+};
+
+// Rotate this lane's 8 elements (8c .. 8c+7) of a head row by the table row:
+// elements i and i + d/2 form a pair, held by lanes c and c ^ (LPR/2) of the
+// same token row.  `pair` is what this lane hands its partner: the register
+// that holds, in the partner, the same head as `u` does here (u itself when
+// both lanes hold one head's row).  First half: x1 c - x2 s; second half:
+// x2 c + x1 s; each product and sum rounded in fp32 (no fused multiply-add),
+// the result rounded to bf16.  Every lane of the wave must call it (it
+// shuffles).
+template <int D>
+__device__ __forceinline__ uint4 rope8(const uint4 &u, const uint4 &pair, const float *row,
+                                       int c) {
+    constexpr int LPR = D / 8, HALF = LPR / 2;
+    const bool first = c < HALF;
+    const int i0 = 8 * (c % HALF);
+    const float4 c0 = reinterpret_cast<const float4 *>(row + i0)[0];
+    const float4 c1 = reinterpret_cast<const float4 *>(row + i0)[1];
+    const float4 s0 = reinterpret_cast<const float4 *>(row + D / 2 + i0)[0];
+    const float4 s1 = reinterpret_cast<const float4 *>(row + D / 2 + i0)[1];
+    const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const uint4 w = make_uint4(__shfl_xor(pair.x, HALF), __shfl_xor(pair.y, HALF),
+                               __shfl_xor(pair.z, HALF), __shfl_xor(pair.w, HALF));
+    float x[8], y[8], o[8];
+    unpack8(u, x);
+    unpack8(w, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float a = __fmul_rn(x[e], cs[e]);
+        const float b = __fmul_rn(y[e], sn[e]);
+        o[e] = first ? __fsub_rn(a, b) : __fadd_rn(a, b);
+    }
+    return pack8(o);
+}
+
 // One wavefront's attention over tokens [t_begin, t_end) (t_begin < t_end,
 // t_begin a multiple of 16) of sequence s for the G query heads of KV head
 // kvh.  On return every lane holds, for each head g of the group, the wave's
@@ -223,8 +263,8 @@ __device__ __forceinline__ void wave_attend(
     const uint16_t *__restrict__ q, const void *k_cache, const void *v_cache,
     const float *k_scale, const float *v_scale, const int32_t *__restrict__ bt,
     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, float scale_log2, int s,
-    int kvh, int t_begin, int t_end, const NewToken &nt, float (&acc)[G][8], float (&mg)[G],
-    float (&lg)[G]) {
+    int kvh, int t_begin, int t_end, const NewToken &nt, const Rope &rope, float (&acc)[G][8],
+    float (&mg)[G], float (&lg)[G]) {
     using Geo = DecodeGeom<D, G>;
     using Tile = typename std::conditional<FP8, uint2, uint4>::type;  // one lane's 8 elements
     constexpr uint32_t EB = FP8 ? 1 : 2;                               // bytes per element
@@ -245,6 +285,15 @@ __device__ __forceinline__ void wave_attend(
     for (int p = 0; p < G; ++p) {
         const int h = h0 + (my_head ^ p);
         qp[p] = reinterpret_cast<const uint4 *>(q + ((size_t)s * num_q_heads + h) * D)[c];
+    }
+    if (rope.row != nullptr) {  // uniform: q rotated at the sequence's last position
+        // the partner lane c ^ (LPR/2) ends with head my_head ^ (G/2), so its
+        // position p ^ (G/2) holds the head this lane's position p holds
+        uint4 qr[G];
+#pragma unroll
+        for (int p = 0; p < G; ++p) qr[p] = rope8<D>(qp[p], qp[p ^ (G / 2)], rope.row, c);
+#pragma unroll
+        for (int p = 0; p < G; ++p) qp[p] = qr[p];
     }
 
 #pragma unroll
@@ -311,6 +360,7 @@ __device__ __forceinline__ void wave_attend(
     if (nt.src_k != nullptr) {  // uniform: only the wave holding the last position
         kn = nt.src_k[c];
         vn = nt.src_v[c];
+        if (rope.row != nullptr) kn = rope8<D>(kn, kn, rope.row, c);  // rotated before it is stored
         if (nt.dst_k != nullptr && row == 0) {
             nt.dst_k[c] = kn;
             nt.dst_v[c] = vn;
@@ -502,12 +552,26 @@ __device__ __forceinline__ NewToken new_token(const uint16_t *k_new, const uint1
     return t;
 }
 
+// The rotation for a sequence whose context (the new token included) holds
+// ctx tokens: the table row of position ctx - 1, clamped into the table (a
+// position past it is a caller error).  Empty when the launch has no table.
+template <int D>
+__device__ __forceinline__ Rope rope_at(const float *table, int32_t positions, int ctx) {
+    Rope r;
+    if (table != nullptr) r.row = table + (size_t)min(max(ctx - 1, 0), positions - 1) * D;
+    return r;
+}
+
 // Write the new token's rows (fused store of a sequence with an empty context).
 template <int D>
-__device__ __forceinline__ void store_only(const NewToken &t) {
+__device__ __forceinline__ void store_only(const NewToken &t, const Rope &rope) {
     const int lane = threadIdx.x & 63;
+    const int c = lane % (D / 8);
+    if (t.src_k == nullptr) return;  // uniform
+    uint4 kk = t.src_k[c];
+    if (rope.row != nullptr) kk = rope8<D>(kk, kk, rope.row, c);  // all lanes shuffle
     if (t.dst_k != nullptr && lane < D / 8) {
-        t.dst_k[lane] = t.src_k[lane];
+        t.dst_k[lane] = kk;
         t.dst_v[lane] = t.src_v[lane];
     }
 }
@@ -524,7 +588,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     int32_t max_parts, float scale_log2, uint16_t *__restrict__ out, float *__restrict__ ws_out,
     float *__restrict__ ws_ml, const uint16_t *__restrict__ k_new,
     const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, uint16_t *k_store,
-    uint16_t *v_store) {
+    uint16_t *v_store, const float *__restrict__ rope_table, int32_t rope_positions) {
     constexpr int LPR = D / 8, TPL = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int part = blockIdx.x * (blockDim.x >> 6) + wave_id_uniform();
@@ -541,7 +605,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         if (part == 0) {
             write_zero_rows<D, G>(out, num_q_heads, s, kvh);
             store_only<D>(new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks,
-                                       num_kv_heads, s, kvh, ctx));
+                                       num_kv_heads, s, kvh, ctx),
+                          rope_at<D>(rope_table, rope_positions, ctx));
         }
         return;
     }
@@ -557,8 +622,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
     float acc[G][8], mg[G], lg[G];
     wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
-                           num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end, nt, acc,
-                           mg, lg);
+                           num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end, nt,
+                           rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
 
     if (nparts == 1) {
 #pragma unroll
@@ -600,7 +665,7 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, float scale_log2,
     uint16_t *__restrict__ out, const uint16_t *__restrict__ k_new,
     const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, uint16_t *k_store,
-    uint16_t *v_store) {
+    uint16_t *v_store, const float *__restrict__ rope_table, int32_t rope_positions) {
     constexpr int LPR = D / 8, TPL = 64 / LPR;
     extern __shared__ float smem[];  // [W][G][D] acc, then [W][G] m, then [W][G] l
     const int W = blockDim.x >> 6;
@@ -618,7 +683,8 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
         if (w == 0) {
             write_zero_rows<D, G>(out, num_q_heads, s, kvh);
             store_only<D>(new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks,
-                                       num_kv_heads, s, kvh, ctx));
+                                       num_kv_heads, s, kvh, ctx),
+                          rope_at<D>(rope_table, rope_positions, ctx));
         }
         return;  // uniform over the workgroup: no barrier is skipped
     }
@@ -637,7 +703,8 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
         float acc[G][8], mg[G], lg[G];
         wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
                                num_q_heads, num_kv_heads, scale_log2, s, kvh, b0 * kBlockTokens,
-                               min(b1 * kBlockTokens, ctx), nt, acc, mg, lg);
+                               min(b1 * kBlockTokens, ctx), nt,
+                               rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (g % TPL == row) {
@@ -734,7 +801,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                            a.max_context_len, a.num_blocks, a.num_q_heads, a.num_kv_heads,
                            scale_log2, (uint16_t *)a.out, (const uint16_t *)a.k_new,
                            (const uint16_t *)a.v_new, a.slots, (uint16_t *)a.k_store,
-                           (uint16_t *)a.v_store);
+                           (uint16_t *)a.v_store, a.rope_table, a.rope_positions);
         return hipGetLastError();
     }
     const int waves = a.max_parts >= 4 ? 4 : (a.max_parts >= 2 ? 2 : 1);
@@ -746,7 +813,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                        a.num_kv_heads, a.partition_tokens, a.max_parts, scale_log2,
                        (uint16_t *)a.out, a.ws_out, a.ws_ml, (const uint16_t *)a.k_new,
                        (const uint16_t *)a.v_new, a.slots, (uint16_t *)a.k_store,
-                       (uint16_t *)a.v_store);
+                       (uint16_t *)a.v_store, a.rope_table, a.rope_positions);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1) return e;
     const int rows = a.num_seqs * a.num_q_heads;

@@ -215,7 +215,8 @@ int decode_call(const void *q, const CacheDesc &cache, const int32_t *block_tabl
                 int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
                 void *workspace, size_t workspace_bytes, int32_t partition_tokens,
                 hipStream_t stream, const void *k_new, const void *v_new, const int32_t *slots,
-                const char *what) {
+                const char *what, const float *rope_table = nullptr,
+                int32_t rope_positions = 0) {
     int rc = check_cache(cache);
     if (rc) return rc;
     if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
@@ -276,6 +277,8 @@ int decode_call(const void *q, const CacheDesc &cache, const int32_t *block_tabl
     float *ws = static_cast<float *>(workspace);
     a.ws_out = need ? ws : nullptr;
     a.ws_ml = need ? ws + (size_t)num_seqs * num_q_heads * parts * cache.head_dim : nullptr;
+    a.rope_table = rope_table;
+    a.rope_positions = rope_positions;
     a.fp8 = cache.fp8;
     a.k_scale = cache.k_scale;
     a.v_scale = cache.v_scale;
@@ -318,6 +321,26 @@ int pkv_store_decode_attn(const void *k, const void *v, const int32_t *slot_mapp
                        num_seqs, max_context_len, num_q_heads, scale, out, workspace,
                        workspace_bytes, partition_tokens, stream, k, v, slot_mapping,
                        "pkv_store_decode_attn launch");
+}
+
+int pkv_store_decode_attn_rope(const void *k, const void *v, const int32_t *slot_mapping,
+                               const void *q, const float *cos_sin, int32_t max_positions,
+                               pkv_cache cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                               float scale, void *out, void *workspace, size_t workspace_bytes,
+                               int32_t partition_tokens, hipStream_t stream) {
+    if (num_seqs > 0 && (!k || !v || !slot_mapping || !cos_sin))
+        return fail(PKV_ERR_NULL, "k, v, slot_mapping or cos_sin is null");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(cos_sin))
+        return fail(PKV_ERR_ALIGN, "k / v / cos_sin must be 16-byte aligned");
+    if (num_seqs > 0 && (max_positions <= 0 || max_context_len > max_positions))
+        return fail(PKV_ERR_SHAPE, "max_positions %d must cover max_context_len %d",
+                    max_positions, max_context_len);
+    return decode_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                       workspace_bytes, partition_tokens, stream, k, v, slot_mapping,
+                       "pkv_store_decode_attn_rope launch", cos_sin, max_positions);
 }
 
 int pkv_decode_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,

@@ -49,6 +49,10 @@ struct DecodeArgs {
     // [num_blocks][num_kv_heads][16]
     bool fp8 = false;
     const float *k_scale = nullptr, *v_scale = nullptr;
+    // rotary embedding of q and the stored token at each sequence's last
+    // position: fp32 table [rope_positions][head_dim] (cos, then sin), or null
+    const float *rope_table = nullptr;
+    int32_t rope_positions = 0;
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

@@ -157,6 +157,18 @@ def test_store_decode_validation(lib):
     assert B.pkv_last_error() != ""
 
 
+def test_store_decode_rope_validation(lib):
+    sd = lambda cs=FAKE, mp=64, s=2, k=FAKE: lib.pkv_store_decode_attn_rope(
+        k, FAKE, FAKE, FAKE, cs, mp, cache(), FAKE, 3, FAKE, s, 37, 4, ctypes.c_float(0.125),
+        FAKE, FAKE, 1 << 30, 0, None)
+    assert sd(s=0, cs=0, mp=0) == 0         # empty batch: nothing launched
+    assert sd(cs=0) == 1 and sd(k=0) == 1
+    assert sd(cs=FAKE + 4) == 4
+    assert sd(mp=0) == 2 and sd(mp=36) == 2  # the table must cover max_context_len 37
+    assert sd(mp=37, s=-1) == 2              # past the table check, the decode checks apply
+    assert B.pkv_last_error() != ""
+
+
 def test_fp8_validation(lib):
     c8 = lambda ks=FAKE, vs=FAKE, d=64: B.PkvCacheFp8(FAKE, FAKE, ks, vs, 16, 2, d, 16)
     st = lambda c, n=4: lib.pkv_store_fp8(FAKE, FAKE, FAKE, n, c, None)

@@ -397,6 +397,139 @@ def test_fused_store_decode_mistral_full_size():
 
 
 # ---------------------------------------------------------------------------
+# rotary position embedding fused into store + decode: q and the new k are
+# rotated at position ctx - 1 (the oracle rotates them on the host, then stores
+# and attends with the rotated rows)
+# ---------------------------------------------------------------------------
+
+def run_rope(c, table, partition_tokens=0, slots=None):
+    d = c.dev
+    wl = c.wl
+    slot_t = d["slot_mapping"] if slots is None else torch.from_numpy(slots).cuda()
+    out = torch.empty_like(d["q"])
+    B.pkv_store_decode_attn_rope(d["k_new"], d["v_new"], slot_t, d["q"],
+                                 torch.from_numpy(table).cuda(), d["k_caches"][0],
+                                 d["v_caches"][0], d["block_tables"], d["context_lens"], wl.scale,
+                                 out, max_context_len=wl.max_context_len,
+                                 partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_rope_step(c, table, slots=None):
+    """Host reference: rotate q and the new k at max(ctx - 1, 0), store the
+    rotated k (and v as it is), attend with the rotated q."""
+    wl, h = c.wl, c.h
+    pos = np.maximum(wl.context_lens.astype(np.int32) - 1, 0).astype(np.int32)
+    q_rot = orc().rope(h["q"], pos, table)
+    k_rot = orc().rope(h["k_new"], pos, table)
+    orc().store(k_rot, h["v_new"], wl.slot_mapping if slots is None else slots, h["kc"], h["vc"])
+    return orc().decode(q_rot, h["kc"], h["vc"], wl.block_tables, wl.context_lens, wl.scale)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 4, 8])
+@pytest.mark.parametrize("part", [16, 64, 0, -1, -3])
+def test_rope_store_decode(d, g, part):
+    lens = [1, 15, 16, 17, 63, 64, 65, 129, 300]
+    wl = W.make_decode(f"rope_d{d}_g{g}", lens, 2 * g, 2, d, 500 + d + g, spare_blocks=2)
+    table = W.rope_table(wl.max_context_len + 37, d)
+    c = Case(wl)
+    say(f"[gpu] rope store+decode d={d} G={g} P={part or 'auto'}")
+    out = run_rope(c, table, part)
+    ref = oracle_rope_step(c, table)
+    assert np.array_equal(bits(c.dev["k_caches"][0]), c.h["kc"]), "rotated K store differs"
+    assert np.array_equal(bits(c.dev["v_caches"][0]), c.h["vc"]), "V store differs"
+    compare(out, ref, f"rope store+decode d{d} g{g} P{part}")
+
+
+@pytest.mark.parametrize("part", [0, 32])
+def test_rope_identity_table_is_plain_fused(part):
+    """cos 1, sin 0 at every position: the rotation is exact, so the step is
+    bit-identical to pkv_store_decode_attn."""
+    wl = W.make_decode("rope_identity", [5, 16, 77, 200], 16, 4, 128, 71, spare_blocks=1)
+    table = np.zeros((wl.max_context_len, 128), np.float32)
+    table[:, :64] = 1.0
+    c = Case(wl)
+    kc2 = c.dev["k_caches"][0].clone()
+    vc2 = c.dev["v_caches"][0].clone()
+    say(f"[gpu] rope identity table P={part or 'auto'}")
+    out = run_rope(c, table, part)
+    d = c.dev
+    plain = torch.empty_like(d["q"])
+    B.pkv_store_decode_attn(d["k_new"], d["v_new"], d["slot_mapping"], d["q"], kc2, vc2,
+                            d["block_tables"], d["context_lens"], wl.scale, plain,
+                            max_context_len=wl.max_context_len, partition_tokens=part)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc2), bits(d["k_caches"][0]))
+    assert np.array_equal(bits(vc2), bits(d["v_caches"][0]))
+    assert np.array_equal(bits(plain), bits(out))
+
+
+def test_rope_table_exactly_covers_context():
+    """max_positions == max_context_len: the last row is the one used."""
+    wl = W.make_decode("rope_exact_table", [48, 3, 48], 8, 2, 128, 72)
+    table = W.rope_table(wl.max_context_len, 128)
+    c = Case(wl)
+    say("[gpu] rope table of exactly max_context_len rows")
+    out = run_rope(c, table)
+    ref = oracle_rope_step(c, table)
+    assert np.array_equal(bits(c.dev["k_caches"][0]), c.h["kc"])
+    compare(out, ref, "rope exact table")
+
+
+def test_rope_skips_and_empty_context():
+    """slot -1 stores nothing (the cached row at ctx - 1 is used as it is); a
+    sequence with no context stores its k rotated at position 0 and outputs 0."""
+    wl = W.make_decode("rope_edges", [20, 33, 0, 40], 8, 2, 64, 73, spare_blocks=1)
+    spare = sorted(set(range(wl.num_blocks)) - set(wl.used_blocks().tolist()))
+    slots = wl.slot_mapping.copy()
+    slots[1] = -1
+    slots[2] = spare[0] * 16 + 5
+    table = W.rope_table(64, 64)
+    c = Case(wl)
+    # sequence 1 stores nothing: its last position must already hold a token
+    slot = int(wl.slot_mapping[1])
+    for cache, host, src in ((c.dev["k_caches"][0], c.h["kc"], c.dev["k_new"]),
+                             (c.dev["v_caches"][0], c.h["vc"], c.dev["v_new"])):
+        row = (src[1] * 0.5).to(torch.bfloat16)
+        cache[slot // 16, :, slot % 16] = row
+        host[slot // 16, :, slot % 16] = bits(row)
+    say("[gpu] rope edges (skip, empty context)")
+    out = run_rope(c, table, 0, slots=slots)
+    ref = oracle_rope_step(c, table, slots=slots)
+    assert np.array_equal(bits(c.dev["k_caches"][0]), c.h["kc"])
+    assert np.all(to_f64(out)[2] == 0.0)
+    compare(out, ref, "rope edges")
+
+
+def test_rope_mistral_full_size():
+    """The benchmark's shape (32 x 4096 GQA, single pass) with the rotation
+    fused; the oracle checks sampled sequences."""
+    wl = W.mistral_gqa(num_layers=1)
+    seqs = [0, 17, 31]
+    table = W.rope_table(wl.max_context_len, wl.head_dim)
+    say(f"[gpu] rope store+decode full size, oracle on seqs {seqs}")
+    t = W.make_tensors(wl, device="cuda", layers=1, nan_fill=True)
+    h = compact_for_oracle(wl, t, seqs)
+    out = torch.empty_like(t["q"])
+    B.pkv_store_decode_attn_rope(t["k_new"], t["v_new"], t["slot_mapping"], t["q"],
+                                 torch.from_numpy(table).cuda(), t["k_caches"][0],
+                                 t["v_caches"][0], t["block_tables"], t["context_lens"], wl.scale,
+                                 out, max_context_len=wl.max_context_len)
+    torch.cuda.synchronize()
+    pos = (h["ctx"] - 1).astype(np.int32)
+    k_rot = orc().rope(h["k_new"], pos, table)
+    orc().store(k_rot, h["v_new"], h["slots"], h["kc"], h["vc"])
+    ref = orc().decode(orc().rope(h["q"], pos, table), h["kc"], h["vc"], h["bt"], h["ctx"],
+                       wl.scale)
+    compare(out[list(seqs)], ref, "rope store+decode full size")
+    for i, s_ in enumerate(seqs):
+        slot = int(wl.slot_mapping[s_])
+        assert np.array_equal(bits(t["k_caches"][0][slot // 16, :, slot % 16]), k_rot[i]), s_
+
+
+# ---------------------------------------------------------------------------
 # FP8 (OCP E4M3, one fp32 scale per token and KV head) cache.  Dequantized
 # values (code x scale) are not bf16 values, so even a one-token context
 # rounds on output, and single-key rows reach magnitudes near 5: the
