@@ -58,6 +58,8 @@ def _bind(lib):
                                 _I32, ctypes.c_float, _P, ctypes.c_int]
     lib.pko_default_threads.restype = ctypes.c_int
     lib.pko_default_threads.argtypes = []
+    lib.pko_copy_blocks.restype = ctypes.c_int
+    lib.pko_copy_blocks.argtypes = [_P, _I32, ctypes.c_int64, _I32, _P, _I32]
     lib.pko_rope.restype = ctypes.c_int
     lib.pko_rope.argtypes = [_P, _P, _I32, _I32, _I32, _P, _I32, _P]
     lib.pko_fp8_decode.restype = ctypes.c_double
@@ -125,6 +127,25 @@ class Oracle:
         if rc != OK:
             raise OracleError(rc, "decode")
         return out
+
+    # -- block copy (copy-on-write) ---------------------------------------------------
+    def copy_blocks(self, pools, copies):
+        """In place: for each (src, dst) row of ``copies`` ([n][2] int32), block
+        dst of every pool (contiguous numpy arrays whose first axis is the
+        block) becomes a byte copy of block src."""
+        pairs = np.ascontiguousarray(np.asarray(copies, dtype=np.int32).reshape(-1, 2))
+        if not pools:
+            return
+        nb = pools[0].shape[0]
+        bb = pools[0].nbytes // max(nb, 1)
+        for p in pools:
+            _check_inplace(p, p.dtype)
+            assert p.shape[0] == nb and p.nbytes == nb * bb
+        ptrs = (ctypes.c_void_p * len(pools))(*[p.ctypes.data for p in pools])
+        rc = self.lib.pko_copy_blocks(ctypes.cast(ptrs, ctypes.c_void_p), len(pools), bb, nb,
+                                      _ptr(pairs), pairs.shape[0])
+        if rc != OK:
+            raise OracleError(rc, "copy_blocks")
 
     # -- rotary position embedding ------------------------------------------------------
     def rope(self, x, positions, cos_sin):

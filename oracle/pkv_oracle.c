@@ -686,3 +686,50 @@ int pko_rope(const uint16_t *x, const int32_t *positions, int32_t num_rows, int3
     }
     return PKO_OK;
 }
+
+/*
+ * Copy whole physical blocks: for each pair (src, dst) of copies [num_pairs][2]
+ * and each of the num_pools pools ([num_blocks][block_bytes] bytes each),
+ * block dst becomes a byte copy of block src.  This is the copy that
+ * copy-on-write needs when a sequence writes into a block it shares ("Nano-vLLM
+ * engine deep-dive", section 2.2; "LLM basics primer" part 4, section 17.7).
+ * A pair with an id outside [0, num_blocks), or with src == dst, copies
+ * nothing.  Two pairs with one dst, or a dst that is also some pair's src,
+ * make the result depend on order: refused with PKO_ERR_DUPLICATE.
+ */
+int pko_copy_blocks(uint8_t *const *pools, int32_t num_pools, int64_t block_bytes,
+                    int32_t num_blocks, const int32_t *copies, int32_t num_pairs)
+{
+    if (num_pools < 0 || block_bytes < 0 || num_blocks < 0 || num_pairs < 0)
+        return PKO_ERR_ARG;
+    if (num_pairs == 0 || num_pools == 0)
+        return PKO_OK;
+    if (!pools || !copies)
+        return PKO_ERR_ARG;
+    unsigned char *role = calloc((size_t)(num_blocks > 0 ? num_blocks : 1), 1);
+    if (!role)
+        return PKO_ERR_ALLOC;
+    /* role bit 1: some pair's src; bit 2: some pair's dst */
+    int rc = PKO_OK;
+    for (int32_t i = 0; i < num_pairs && rc == PKO_OK; ++i) {
+        int32_t src = copies[2 * i], dst = copies[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst)
+            continue;
+        if ((role[dst] & 2) || (role[dst] & 1) || (role[src] & 2))
+            rc = PKO_ERR_DUPLICATE;
+        role[src] |= 1;
+        role[dst] |= 2;
+    }
+    free(role);
+    if (rc != PKO_OK)
+        return rc;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        int32_t src = copies[2 * i], dst = copies[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst)
+            continue;
+        for (int32_t p = 0; p < num_pools; ++p)
+            memcpy(pools[p] + dst * block_bytes, pools[p] + src * block_bytes,
+                   (size_t)block_bytes);
+    }
+    return PKO_OK;
+}

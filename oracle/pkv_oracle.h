@@ -56,6 +56,8 @@ int pko_store_fp8(const uint16_t *k, const uint16_t *v, const int32_t *slot_mapp
                   float *v_scales, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                   int32_t block_size);
 /* Rotary position embedding of bf16 rows (see pkv_oracle.c for the formula). */
+int pko_copy_blocks(uint8_t *const *pools, int32_t num_pools, int64_t block_bytes,
+                    int32_t num_blocks, const int32_t *copies, int32_t num_pairs);
 int pko_rope(const uint16_t *x, const int32_t *positions, int32_t num_rows, int32_t heads,
              int32_t head_dim, const float *cos_sin, int32_t max_positions, uint16_t *out);
 

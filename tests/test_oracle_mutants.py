@@ -56,6 +56,13 @@ MUTANTS = [
      "float x2 = bf16_bits_to_float(xr[(i + 1) % head_dim]);"),
     ("rope_cos_sin_swapped", "const float *sn = c + half;", "const float *sn = c; c = c + half;"),
     ("rope_truncates", "u += 0x7fffu + lsb;", "u += 0u * lsb;"),
+    # block copy
+    ("copy_direction_swapped",
+     "memcpy(pools[p] + dst * block_bytes, pools[p] + src * block_bytes,",
+     "memcpy(pools[p] + src * block_bytes, pools[p] + dst * block_bytes,"),
+    ("copy_first_pool_only", "for (int32_t p = 0; p < num_pools; ++p)\n            memcpy",
+     "for (int32_t p = 0; p < 1; ++p)\n            memcpy"),
+    ("copy_order_unchecked", "rc = PKO_ERR_DUPLICATE;", "(void)0;"),
 ]
 
 
