@@ -76,7 +76,9 @@ typedef enum {
     PKV_ERR_UNSUPPORTED = 3, /* head_dim, block_size or group size not supported */
     PKV_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
     PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
-    PKV_ERR_HIP = 6          /* the HIP runtime reported an error */
+    PKV_ERR_HIP = 6,         /* the HIP runtime reported an error */
+    PKV_ERR_CAPACITY = 7,    /* the block pool has too few free blocks */
+    PKV_ERR_SEQUENCE = 8     /* a sequence id is unknown, or already taken */
 } pkv_status;
 
 /* One layer's K and V pools.  k and v are device pointers to bf16 arrays of

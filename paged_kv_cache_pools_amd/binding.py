@@ -16,14 +16,20 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 
 PKV_OK = 0
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
-                4: "PKV_ERR_ALIGN", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_HIP"}
+                4: "PKV_ERR_ALIGN", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_HIP",
+                7: "PKV_ERR_CAPACITY", 8: "PKV_ERR_SEQUENCE"}
+PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGN = 1, 2, 3, 4
+PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_CAPACITY, PKV_ERR_SEQUENCE = 5, 6, 7, 8
 
-# every symbol include/pkv.h declares
+# every symbol include/pkv.h and include/pkv_pool.h declare
 EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
             "pkv_decode_attn", "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
             "pkv_prefill_attn", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_kv_bytes",
-            "pkv_status_string", "pkv_last_error"]
+            "pkv_status_string", "pkv_last_error",
+            "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
+            "pkv_pool_fork", "pkv_pool_free_seq", "pkv_pool_block_tables", "pkv_pool_num_free",
+            "pkv_pool_refcount", "pkv_pool_seq_len", "pkv_copy_blocks"]
 
 
 class PkvError(RuntimeError):
@@ -88,6 +94,28 @@ def load(path: str = LIB_PATH):
     lib.pkv_prefill_attn.restype = ctypes.c_int
     lib.pkv_prefill_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                      ctypes.c_float, _P, _P]
+    lib.pkv_pool_create.restype = ctypes.c_int
+    lib.pkv_pool_create.argtypes = [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pkv_pool_destroy.restype = None
+    lib.pkv_pool_destroy.argtypes = [_P]
+    lib.pkv_pool_add_seq.restype = ctypes.c_int
+    lib.pkv_pool_add_seq.argtypes = [_P, _I64, _P, _I32, _P, _P]
+    lib.pkv_pool_append.restype = ctypes.c_int
+    lib.pkv_pool_append.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P]
+    lib.pkv_pool_fork.restype = ctypes.c_int
+    lib.pkv_pool_fork.argtypes = [_P, _I64, _I64]
+    lib.pkv_pool_free_seq.restype = ctypes.c_int
+    lib.pkv_pool_free_seq.argtypes = [_P, _I64]
+    lib.pkv_pool_block_tables.restype = ctypes.c_int
+    lib.pkv_pool_block_tables.argtypes = [_P, _P, _I32, _I32, _P, _P]
+    lib.pkv_pool_num_free.restype = _I32
+    lib.pkv_pool_num_free.argtypes = [_P]
+    lib.pkv_pool_refcount.restype = _I32
+    lib.pkv_pool_refcount.argtypes = [_P, _I32]
+    lib.pkv_pool_seq_len.restype = _I32
+    lib.pkv_pool_seq_len.argtypes = [_P, _I64]
+    lib.pkv_copy_blocks.restype = ctypes.c_int
+    lib.pkv_copy_blocks.argtypes = [_P, _I32, _SZ, _I32, _P, _I32, _P]
     lib.pkv_kv_bytes.restype = ctypes.c_uint64
     lib.pkv_kv_bytes.argtypes = [_I32, _I32, _I32, _I64, _I32]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -403,3 +431,131 @@ def pkv_status_string(status: int) -> str:
 
 def pkv_last_error() -> str:
     return load().pkv_last_error().decode()
+
+
+# ---------------------------------------------------------------------------
+# block pool (host) and block copy (device)
+# ---------------------------------------------------------------------------
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class BlockPool:
+    """The C++ block pool (include/pkv_pool.h): marshalling only.
+
+    Host-side numpy int32/int64 arrays in and out; every rule lives in the
+    library."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, prefix_caching: bool = False):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        _check(self._lib.pkv_pool_create(num_blocks, block_size, int(bool(prefix_caching)),
+                                         ctypes.byref(h)), "pkv_pool_create")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_seq(self, seq_id: int, tokens):
+        """Admit a prompt -> (slots int32 [n], -1 where cached; num_cached)."""
+        import numpy as np
+
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        slots = np.empty(tok.shape[0], np.int32)
+        cached = ctypes.c_int32(0)
+        _check(self._lib.pkv_pool_add_seq(self._h, int(seq_id), _np_ptr(tok), tok.shape[0],
+                                          _np_ptr(slots), ctypes.byref(cached)),
+               "pkv_pool_add_seq")
+        return slots, cached.value
+
+    def append(self, seq_ids, tokens):
+        """One token per sequence -> (slots int32 [n], copies int32 [k][2]).
+        On failure the PkvError carries .num_done."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        if ids.shape != tok.shape:
+            raise ValueError("seq_ids and tokens differ in length")
+        n = ids.shape[0]
+        slots = np.empty(n, np.int32)
+        copies = np.empty((max(n, 1), 2), np.int32)
+        ncopies, done = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = self._lib.pkv_pool_append(self._h, _np_ptr(ids), _np_ptr(tok), n, _np_ptr(slots),
+                                       _np_ptr(copies), ctypes.byref(ncopies), ctypes.byref(done))
+        if st != PKV_OK:
+            err = PkvError(st, "pkv_pool_append", self._lib.pkv_last_error().decode())
+            err.num_done = done.value
+            err.slots = slots[:done.value].copy()
+            err.copies = copies[:ncopies.value].copy()
+            raise err
+        return slots, copies[:ncopies.value].copy()
+
+    def fork(self, parent_id: int, child_id: int):
+        _check(self._lib.pkv_pool_fork(self._h, int(parent_id), int(child_id)), "pkv_pool_fork")
+
+    def free_seq(self, seq_id: int):
+        _check(self._lib.pkv_pool_free_seq(self._h, int(seq_id)), "pkv_pool_free_seq")
+
+    def block_tables(self, seq_ids, max_blocks_per_seq: int):
+        """-> (block_tables int32 [n][max_blocks_per_seq] padded with -1,
+        context_lens int32 [n])."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.shape[0]
+        bt = np.empty((n, max_blocks_per_seq), np.int32)
+        ctx = np.empty(n, np.int32)
+        _check(self._lib.pkv_pool_block_tables(self._h, _np_ptr(ids), n, max_blocks_per_seq,
+                                               _np_ptr(bt), _np_ptr(ctx)), "pkv_pool_block_tables")
+        return bt, ctx
+
+    def block_table(self, seq_id: int):
+        n = self.seq_len(seq_id)
+        if n < 0:
+            raise PkvError(PKV_ERR_SEQUENCE, "block_table", f"unknown sequence {seq_id}")
+        bt, _ = self.block_tables([seq_id], max(1, -(-n // self.block_size)))
+        return [int(b) for b in bt[0] if b >= 0]
+
+    def num_free(self) -> int:
+        return self._lib.pkv_pool_num_free(self._h)
+
+    def refcount(self, block: int) -> int:
+        return self._lib.pkv_pool_refcount(self._h, block)
+
+    def seq_len(self, seq_id: int) -> int:
+        return self._lib.pkv_pool_seq_len(self._h, int(seq_id))
+
+
+def pkv_copy_blocks(pools, copies, stream=None):
+    """Block dst of every pool becomes a copy of block src, for each (src, dst)
+    row of ``copies`` (int32 [k][2] on the device).  ``pools``: device tensors
+    whose first axis is the block (a layer's K or V cache, FP8 codes or
+    scales), all with the same bytes per block."""
+    import torch
+
+    lib = load()
+    if len(pools) == 0 or copies.numel() == 0:
+        return
+    _need(copies, "copies", torch.int32, 2)
+    if copies.shape[1] != 2:
+        raise ValueError("copies must be [k][2]")
+    nb = pools[0].shape[0]
+    bb = pools[0].numel() * pools[0].element_size() // max(nb, 1)
+    for i, p in enumerate(pools):
+        if not isinstance(p, torch.Tensor) or not p.is_cuda or not p.is_contiguous():
+            raise TypeError(f"pools[{i}] must be a contiguous device tensor")
+        if p.shape[0] != nb or p.numel() * p.element_size() != nb * bb:
+            raise ValueError(f"pools[{i}]: every pool must have {nb} blocks of {bb} bytes")
+    ptrs = (ctypes.c_void_p * len(pools))(*[p.data_ptr() for p in pools])
+    _check(lib.pkv_copy_blocks(ctypes.cast(ptrs, ctypes.c_void_p), len(pools), bb, nb,
+                               copies.data_ptr(), copies.shape[0], _stream(copies, stream)),
+           "pkv_copy_blocks")

@@ -4,6 +4,7 @@
 // geometry, workspace sizing and error strings.  The arithmetic lives in the
 // kernels (store.hip, decode.hip, prefill.hip).
 #include "pkv.h"
+#include "pkv_pool.h"
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -11,7 +12,7 @@
 
 #include "pkv_internal.h"
 
-namespace {
+namespace pkv {
 
 thread_local char g_last_error[512] = "";
 
@@ -27,6 +28,14 @@ int ok() {
     g_last_error[0] = '\0';
     return PKV_OK;
 }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+using pkv::g_last_error;
+using pkv::ok;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -127,6 +136,30 @@ int32_t fused_waves_for(int64_t units, int32_t max_context_len, int64_t kTargetW
 
 extern "C" {
 
+int pkv_copy_blocks(void *const *pools, int32_t num_pools, size_t block_bytes, int32_t num_blocks,
+                    const int32_t *copies, int32_t num_copies, hipStream_t stream) {
+    if (num_pools < 0 || num_blocks < 0 || num_copies < 0)
+        return fail(PKV_ERR_SHAPE, "num_pools %d, num_blocks %d, num_copies %d", num_pools,
+                    num_blocks, num_copies);
+    if (num_pools == 0 || num_copies == 0) return ok();
+    if (!pools || !copies) return fail(PKV_ERR_NULL, "pools or copies is null");
+    if (block_bytes == 0 || block_bytes % 16 != 0)
+        return fail(PKV_ERR_SHAPE, "block_bytes %zu: a positive multiple of 16", block_bytes);
+    if (!aligned16(copies)) return fail(PKV_ERR_ALIGN, "copies must be 16-byte aligned");
+    for (int32_t i = 0; i < num_pools; ++i) {
+        if (!pools[i]) return fail(PKV_ERR_NULL, "pools[%d] is null", i);
+        if (!aligned16(pools[i])) return fail(PKV_ERR_ALIGN, "pools[%d] is not 16-byte aligned", i);
+    }
+    const size_t chunks = (block_bytes + 4095) / 4096;  // the finest chunking a launch uses
+    if (chunks * (size_t)num_copies > (size_t)INT32_MAX)
+        return fail(PKV_ERR_SHAPE, "%d copies of %zu-byte blocks: too many workgroups", num_copies,
+                    block_bytes);
+    pkv::CopyArgs a{pools, num_pools, block_bytes, num_blocks, copies, num_copies, stream};
+    const hipError_t e = pkv::launch_copy_blocks(a);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_copy_blocks launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char *pkv_status_string(int status) {
     switch (status) {
         case PKV_OK: return "PKV_OK";
@@ -136,6 +169,8 @@ const char *pkv_status_string(int status) {
         case PKV_ERR_ALIGN: return "PKV_ERR_ALIGN: a device pointer is not 16-byte aligned";
         case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE: workspace missing or too small";
         case PKV_ERR_HIP: return "PKV_ERR_HIP: the HIP runtime reported an error";
+        case PKV_ERR_CAPACITY: return "PKV_ERR_CAPACITY: not enough free blocks in the pool";
+        case PKV_ERR_SEQUENCE: return "PKV_ERR_SEQUENCE: unknown or duplicate sequence id";
         default: return "unknown pkv status";
     }
 }

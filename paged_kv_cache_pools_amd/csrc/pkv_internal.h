@@ -7,6 +7,12 @@
 
 namespace pkv {
 
+// Error reporting shared by every exported entry: record a one-line,
+// thread-local description for pkv_last_error() and return the status.
+extern thread_local char g_last_error[512];
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int ok();
+
 struct StoreArgs {
     const void *k, *v;
     const int32_t *slots;
@@ -68,5 +74,18 @@ struct PrefillArgs {
     void *out;
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// Whole-block copies (copy.hip).
+constexpr int kMaxCopyPools = 64;  // pool pointers per launch (kernel arguments)
+struct CopyArgs {
+    void *const *pools;  // host array of num_pools device pointers
+    int32_t num_pools;
+    size_t block_bytes;
+    int32_t num_blocks;
+    const int32_t *copies;  // device [num_copies][2]
+    int32_t num_copies;
+    hipStream_t stream;
+};
+hipError_t launch_copy_blocks(const CopyArgs &a);
 
 }  // namespace pkv

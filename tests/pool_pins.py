@@ -39,7 +39,8 @@ class Tracker:
         return self.intern[key]
 
     def snapshot(self):
-        return copy.deepcopy((self.pool.__dict__, self.stamp, self.ids))
+        state = self.pool.state() if hasattr(self.pool, "state") else self.pool.__dict__
+        return copy.deepcopy((state, self.stamp, self.ids))
 
     def add(self, sid, tokens):
         slots, cached = self.pool.add_seq(sid, tokens)
