@@ -53,6 +53,8 @@ def parse():
                     help="skip the FP8-cache leg of the decode workload")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the Qwen-style MHA and continuous-batch decode workloads")
+    ap.add_argument("--no-mixed", action="store_true",
+                    help="skip the mixed decode + prefill iteration")
     ap.add_argument("--no-pool", action="store_true",
                     help="skip the block-pool bookkeeping and block-copy leg")
     ap.add_argument("--no-rope", action="store_true",
@@ -373,6 +375,9 @@ def main():
     if not args.no_other:
         result["other_decode_workloads"] = [bench_other(torch, B, W, dev, name)
                                             for name in ("qwen_mha", "cont_batch")]
+    if not args.no_mixed:
+        result["mixed_step"] = [bench_mixed(torch, B, W, dev, name)
+                                for name in ("mixed_step", "mixed_tail")]
     if not args.no_pool:
         result["block_pool"] = bench_pool(torch, B, W, dev)
     if host is not None:
@@ -595,6 +600,100 @@ def bench_pool(torch, B, W, dev, steps=64):
     del pools
     torch.cuda.empty_cache()
     return {"host": host, "copy": device}
+
+
+def bench_mixed(torch, B, W, dev, name="mixed_step", iters=20):
+    """One continuous-batching iteration in one launch (pkv_mixed_attn), on
+    the 32 x 4096 GQA decode batch plus prompt chunks: "mixed_step", 4 chunks
+    of 496 new tokens after 0 / 512 / 1536 / 3072 cached ones (2016 new
+    tokens), or "mixed_tail", one 64-token chunk after 4032 cached ones.
+    Timed against the same work as two launches (pkv_decode_attn on the
+    decode sequences, then pkv_prefill_attn on the chunks), and without the
+    key-range split of prefill units.  Two layer pools alternate.  The bound
+    for one launch that overlaps both kinds of work perfectly is
+    max(decode bytes / HBM peak, prefill flops / bf16 MFMA peak)."""
+    wl = W.CONFIGS[name]()
+    nd = 32
+    t = W.make_tensors(wl, device=dev, layers=2, nan_fill=False)
+    for l in range(2):
+        B.pkv_store(t["k_new"], t["v_new"], t["slot_mapping"], t["k_caches"][l], t["v_caches"][l])
+    out = torch.empty_like(t["q"])
+    mnl = int(wl.new_lens[nd:].max())
+    mcl = int(wl.context_lens.max())
+    q_dec, out_dec = t["q"][:nd], out[:nd]
+    bt_dec, ctx_dec = t["block_tables"][:nd].contiguous(), t["context_lens"][:nd].contiguous()
+    q_pf, out_pf = t["q"][nd:], out[nd:]
+    bt_pf, ctx_pf = t["block_tables"][nd:].contiguous(), t["context_lens"][nd:].contiguous()
+    cu_pf = (t["cu_new_lens"][nd:] - nd).contiguous()
+    P = B.pkv_decode_partition_tokens(nd, wl.num_kv_heads, 4096)
+    ws = torch.empty(max(16, B.pkv_decode_workspace_bytes(nd, wl.num_q_heads, wl.head_dim, 4096, P)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    ws_bytes = B.pkv_mixed_workspace_bytes(wl.num_seqs, nd, mnl, mcl, wl.num_q_heads,
+                                           wl.num_kv_heads, wl.head_dim)
+    ws_mixed = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def mixed(l):
+        B.pkv_mixed_attn(t["q"], t["k_caches"][l], t["v_caches"][l], t["block_tables"],
+                         t["cu_new_lens"], t["context_lens"], nd, wl.scale, out,
+                         max_new_len=mnl, max_context_len=mcl, workspace=ws_mixed)
+
+    def mixed_whole(l):
+        B.pkv_mixed_attn(t["q"], t["k_caches"][l], t["v_caches"][l], t["block_tables"],
+                         t["cu_new_lens"], t["context_lens"], nd, wl.scale, out,
+                         max_new_len=mnl, max_context_len=mcl, split=False)
+
+    def separate(l):
+        B.pkv_decode_attn(q_dec, t["k_caches"][l], t["v_caches"][l], bt_dec, ctx_dec, wl.scale,
+                          out_dec, max_context_len=4096, workspace=ws, partition_tokens=P)
+        B.pkv_prefill_attn(q_pf, t["k_caches"][l], t["v_caches"][l], bt_pf, cu_pf, ctx_pf,
+                           wl.scale, out_pf, max_new_len=mnl, max_context_len=mcl)
+
+    def timed(fn):
+        for l in (0, 1, 0, 1):
+            fn(l)
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(iters):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(i & 1)
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return launch_stats([a.elapsed_time(b) for a, b in evs])
+
+    for fn in (mixed, mixed_whole, separate):  # every variant warm before any is timed
+        timed(fn)
+    mixed_ms, mixed_stats = timed(mixed)
+    whole_ms, _ = timed(mixed_whole)
+    sep_ms, sep_stats = timed(separate)
+    S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
+    dec_bytes = (int(wl.context_lens[:nd].sum()) * 2 * Hkv * D * 2 + 2 * nd * Hq * D * 2
+                 + 4 * int((-(-wl.context_lens[:nd] // 16)).sum()) + 4 * nd)
+    pf_flops = 0.0
+    for p in range(nd, S):
+        c, n = int(wl.context_lens[p] - wl.new_lens[p]), int(wl.new_lens[p])
+        pf_flops += 4.0 * D * Hq * (n * c + n * (n + 1) / 2)
+    t_hbm = dec_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = pf_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    bound_ms = max(t_hbm, t_mfma) * 1e3
+    del t
+    torch.cuda.empty_cache()
+    what = ("4 prefill chunks x 496 new (cached 0/512/1536/3072)" if name == "mixed_step"
+            else "1 prefill chunk of 64 new after 4032 cached")
+    return {"workload": f"{name}: 32 decode seqs x 4096 + {what}, 32q/8kv, d 128",
+            "mixed_us": round(mixed_ms * 1e3, 2), "separate_us": round(sep_ms * 1e3, 2),
+            "mixed_unsplit_us": round(whole_ms * 1e3, 2), "split_workspace_bytes": ws_bytes,
+            "speedup_vs_separate": round(sep_ms / mixed_ms, 4),
+            "decode_bytes": dec_bytes, "prefill_gflop": round(pf_flops / 1e9, 3),
+            "roofline": {"bound": "hbm+mfma overlap", "kernel": "mixed_kernel<128,4>",
+                         "bound_us": round(bound_ms * 1e3, 2),
+                         "hbm_us": round(t_hbm * 1e6, 2), "mfma_us": round(t_mfma * 1e6, 2),
+                         "frac": round(bound_ms / mixed_ms, 4),
+                         "launch_timing": mixed_stats},
+            "separate_timing": sep_stats}
 
 
 def bench_prefill(args, torch, B, W, dev):

@@ -210,6 +210,45 @@ int pkv_store_decode_attn_rope(const void *k, const void *v, const int32_t *slot
                                int32_t partition_tokens, hipStream_t stream);
 
 /*
+ * pkv_mixed_attn -- one continuous-batching iteration in one launch: decode
+ * sequences and prefill chunks together ([NVE] §5.1-5.2: iteration-level
+ * scheduling runs the running sequences' next tokens and newly admitted
+ * requests as one batch; [LLM4] §17.5).  Every sequence is computed as in
+ * pkv_prefill_attn -- new token i of sequence s sits at position c_s + i and
+ * attends to keys 0 .. c_s + i -- and arguments have the same layout and
+ * meaning, with:
+ *   num_decode_seqs  sequences 0 .. num_decode_seqs-1 are decode sequences,
+ *                    one new token each; they are computed as decode (the
+ *                    sequence's K/V split across the waves of a workgroup).  A
+ *                    sequence there with more new tokens is still computed in
+ *                    full, more slowly; one with none writes nothing.
+ *   num_seqs         all sequences; num_decode_seqs .. num_seqs-1 are prefill
+ *                    chunks, computed as MFMA query tiles.
+ *   max_new_len      bounds the prefill chunks' new tokens (decode sequences
+ *                    need not count).
+ *   workspace        optional (null: none).  With pkv_mixed_workspace_bytes
+ *                    bytes or more, prefill chunks with long cached contexts
+ *                    are split over several workgroups by key range, and a
+ *                    second small launch merges their partial results; this
+ *                    shortens the step when chunks are few.  No initial
+ *                    contents are needed.  Calls that share a workspace must
+ *                    not overlap.
+ * The K/V of every new token must be stored before the call (one pkv_store
+ * over the whole batch).  The result does not depend on the split beyond
+ * fp32 rounding.
+ */
+int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                   int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                   const int32_t *context_lens, int32_t num_decode_seqs, int32_t num_seqs,
+                   int32_t max_new_len, int32_t max_context_len, int32_t num_q_heads, float scale,
+                   void *out, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes pkv_mixed_attn can use for these sizes (0: no split). */
+size_t pkv_mixed_workspace_bytes(int32_t num_seqs, int32_t num_decode_seqs, int32_t max_new_len,
+                                 int32_t max_context_len, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim);
+
+/*
  * pkv_prefill_attn -- chunked causal prefill over the paged cache.  Prompt p
  * has n_p = cu_new_lens[p+1] - cu_new_lens[p] new tokens whose K/V are
  * already stored after c_p = context_lens[p] - n_p cached ones.  New token i

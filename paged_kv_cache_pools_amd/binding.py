@@ -24,7 +24,7 @@ PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_CAPACITY, PKV_ERR_SEQUENCE = 5, 6, 7, 8
 # every symbol include/pkv.h and include/pkv_pool.h declare
 EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
             "pkv_decode_attn", "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
-            "pkv_prefill_attn", "pkv_store_fp8",
+            "pkv_prefill_attn", "pkv_mixed_attn", "pkv_mixed_workspace_bytes", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_kv_bytes",
             "pkv_status_string", "pkv_last_error",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
@@ -116,6 +116,11 @@ def load(path: str = LIB_PATH):
     lib.pkv_pool_seq_len.argtypes = [_P, _I64]
     lib.pkv_copy_blocks.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [_P, _I32, _SZ, _I32, _P, _I32, _P]
+    lib.pkv_mixed_attn.restype = ctypes.c_int
+    lib.pkv_mixed_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                   ctypes.c_float, _P, _P, _SZ, _P]
+    lib.pkv_mixed_workspace_bytes.restype = _SZ
+    lib.pkv_mixed_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
     lib.pkv_kv_bytes.restype = ctypes.c_uint64
     lib.pkv_kv_bytes.argtypes = [_I32, _I32, _I32, _I64, _I32]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -366,6 +371,55 @@ def pkv_prefill_attn(q, k_cache, v_cache, block_tables, cu_new_lens, context_len
                                 int(max_new_len), int(max_context_len), hq, float(scale),
                                 out.data_ptr(), _stream(q, stream)),
            "pkv_prefill_attn")
+    return out
+
+
+def pkv_mixed_workspace_bytes(num_seqs: int, num_decode: int, max_new_len: int,
+                              max_context_len: int, num_q_heads: int, num_kv_heads: int,
+                              head_dim: int) -> int:
+    return int(load().pkv_mixed_workspace_bytes(num_seqs, num_decode, max_new_len,
+                                                max_context_len, num_q_heads, num_kv_heads,
+                                                head_dim))
+
+
+def pkv_mixed_attn(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens, num_decode: int,
+                   scale, out, max_new_len: int, max_context_len: int, workspace=None,
+                   split: bool = True, stream=None):
+    """One continuous-batching iteration: sequences 0 .. num_decode-1 are decode
+    sequences (one new token each), the rest prefill chunks; tensors as for
+    pkv_prefill_attn.  ``workspace``: a uint8 device tensor of at least
+    pkv_mixed_workspace_bytes (any contents); None allocates one when
+    ``split`` and the sizes call for it, ``split=False`` passes none."""
+    import torch
+
+    lib = load()
+    cache = _cache(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(cu_new_lens, "cu_new_lens", torch.int32, 1)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    total, hq, d = q.shape
+    s = context_lens.shape[0]
+    if tuple(out.shape) != (total, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    if cu_new_lens.shape[0] != s + 1 or block_tables.shape[0] != s:
+        raise ValueError("cu_new_lens / block_tables do not match context_lens")
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        if workspace is None:
+            need = pkv_mixed_workspace_bytes(s, int(num_decode), int(max_new_len),
+                                             int(max_context_len), hq, cache.num_kv_heads, d)
+            if need > 0:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            _need(workspace, "workspace", torch.uint8, 1)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    _check(lib.pkv_mixed_attn(q.data_ptr(), cache, block_tables.data_ptr(), block_tables.shape[1],
+                              cu_new_lens.data_ptr(), context_lens.data_ptr(), int(num_decode), s,
+                              int(max_new_len), int(max_context_len), hq, float(scale),
+                              out.data_ptr(), ws_ptr, ws_bytes, _stream(q, stream)),
+           "pkv_mixed_attn")
     return out
 
 

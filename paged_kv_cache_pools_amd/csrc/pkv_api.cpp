@@ -7,6 +7,8 @@
 #include "pkv_pool.h"
 
 #include <stdarg.h>
+
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -134,7 +136,118 @@ int32_t fused_waves_for(int64_t units, int32_t max_context_len, int64_t kTargetW
 
 }  // namespace
 
+namespace {
+
+// Split geometry of a mixed launch: how many workgroups a prefill unit may
+// use, and the workspace that needs (0 when units are not split).  Units are
+// split only when there are fewer of them than compute units (256) and their
+// contexts are long: up to one segment per 512 keys of max_context_len (the
+// smallest segment the kernel makes), at most 8.  With more units the GPU is already full and a split only adds the
+// partial results' traffic and the merge launch (measured: 4 chunks x 8 KV
+// heads x 16 query blocks ran 219 us split against 229 us whole, merge
+// included, while one 64-token chunk after 4032 cached keys is one
+// workgroup's walk over 64 key chunks per KV head).
+struct MixedSplit {
+    int64_t units = 0;
+    int32_t slots = 1;
+    size_t bytes = 0;
+};
+
+MixedSplit mixed_split(int32_t num_seqs, int32_t num_decode_seqs, int32_t max_new_len,
+                       int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim) {
+    MixedSplit m;
+    if (num_seqs <= num_decode_seqs || max_new_len <= 0 || num_kv_heads <= 0 ||
+        num_q_heads < num_kv_heads)
+        return m;
+    m.units = (int64_t)(num_seqs - num_decode_seqs) * num_kv_heads *
+              pkv::mixed_query_blocks(max_new_len, num_q_heads / num_kv_heads);
+    const int64_t by_ctx = ((int64_t)max_context_len + 511) / 512;
+    const int64_t by_fill = (256 + m.units - 1) / m.units;
+    m.slots = (int32_t)std::max<int64_t>(1, std::min<int64_t>(pkv::kMaxSegments, std::min(by_ctx, by_fill)));
+    if (m.slots > 1) m.bytes = (size_t)m.units * m.slots * pkv::mixed_partial_bytes(head_dim);
+    return m;
+}
+
+}  // namespace
+
 extern "C" {
+
+size_t pkv_mixed_workspace_bytes(int32_t num_seqs, int32_t num_decode_seqs, int32_t max_new_len,
+                                 int32_t max_context_len, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim) {
+    if (num_seqs < 0 || num_decode_seqs < 0 || num_decode_seqs > num_seqs || max_new_len < 0 ||
+        max_context_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
+        return 0;
+    return mixed_split(num_seqs, num_decode_seqs, max_new_len, max_context_len, num_q_heads,
+                       num_kv_heads, head_dim).bytes;
+}
+
+int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                   int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                   const int32_t *context_lens, int32_t num_decode_seqs, int32_t num_seqs,
+                   int32_t max_new_len, int32_t max_context_len, int32_t num_q_heads, float scale,
+                   void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
+    if (num_seqs < 0 || num_decode_seqs < 0 || num_decode_seqs > num_seqs || max_new_len < 0 ||
+        max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(PKV_ERR_SHAPE, "num_decode_seqs %d, num_seqs %d, max_new_len %d, max_context_len %d",
+                    num_decode_seqs, num_seqs, max_new_len, max_context_len);
+    if (num_seqs == 0) return ok();
+    if (max_new_len > max_context_len)
+        return fail(PKV_ERR_SHAPE, "max_new_len %d exceeds max_context_len %d", max_new_len,
+                    max_context_len);
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+        return fail(PKV_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq %d x 16",
+                    max_context_len, max_blocks_per_seq);
+    if (cache.num_blocks == 0)
+        return fail(PKV_ERR_SHAPE, "an empty pool cannot hold a context of %d tokens",
+                    max_context_len);
+    if (!q || !out || !context_lens || !cu_new_lens || !block_tables)
+        return fail(PKV_ERR_NULL, "q, out, cu_new_lens, context_lens or block_tables is null");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
+    const int64_t nqb = (max_new_len + 31) / 32 * 8;  // the most query blocks any group size makes
+    if ((int64_t)num_decode_seqs * cache.num_kv_heads +
+            (int64_t)(num_seqs - num_decode_seqs) * cache.num_kv_heads * nqb > INT32_MAX)
+        return fail(PKV_ERR_SHAPE, "%d sequences of up to %d new tokens exceed one launch's grid",
+                    num_seqs, max_new_len);
+    pkv::MixedArgs a{};
+    a.q = q;
+    a.k_cache = cache.k;
+    a.v_cache = cache.v;
+    a.block_tables = block_tables;
+    a.cu_new_lens = cu_new_lens;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_new_len = max_new_len;
+    a.max_context_len = max_context_len;
+    a.num_blocks = cache.num_blocks;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache.num_kv_heads;
+    a.head_dim = cache.head_dim;
+    a.scale = scale;
+    a.out = out;
+    a.num_decode = num_decode_seqs;
+    if (workspace) {  // without one, prefill units run whole
+        const MixedSplit m = mixed_split(num_seqs, num_decode_seqs, max_new_len, max_context_len,
+                                         num_q_heads, cache.num_kv_heads, cache.head_dim);
+        if (m.slots > 1) {
+            if (workspace_bytes < m.bytes)
+                return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                            m.bytes);
+            if (!aligned16(workspace))
+                return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+            a.seg_slots = m.slots;
+            a.partials = static_cast<float *>(workspace);
+        }
+    }
+    return hip_status(pkv::launch_mixed(a, stream), "pkv_mixed_attn launch");
+}
 
 int pkv_copy_blocks(void *const *pools, int32_t num_pools, size_t block_bytes, int32_t num_blocks,
                     const int32_t *copies, int32_t num_copies, hipStream_t stream) {

@@ -75,6 +75,23 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
+// Most workgroups a prefill unit of a mixed step splits into (prefill_tile.h).
+constexpr int kMaxSegments = 8;
+
+// Mixed decode + prefill step (mixed.hip): sequences 0 .. num_decode-1 are
+// decode sequences; max_new_len bounds the others' new tokens.
+constexpr int kMixedWaves = 4;  // waves of a mixed-step workgroup (either kind)
+struct MixedArgs : PrefillArgs {
+    int32_t num_decode;
+    int32_t seg_slots = 1;       // workgroups a prefill unit may split into
+    float *partials = nullptr;   // [prefill units][seg_slots] partial results
+};
+hipError_t launch_mixed(const MixedArgs &a, hipStream_t stream);
+// Prefill query blocks of a mixed launch, and the bytes of one segment's
+// partial result.
+int mixed_query_blocks(int32_t max_new_len, int32_t group);
+size_t mixed_partial_bytes(int32_t head_dim);
+
 // Whole-block copies (copy.hip).
 constexpr int kMaxCopyPools = 64;  // pool pointers per launch (kernel arguments)
 struct CopyArgs {

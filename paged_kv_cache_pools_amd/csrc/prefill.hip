@@ -1,122 +1,9 @@
-// prefill.hip -- chunked causal prefill attention over the paged cache, on
-// the gfx950 matrix cores.
-//
-// Prompt p has c cached tokens and n new ones (their K/V already stored).  New
-// token i sits at position c + i and attends to keys 0 .. c + i inclusive:
-// itself and what precedes it, never a later token (Nano-vLLM engine
-// deep-dive §3.2, lower-triangular causal mask; LLM primer part 4 §22 steps
-// 6-8, where the masked weight is exactly 0).  Prefill does O(n * ctx * d)
-// work on O(ctx * d) bytes, so unlike decode it is compute-bound (primer
-// §17.1) and Q K^T and P V run as bf16 MFMA with fp32 accumulation.
-//
-// Formulation (chosen for CDNA4's MFMA register layouts):
-//   S^T = K Q^T  with A = K rows (keys x d) and B = Q^T (d x query columns),
-//   O^T = V^T P^T with A = V^T (d x keys)  and B = P^T (keys x columns).
-// In the 16x16 accumulator layout each lane holds 4 consecutive rows of one
-// column, so every score a lane holds belongs to ONE query column: the online
-// softmax state and the rescale of O^T are lane-local, and the exponentiated
-// scores become the B operand of the P V product without any cross-lane
-// shuffle (the order of the contraction index inside an MFMA is free, so both
-// operands use the same key permutation sigma below).
-//
-// Work split: a workgroup (4 wavefronts) owns one (prompt, KV head, block of
-// query tokens); each wave owns 32 query columns = 32/G tokens x the G query
-// heads that share the KV head, so every K/V fragment read from LDS feeds 2
-// MFMAs.  32 columns keep a wave's O^T, Q^T, scores and staging within 256
-// registers, so two workgroups share a CU and one's softmax overlaps the
-// other's MFMAs.  Keys stream in chunks of 64 (4 cache blocks) gathered through the
-// block table: while a chunk is computed from one LDS buffer, the next one is
-// loaded into registers and written to the other buffer afterwards, so global
-// latency hides behind the MFMAs and one barrier per chunk suffices.  K is
-// stored row-major (one padded row per key), V transposed (one padded row per
-// head_dim element) so the A operand of P V is two 8-byte LDS reads.
-//
-// Softmax: scores stay fp32; the scale (log2 e folded in) is applied in the
-// FMA that feeds exp2.  The running maximum is raised only when a chunk's
-// maximum exceeds it by more than 2^8 (the decision is taken for the whole
-// wave), so O^T is rescaled on a few chunks instead of every one; weights are
-// then at most 2^8, far from fp32 or bf16 overflow, and the final division by
-// the weight sum, accumulated with the same stale maximum, is exact algebra.
-// For the P V product each weight is split into bf16 hi + lo parts (two
-// MFMAs), so P carries about 16 significant bits into the matrix cores.
-//
-// Keys at or past the context end are zero in LDS (V) or masked by select (S),
-// so NaN bits in unused slots never reach the output.
-#include <math.h>
-
-#include "pkv_device.h"
-#include "pkv_internal.h"
+// prefill.hip -- the chunked causal prefill kernel (gfx950): one workgroup
+// per (prompt, KV head, block of query tokens), each running the MFMA query
+// tile of prefill_tile.h.
+#include "prefill_tile.h"
 
 namespace pkv {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4 &a, const uint4 &b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-// two fp32 -> packed bf16 (hardware convert, round to nearest even)
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
-
-// Split two finite fp32 softmax weights into bf16 hi and lo parts with
-// p == hi + lo to about 2^-16 relative: hi is p truncated to bf16 (its upper
-// half), lo is the exact remainder p - hi rounded to bf16.  P V is computed as
-// hi V + lo V, which keeps the weights' rounding far below the bf16 rounding
-// of the output: with bf16 weights alone a row of a few keys whose output is
-// near 2 can miss a 1e-2 absolute bound.
-__device__ __forceinline__ void split2_bf16(float p0, float p1, uint32_t &hi, uint32_t &lo) {
-    const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
-    hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // (b0 >> 16) | (b1 & 0xffff0000)
-    lo = cvt_pk_bf16(p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u));
-}
-
-// The running maximum is raised only when it grows by more than this (log2
-// units), which bounds every softmax weight by 2^8.
-constexpr float kRescaleLog2 = 8.0f;
-
-// s_waitcnt immediate: vector-memory count 0, export and LDS counts left at
-// their maxima (no wait on them).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-template <int D, int G>
-struct PrefillGeom {
-    static constexpr int WAVES = 4;
-    static constexpr int THREADS = 64 * WAVES;
-    static constexpr int COLS = 32;              // query columns per wave
-    static constexpr int NT = COLS / 16;         // 16-column MFMA tiles per wave
-    static constexpr int TW = COLS / G;          // query tokens per wave
-    static constexpr int TWG = WAVES * TW;       // query tokens per workgroup
-    static constexpr int KC = 64;                // keys per chunk (4 cache blocks)
-    static constexpr int KSTEPS = D / 32;        // MFMA k-steps over head_dim
-    static constexpr int MT = D / 16;            // head_dim tiles of O^T
-    static constexpr int KROW = D * 2;           // bytes per K row in LDS (swizzled, unpadded)
-    static constexpr int CPR = D / 8;            // 16-byte slots per K row
-    static constexpr int RPS = 64 / CPR;         // K rows per 1 KiB direct-load segment
-    static constexpr int VROW = KC * 2 + 8;      // bytes per V^T row in LDS (34 dwords)
-    static constexpr int KBYTES = KC * KROW;
-    static constexpr int VBYTES = D * VROW;
-    static constexpr int BUF = KBYTES + VBYTES;  // one LDS buffer
-    static constexpr int CPB = kBlockTokens * D / 8;   // 16-byte chunks per block tile
-    static constexpr int KLOADS = KC * D / 8 / THREADS;  // K direct loads per thread
-    static constexpr int VITEMS = (KC / 2) * (D / 8) / THREADS;  // V key-pair items per thread
-    static_assert(D == 64 || D == 128, "head_dim");
-    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-    static_assert(CPB % 64 == 0 && D % 64 == 0, "a wave's staging stays inside one block");
-    static_assert(kBlockTokens % RPS == 0, "a K segment stays inside one block");
-    // K slot of 16-byte chunk dc of chunk row r: an XOR swizzle that makes the
-    // 16 lanes of an MFMA operand read (16 rows, one chunk) hit 16 distinct
-    // bank groups; for D = 64 two rows share a 256-byte bank line, so the
-    // swizzle uses the row pair.
-    static __device__ __forceinline__ int kslot(int r, int dc) {
-        return D == 128 ? (dc ^ (r & 15)) : (dc ^ ((r >> 1) & 7));
-    }
-};
 
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
@@ -127,11 +14,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     int32_t num_q_heads, int32_t num_kv_heads, int32_t num_qblocks, float scale_log2,
     uint16_t *__restrict__ out) {
     using Geo = PrefillGeom<D, G>;
-    constexpr int TW = Geo::TW, TWG = Geo::TWG, KC = Geo::KC, KSTEPS = Geo::KSTEPS, NT = Geo::NT;
-    constexpr int MT = Geo::MT, KROW = Geo::KROW, VROW = Geo::VROW, CPR = Geo::CPR;
-    constexpr int KLOADS = Geo::KLOADS, VITEMS = Geo::VITEMS;
-    const float kNegInf = -INFINITY;
-
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Geo::BUF];
 
     // ---- work unit.  Workgroups are dealt to the 8 XCDs round-robin by their
@@ -150,290 +32,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int qb = num_qblocks - 1 - unit % num_qblocks;
     const int p = (unit / num_qblocks) % num_seqs;
     const int kvh = unit / (num_qblocks * num_seqs);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = wave_id_uniform();
-    const int a = lane >> 4;    // 16-lane group
-    const int col = lane & 15;  // column within an N-tile
-
-    const int row0 = cu_new_lens[p];
-    int ctx = context_lens[p];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
-    const int n = min(cu_new_lens[p + 1] - row0, ctx);
-    const int c = ctx - n;
-    const int T0 = qb * TWG;
-    if (n <= 0 || T0 >= n) return;  // uniform over the workgroup
-    const int kend = c + min(T0 + TWG, n);  // keys [0, kend) are visible to someone here
-    const int nchunks = (kend + KC - 1) / KC;
-
-    // a negative scale is applied by flipping the sign of q (exact in bf16),
-    // so the softmax below can take the maximum of the raw scores
-    const uint32_t qsign = scale_log2 < 0.f ? 0x80008000u : 0u;
-    const float sl = fabsf(scale_log2);
-
-    // ---- Q^T fragments (B operand): column j = nt*16 + col of this wave is
-    // token  T0 + w*TW + j / G,  query head  kvh*G + j % G
-    uint4 qf[NT][KSTEPS];
-    int pos[NT];  // absolute position of each N-tile's column for this lane
-    bool live[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int j = nt * 16 + col;
-        const int tok = T0 + w * TW + j / G;
-        const int h = kvh * G + j % G;
-        live[nt] = tok < n;
-        pos[nt] = c + tok;
-        const uint4 *src = reinterpret_cast<const uint4 *>(
-            q + ((size_t)(row0 + min(tok, n - 1)) * num_q_heads + h) * D);
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            uint4 u = src[ks * 4 + a];
-            u = make_uint4(u.x ^ qsign, u.y ^ qsign, u.z ^ qsign, u.w ^ qsign);
-            if (!live[nt]) u = make_uint4(0u, 0u, 0u, 0u);
-            qf[nt][ks] = u;
-        }
-    }
-
-    f32x4_t o[MT][NT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[NT], l[NT];  // running max (log2 domain, shared by the column's lanes), partial sums
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        m[nt] = kNegInf;
-        l[nt] = 0.f;
-    }
-    // positions of this wave's first and last live token: chunks wholly below
-    // the first need no causal mask, chunks wholly above the last are skipped
-    const int wave_min_pos = c + T0 + w * TW;
-    const int wave_max_pos = c + min(T0 + (w + 1) * TW, n) - 1;
-    const bool wave_live = T0 + w * TW < n;
-
-    const int32_t *bt = block_tables + (size_t)p * max_blocks_per_seq;
-    const size_t tile = (size_t)kBlockTokens * D;
-
-    // ---- staging of one key chunk.  K goes global -> LDS directly (16-byte
-    // loads whose LDS destination is the wave's 1 KiB segment, lane-linear):
-    // each lane fetches the global chunk that belongs at its LDS slot, so no
-    // register holds K.  V goes global -> registers -> LDS, transposed: thread
-    // t moves key pairs (2 keys x 8 elements).  Each wave's share of an
-    // instruction lies in one cache block, so the block id is a scalar.  K rows
-    // past the context end read some valid block (their scores are masked); V
-    // keys past it are zero.
-    auto block_id = [&](int lb) {
-        int pb = 0;
-        if (lb * kBlockTokens < ctx) {
-            pb = bt[lb];
-            pb = ((unsigned)pb < (unsigned)num_blocks) ? pb : 0;
-        }
-        return pb;
-    };
-    auto stage_k = [&](unsigned char *buf, int k0) {
-#pragma unroll
-        for (int it = 0; it < KLOADS; ++it) {
-            const int g = it * Geo::WAVES + w;            // 1 KiB segment of the K buffer
-            const int r = g * Geo::RPS + lane / CPR;      // key row within the chunk
-            const int dc = Geo::kslot(r, lane % CPR);     // chunk this slot holds
-            const int pb = block_id(k0 / kBlockTokens + (g * Geo::RPS) / kBlockTokens);
-            const uint16_t *src =
-                k_cache + (((size_t)pb * num_kv_heads + kvh) * kBlockTokens + r % kBlockTokens) * D +
-                dc * 8;
-            __builtin_amdgcn_global_load_lds(
-                src, (__attribute__((address_space(3))) void *)(buf + g * 1024), 16, 0, 0);
-        }
-    };
-    uint4 vreg[VITEMS][2];
-    auto stage_load = [&](int k0) {
-#pragma unroll
-        for (int it = 0; it < VITEMS; ++it) {
-            const int id = it * Geo::THREADS + tid;
-            const int blk = __builtin_amdgcn_readfirstlane(id / D);  // D items per block
-            const int within = id % D;
-            const int pair = within % 8, dc = within / 8;
-            const int lb = k0 / kBlockTokens + blk;
-            const int key = lb * kBlockTokens + 2 * pair;
-            // a key past the context end contributes exactly nothing: its V is
-            // zero (the block id is clamped to a valid block before the read)
-            const uint4 *base = reinterpret_cast<const uint4 *>(
-                v_cache + ((size_t)block_id(lb) * num_kv_heads + kvh) * tile);
-            const uint4 x0 = base[(2 * pair) * (D / 8) + dc];
-            const uint4 x1 = base[(2 * pair + 1) * (D / 8) + dc];
-            const uint32_t k0m = key < ctx ? 0xffffffffu : 0u;
-            const uint32_t k1m = key + 1 < ctx ? 0xffffffffu : 0u;
-            vreg[it][0] = make_uint4(x0.x & k0m, x0.y & k0m, x0.z & k0m, x0.w & k0m);
-            vreg[it][1] = make_uint4(x1.x & k1m, x1.y & k1m, x1.z & k1m, x1.w & k1m);
-        }
-    };
-    auto stage_store = [&](unsigned char *buf) {
-        unsigned char *lv = buf + Geo::KBYTES;
-#pragma unroll
-        for (int it = 0; it < VITEMS; ++it) {
-            const int id = it * Geo::THREADS + tid;
-            const int blk = id / D, within = id % D;
-            const int pair = within % 8, dc = within / 8;
-            const int kcol = blk * kBlockTokens + 2 * pair;  // key column within the chunk
-            const uint32_t w0[4] = {vreg[it][0].x, vreg[it][0].y, vreg[it][0].z, vreg[it][0].w};
-            const uint32_t w1[4] = {vreg[it][1].x, vreg[it][1].y, vreg[it][1].z, vreg[it][1].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
-                *reinterpret_cast<uint32_t *>(lv + (dc * 8 + 2 * e) * VROW + kcol * 2) = lo;
-                *reinterpret_cast<uint32_t *>(lv + (dc * 8 + 2 * e + 1) * VROW + kcol * 2) = hi;
-            }
-        }
-    };
-
-    // ---- one chunk's attention for this wave, from LDS buffer `buf`, in two
-    // halves of 32 keys (Q K^T, softmax, P V each), which keeps the scores of
-    // only half a chunk in registers at a time
-    auto compute = [&](const unsigned char *buf, int k0) {
-        const unsigned char *lk = buf;
-        const unsigned char *lv = buf + Geo::KBYTES;
-        const bool need_mask = (k0 + KC - 1 > wave_min_pos) || (k0 + KC > ctx);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            // S^T = K Q^T over key tiles 2 hf and 2 hf + 1
-            f32x4_t s[2][NT];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int kt = 2 * hf + t;
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) s[t][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const int r = kt * 16 + col;
-                    const uint4 kf = *reinterpret_cast<const uint4 *>(
-                        lk + r * KROW + Geo::kslot(r, ks * 4 + a) * 16);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) s[t][nt] = mfma16x16x32(kf, qf[nt][ks], s[t][nt]);
-                }
-            }
-
-            // per column: masked raw maximum (s[t][nt][r] is key k0 + 32 hf + 16 t + 4 a + r)
-            float mc[NT];
-            bool grow = false;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                float bm = kNegInf;
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float v = s[t][nt][r];
-                        if (need_mask) {
-                            const int key = k0 + hf * 32 + t * 16 + a * 4 + r;
-                            v = (key < ctx && key <= pos[nt]) ? v : kNegInf;
-                            s[t][nt][r] = v;
-                        }
-                        bm = fmaxf(bm, v);
-                    }
-                bm = fmaxf(bm, __shfl_xor(bm, 16));
-                bm = fmaxf(bm, __shfl_xor(bm, 32));
-                const float bms = (bm == kNegInf) ? kNegInf : bm * sl;
-                mc[nt] = fmaxf(m[nt], bms);
-                grow |= mc[nt] > m[nt] + kRescaleLog2;
-            }
-            // raise the maxima (and rescale) only when some column outgrew its
-            // maximum by more than 2^8; a wave-wide decision, so the branch is uniform
-            if (__any(grow)) {
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const float alpha = (mc[nt] == kNegInf) ? 1.f : exp2f(m[nt] - mc[nt]);
-                    m[nt] = mc[nt];
-                    l[nt] *= alpha;
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
-                }
-            }
-
-            // weights, their partial sums, and P^T as the B operand (bf16).  Key
-            // permutation sigma: MFMA k-slot (a, 0..3) <- keys 4a..4a+3 of the
-            // half's first 16, k-slot (a, 4..7) <- keys 16+4a..16+4a+3
-            uint4 ph[NT], pl[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const float mu = (m[nt] == kNegInf) ? 0.f : m[nt];
-                float psum = 0.f;
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float e = __builtin_amdgcn_exp2f(fmaf(s[t][nt][r], sl, -mu));
-                        if (need_mask) e = (s[t][nt][r] == kNegInf) ? 0.f : e;
-                        s[t][nt][r] = e;
-                        psum += e;
-                    }
-                l[nt] += psum;
-                split2_bf16(s[0][nt][0], s[0][nt][1], ph[nt].x, pl[nt].x);
-                split2_bf16(s[0][nt][2], s[0][nt][3], ph[nt].y, pl[nt].y);
-                split2_bf16(s[1][nt][0], s[1][nt][1], ph[nt].z, pl[nt].z);
-                split2_bf16(s[1][nt][2], s[1][nt][3], ph[nt].w, pl[nt].w);
-            }
-
-            // O^T += V^T P^T over the half's 32 keys
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const unsigned char *vrow = lv + (mt * 16 + col) * VROW;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + a * 4) * 2);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + 16 + a * 4) * 2);
-                const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    o[mt][nt] = mfma16x16x32(vf, ph[nt], o[mt][nt]);
-                    o[mt][nt] = mfma16x16x32(vf, pl[nt], o[mt][nt]);
-                }
-            }
-        }
-    };
-
-    // ---- the chunk pipeline: compute chunk j from buffer j % 2 while chunk
-    // j + 1 travels global -> registers; the registers go to the other buffer
-    // after the compute.  That buffer was last read in chunk j - 1, which every
-    // wave finished before the previous barrier.
-    // The direct K loads complete asynchronously: every wave waits for its own
-    // (vmcnt 0) before the barrier that publishes the buffer.
-    stage_k(lds, 0);
-    stage_load(0);
-    stage_store(lds);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    for (int j = 0; j < nchunks; ++j) {
-        const int k0 = j * KC;
-        const bool more = j + 1 < nchunks;
-        if (more) {
-            stage_k(lds + ((j + 1) & 1) * Geo::BUF, k0 + KC);
-            stage_load(k0 + KC);
-        }
-        if (wave_live && k0 <= wave_max_pos) compute(lds + (j & 1) * Geo::BUF, k0);
-        if (more) stage_store(lds + ((j + 1) & 1) * Geo::BUF);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-    }
-
-    // ---- normalise and write: o[mt][nt][r] is O^T[d = 16 mt + 4 a + r][column]
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        float lt = l[nt];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
-        if (!live[nt]) continue;
-        const float inv = 1.f / lt;
-        const int j = nt * 16 + col;
-        const int tok = T0 + w * TW + j / G;
-        const int h = kvh * G + j % G;
-        uint16_t *dst = out + ((size_t)(row0 + tok) * num_q_heads + h) * D;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            uint2 pk;
-            pk.x = pack_bf16x2(o[mt][nt][0] * inv, o[mt][nt][1] * inv);
-            pk.y = pack_bf16x2(o[mt][nt][2] * inv, o[mt][nt][3] * inv);
-            *reinterpret_cast<uint2 *>(dst + mt * 16 + a * 4) = pk;
-        }
-    }
+    prefill_unit<D, G>(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens,
+                       max_blocks_per_seq, max_context_len, num_blocks, num_q_heads, num_kv_heads,
+                       scale_log2, out, p, qb, kvh, lds);
 }
 
 template <int D, int G>

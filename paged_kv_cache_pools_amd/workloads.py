@@ -245,12 +245,32 @@ def chunked_prefill(seed: int = 5) -> Workload:
     return make_prefill("chunked_prefill", cached, [2048] * 8, 32, 8, 128, seed)
 
 
+def mixed_step(seed: int = 6) -> Workload:
+    """One continuous-batching iteration of 2016 new tokens: the 32 x 4096 GQA
+    decode batch (one new token each, listed first) plus 4 prompt chunks of
+    496 new tokens after 0, 512, 1536 and 3072 cached ones; 32 q / 8 kv heads,
+    d 128."""
+    cached = [4095] * 32 + [0, 512, 1536, 3072]
+    new = [1] * 32 + [496] * 4
+    return make_prefill("mixed_step", cached, new, 32, 8, 128, seed)
+
+
+def mixed_tail(seed: int = 7) -> Workload:
+    """A continuous-batching iteration whose only prompt work is the last
+    64-token chunk of a 4096-token prompt: the 32 x 4096 GQA decode batch plus
+    one chunk of 64 new tokens after 4032 cached ones; 32 q / 8 kv heads,
+    d 128."""
+    return make_prefill("mixed_tail", [4095] * 32 + [4032], [1] * 32 + [64], 32, 8, 128, seed)
+
+
 CONFIGS = {
     "tiny": tiny,
     "qwen_mha": qwen_mha,
     "mistral_gqa": mistral_gqa,
     "cont_batch": cont_batch,
     "chunked_prefill": chunked_prefill,
+    "mixed_step": mixed_step,
+    "mixed_tail": mixed_tail,
 }
 
 

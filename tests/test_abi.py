@@ -172,6 +172,38 @@ def test_store_decode_rope_validation(lib):
     assert B.pkv_last_error() != ""
 
 
+def test_mixed_validation(lib):
+    mx = lambda nd=1, s=3, mn=16, mc=40, q=FAKE, c=None, hq=4, ws=None, wsb=0, mb=4: \
+        lib.pkv_mixed_attn(q, c or cache(), FAKE, mb, FAKE, FAKE, nd, s, mn, mc, hq,
+                           ctypes.c_float(0.125), FAKE, ws, wsb, None)
+    assert mx(s=0, nd=0) == 0               # empty batch: nothing launched
+    assert mx(nd=4) == 2 and mx(nd=-1) == 2  # more decode sequences than sequences
+    assert mx(mn=50) == 2                   # more new tokens than context
+    assert mx(mc=80) == 2                   # beyond max_blocks * 16
+    assert mx(q=0) == 1 and mx(q=FAKE + 8) == 4
+    assert mx(hq=6) == 3 and mx(c=cache(d=96)) == 3
+    # a workspace too small for the split these sizes call for
+    assert B.pkv_mixed_workspace_bytes(3, 1, 16, 3000, 4, 2, 64) > 0
+    assert mx(ws=FAKE, wsb=16, mc=3000, mb=200) == 5
+    assert mx(ws=FAKE + 4, wsb=1 << 30, mc=3000, mb=200) == 4
+    assert B.pkv_last_error() != ""
+
+
+def test_mixed_workspace_sizing(lib):
+    # 32 decode seqs + 1 chunk of 64 after 4032 cached, GQA 32/8, d 128: 1 x 8
+    # x 2 units, 8 segments each (4096 / 512), 4 waves x 32 columns x 132
+    # floats per segment
+    units = 1 * 8 * 2
+    assert B.pkv_mixed_workspace_bytes(33, 32, 64, 4096, 32, 8, 128) == units * 8 * 4 * 2 * 16 * 132 * 4
+    # 4 chunks of 496: 4 x 8 x 16 = 512 units fill the GPU: no split
+    assert B.pkv_mixed_workspace_bytes(36, 32, 496, 4096, 32, 8, 128) == 0
+    # many units, or short contexts, or no prefill: no split
+    assert B.pkv_mixed_workspace_bytes(40, 8, 2048, 6144, 32, 8, 128) == 0
+    assert B.pkv_mixed_workspace_bytes(4, 2, 64, 500, 32, 8, 128) == 0   # one segment's worth of keys
+    assert B.pkv_mixed_workspace_bytes(8, 8, 1, 4096, 32, 8, 128) == 0
+    assert B.pkv_mixed_workspace_bytes(4, 5, 64, 900, 32, 8, 128) == 0   # invalid: no bytes
+
+
 def test_fp8_validation(lib):
     c8 = lambda ks=FAKE, vs=FAKE, d=64: B.PkvCacheFp8(FAKE, FAKE, ks, vs, 16, 2, d, 16)
     st = lambda c, n=4: lib.pkv_store_fp8(FAKE, FAKE, FAKE, n, c, None)
