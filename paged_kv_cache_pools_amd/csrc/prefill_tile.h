@@ -81,6 +81,25 @@ __device__ __forceinline__ void split2_bf16(float p0, float p1, uint32_t &hi, ui
     lo = cvt_pk_bf16(p0 - __uint_as_float(b0 & 0xffff0000u), p1 - __uint_as_float(b1 & 0xffff0000u));
 }
 
+// Reductions across the four 16-lane rows of a wave, in VALU: the gfx950 lane
+// swaps hand each lane the value of the same lane in the partner row (16 or
+// 32 lanes away), replacing an LDS-crossbar shuffle.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+// sums in the same order on every lane: (row 0 + row 1) + (row 2 + row 3)
+__device__ __forceinline__ float sum_rows(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // The running maximum is raised only when it grows by more than this (log2
 // units), which bounds every softmax weight by 2^8.
 constexpr float kRescaleLog2 = 8.0f;
@@ -335,14 +354,16 @@ __device__ __forceinline__ void prefill_unit(
         for (int hf = 0; hf < 2; ++hf) {
             // S^T = K Q^T over key tiles 2 hf and 2 hf + 1
             f32x4_t s[2][NT];
+            // (both key tiles per k-step: 4 independent accumulators)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int kt = 2 * hf + t;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) s[t][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const int r = kt * 16 + col;
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int r = (2 * hf + t) * 16 + col;
                     const uint4 kf = *reinterpret_cast<const uint4 *>(
                         lk + r * KROW + Geo::kslot(r, ks * 4 + a) * 16);
 #pragma unroll
@@ -378,8 +399,7 @@ __device__ __forceinline__ void prefill_unit(
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[t][nt][r]);
-                bm = fmaxf(bm, __shfl_xor(bm, 16));
-                bm = fmaxf(bm, __shfl_xor(bm, 32));
+                bm = max_xor32(max_xor16(bm));
                 const float bms = (bm == kNegInf) ? kNegInf : bm * sl;
                 mc[nt] = fmaxf(m[nt], bms);
                 grow |= mc[nt] > m[nt] + kRescaleLog2;
@@ -435,18 +455,29 @@ __device__ __forceinline__ void prefill_unit(
                 split2_bf16(s[1][nt][2], s[1][nt][3], ph[nt].w, pl[nt].w);
             }
 
-            // O^T += V^T P^T over the half's 32 keys
+            // O^T += V^T P^T over the half's 32 keys, two head_dim tiles at a
+            // time so that 4 independent accumulators separate each MFMA from
+            // the one that reads its result
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const unsigned char *vrow = lv + (mt * 16 + col) * VROW;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + a * 4) * 2);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + 16 + a * 4) * 2);
-                const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            for (int mt = 0; mt < MT; mt += 2) {
+                uint4 vf[2];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    o[mt][nt] = mfma16x16x32(vf, ph[nt], o[mt][nt]);
-                    o[mt][nt] = mfma16x16x32(vf, pl[nt], o[mt][nt]);
+                for (int u = 0; u < 2; ++u) {
+                    const unsigned char *vrow = lv + ((mt + u) * 16 + col) * VROW;
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + a * 4) * 2);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + 16 + a * 4) * 2);
+                    vf[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 }
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        o[mt + u][nt] = mfma16x16x32(vf[u], ph[nt], o[mt + u][nt]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        o[mt + u][nt] = mfma16x16x32(vf[u], pl[nt], o[mt + u][nt]);
             }
         }
     };
@@ -479,9 +510,7 @@ __device__ __forceinline__ void prefill_unit(
     float lt[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        lt[nt] = l[nt];
-        lt[nt] += __shfl_xor(lt[nt], 16);
-        lt[nt] += __shfl_xor(lt[nt], 32);
+        lt[nt] = sum_rows(l[nt]);
     }
 
     if constexpr (SPLIT) {
