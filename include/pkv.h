@@ -235,7 +235,9 @@ int pkv_store_decode_attn_rope(const void *k, const void *v, const int32_t *slot
  *                    not overlap.
  * The K/V of every new token must be stored before the call (one pkv_store
  * over the whole batch).  The result does not depend on the split beyond
- * fp32 rounding.
+ * fp32 rounding.  With num_decode_seqs = 0 this is chunked prefill that can
+ * split few long-context chunks (the last chunk of a long prompt), which
+ * pkv_prefill_attn runs as one workgroup per query block and KV head.
  */
 int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
                    int32_t max_blocks_per_seq, const int32_t *cu_new_lens,

@@ -188,3 +188,18 @@ def test_mixed_tail_full_size_split():
     cu = np.concatenate([[0], np.cumsum(h["new_lens"])]).astype(np.int32)
     ref = orc().prefill(h["q"], h["kc"], h["vc"], h["bt"], cu, h["ctx"], wl.scale)
     compare(out.index_select(0, torch.from_numpy(h["tok"]).cuda()), ref, "mixed tail full size")
+
+
+def test_mixed_prefill_only_split():
+    """With no decode sequences pkv_mixed_attn is chunked prefill whose few,
+    long-context chunks split by key range: the last chunks of two long
+    prompts."""
+    wl = W.make_prefill("prefill_tails", [3000, 1900], [32, 17], 16, 4, 128, 740, spare_blocks=1)
+    need = B.pkv_mixed_workspace_bytes(2, 0, 32, int(wl.context_lens.max()), 16, 4, 128)
+    assert need > 0
+    c = Case(wl)
+    c.gpu_store()
+    say(f"[gpu] prefill-only mixed launch with split units, workspace {need} B")
+    out = run_mixed(c, 0, workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    c.oracle_store()
+    compare(out, c.oracle_prefill(), "prefill-only split")
