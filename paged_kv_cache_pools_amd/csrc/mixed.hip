@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256) void mixed_merge_kernel(
     const float *__restrict__ partials, int32_t seg_slots) {
     const int num_prefill = num_seqs - num_decode;
     constexpr int PARTS = prefill_merge_parts<D, G>();
+    static_assert(PARTS <= kMaxSegments, "the host's grid bound covers the merge launch");
     const int unit = blockIdx.x / PARTS;  // (rank * num_qblocks + qb from the last) * H_kv + kvh
     const int kvh = unit % num_kv_heads;
     const int qb = num_qblocks - 1 - (unit / num_kv_heads) % num_qblocks;

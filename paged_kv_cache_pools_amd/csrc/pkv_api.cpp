@@ -210,9 +210,13 @@ int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
         return fail(PKV_ERR_NULL, "q, out, cu_new_lens, context_lens or block_tables is null");
     if (!aligned16(q) || !aligned16(out))
         return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
-    const int64_t nqb = (max_new_len + 31) / 32 * 8;  // the most query blocks any group size makes
+    // the largest grid any group size and split can make: query blocks hold at
+    // least 16 tokens (group 8), a unit splits into at most kMaxSegments
+    // workgroups, and the merge launch uses at most that many per unit
+    const int64_t nqb = (max_new_len + 15) / 16;
     if ((int64_t)num_decode_seqs * cache.num_kv_heads +
-            (int64_t)(num_seqs - num_decode_seqs) * cache.num_kv_heads * nqb > INT32_MAX)
+            (int64_t)(num_seqs - num_decode_seqs) * cache.num_kv_heads * nqb * pkv::kMaxSegments >
+        INT32_MAX)
         return fail(PKV_ERR_SHAPE, "%d sequences of up to %d new tokens exceed one launch's grid",
                     num_seqs, max_new_len);
     pkv::MixedArgs a{};
