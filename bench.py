@@ -514,8 +514,48 @@ def bench_other(torch, B, W, dev, name, iters=20):
     if wl.shared_blocks:
         uniq = unique_tok * 2 * wl.num_kv_heads * wl.head_dim * 2
         res["unique_kv_gbs"] = round(uniq / us / 1e3, 1)
+        res["shared_prefix"] = bench_prefix(torch, B, wl, t, out, stream, iters, logical, uniq)
     del t
     return res
+
+
+def bench_prefix(torch, B, wl, t, out, stream, iters, logical, uniq):
+    """The same step as store + pkv_decode_attn_prefix: groups found by
+    pkv_prefix_groups on the host tables, each group's prefix read once."""
+    dev = t["q"].device
+    starts, plens, mg = B.pkv_prefix_groups(wl.block_tables, wl.context_lens)
+    gs, pl = torch.from_numpy(starts).to(dev), torch.from_numpy(plens).to(dev)
+    ptoks = (0, 128, 256, 512)
+    ws = torch.empty(max(B.pkv_decode_prefix_workspace_bytes(
+        wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.max_context_len, p)
+        for p in ptoks), dtype=torch.uint8, device=dev)
+
+    def run(l, p):
+        B.pkv_store(t["k_new"], t["v_new"], t["slot_mapping"], t["k_caches"][l], t["v_caches"][l])
+        B.pkv_decode_attn_prefix(t["q"], t["k_caches"][l], t["v_caches"][l], t["block_tables"],
+                                 t["context_lens"], wl.scale, out, gs, pl, mg,
+                                 max_context_len=wl.max_context_len, workspace=ws,
+                                 partition_tokens=p)
+
+    for p in ptoks:
+        for l in (0, 1):
+            run(l, p)
+    torch.cuda.synchronize()
+    sweep = {}
+    for p in ptoks:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(iters):
+            run(i & 1, p)
+        b.record(stream)
+        torch.cuda.synchronize()
+        sweep["auto" if p == 0 else str(p)] = round(a.elapsed_time(b) * 1e3 / iters, 2)
+    us = sweep["auto"]
+    return {"groups": len(plens), "prefix_lens": sorted(set(int(x) for x in plens)),
+            "max_group_size": int(mg), "us_per_step": us,
+            "us_by_partition_tokens": sweep, "logical_kv_gbs": round(logical / us / 1e3, 1),
+            "unique_kv_gbs": round(uniq / us / 1e3, 1),
+            "tokens_per_s": round(wl.num_seqs / (us * 1e-6), 1)}
 
 
 def bench_pool(torch, B, W, dev, steps=64):

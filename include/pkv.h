@@ -111,8 +111,8 @@ int pkv_store(const void *k, const void *v, const int32_t *slot_mapping, int32_t
  * passed partition_tokens = 0:
  *   -W (W in 1..8): the single-pass kernel, one workgroup of W wavefronts per
  *      (sequence, KV head); the waves split the sequence's blocks evenly and
- *      merge through LDS.  Chosen when there are at least 128 such units and
- *      max_context_len <= 8192.
+ *      merge through LDS.  Chosen when there are at least 128 such units,
+ *      max_context_len <= 8192 and no wave walks more than 1024 tokens.
  *   P > 0 (a multiple of 16): two-pass split-KV, one wavefront per (sequence,
  *      KV head, P-token partition), partials merged by a second kernel; P is
  *      chosen so that the partitions fill the GPU.
@@ -249,6 +249,75 @@ int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
 size_t pkv_mixed_workspace_bytes(int32_t num_seqs, int32_t num_decode_seqs, int32_t max_new_len,
                                  int32_t max_context_len, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * pkv_decode_attn_prefix -- pkv_decode_attn for a batch in which groups of
+ * consecutive sequences share their first tokens through the same physical
+ * blocks (prefix sharing: [LLM4] §17.6-17.7; [NVE] §2.2 prefix cache).  The
+ * result is pkv_decode_attn's, up to the order of fp32 rounding; the shared
+ * blocks are read once per group instead of once per sequence.  The group's
+ * queries attend to the prefix together on the matrix cores (one query tile
+ * per group, KV head and key range; P is rounded to bf16 in two parts, as in
+ * pkv_prefill_attn), each sequence's remaining tokens run as split-KV
+ * partitions, and a second launch merges the partial results exactly.
+ *   group_starts     int32 [num_groups + 1], device: group g is sequences
+ *                    group_starts[g] .. group_starts[g+1]-1 (nondecreasing,
+ *                    within 0 .. num_seqs).  A sequence outside every group
+ *                    shares nothing.
+ *   prefix_lens      int32 [num_groups], device: tokens at the front of every
+ *                    sequence of group g that lie in the same physical blocks
+ *                    (rounded down to whole blocks; 0: the group shares nothing).
+ *   num_groups       >= 0 (0: every sequence is computed as split-KV decode).
+ *   max_group_size   host-side bound of the sizes of groups with a prefix;
+ *                    sizes the grid.
+ *   partition_tokens length of a tail partition (counted from the prefix
+ *                    end): a positive multiple of 16, or 0 for automatic.
+ *   workspace        device scratch of at least
+ *                    pkv_decode_prefix_workspace_bytes(num_seqs, num_q_heads,
+ *                    cache.num_kv_heads, cache.head_dim, max_context_len,
+ *                    partition_tokens) bytes; no initial contents needed.
+ *                    Calls that share a workspace must not overlap.
+ * Every other argument as for pkv_decode_attn.  Preconditions on device data
+ * (not checked on the host): the first prefix_lens[g] / 16 entries of every
+ * member's block-table row equal those of the group's first row (the prefix
+ * is read through that row).  A sequence whose group's prefix exceeds its
+ * context, or that lies beyond the first max_group_size sequences of its
+ * group, gets NaN output.  pkv_prefix_groups finds valid groups from host
+ * copies of the block tables.
+ */
+int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                           float scale, const int32_t *group_starts, const int32_t *prefix_lens,
+                           int32_t num_groups, int32_t max_group_size, void *out, void *workspace,
+                           size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream);
+
+/* Workspace bytes pkv_decode_attn_prefix needs for these sizes (0 on invalid
+ * arguments). */
+size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ * pkv_prefix_groups -- groups for pkv_decode_attn_prefix, from HOST copies of
+ * the block tables and context lengths.  Scans the sequences in order: a run
+ * starts at sequence s, takes as its prefix the whole blocks s and s + 1
+ * share at the front of their rows (blocks wholly inside both contexts), and
+ * extends over each next sequence that shares at least those blocks with s.
+ * A run of two or more sequences whose prefix holds at least
+ * min_prefix_tokens tokens (at least one block) is a group; consecutive
+ * sequences in no such run form groups of prefix 0.  A batch that lists
+ * requests with a common prompt next to each other ([NVE] §2.2: the prefix
+ * cache hands them the same blocks) is grouped fully.
+ *   group_starts    host, room for num_seqs + 1 entries
+ *   prefix_lens     host, room for num_seqs entries
+ *   num_groups      out: groups written
+ *   max_group_size  out: the largest group with a prefix (0 if none)
+ */
+int pkv_prefix_groups(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t min_prefix_tokens,
+                      int32_t *group_starts, int32_t *prefix_lens, int32_t *num_groups,
+                      int32_t *max_group_size);
 
 /*
  * pkv_prefill_attn -- chunked causal prefill over the paged cache.  Prompt p

@@ -29,7 +29,8 @@ EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_by
             "pkv_status_string", "pkv_last_error",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
             "pkv_pool_fork", "pkv_pool_free_seq", "pkv_pool_block_tables", "pkv_pool_num_free",
-            "pkv_pool_refcount", "pkv_pool_seq_len", "pkv_copy_blocks"]
+            "pkv_pool_refcount", "pkv_pool_seq_len", "pkv_copy_blocks",
+            "pkv_decode_attn_prefix", "pkv_decode_prefix_workspace_bytes", "pkv_prefix_groups"]
 
 
 class PkvError(RuntimeError):
@@ -121,6 +122,14 @@ def load(path: str = LIB_PATH):
                                    ctypes.c_float, _P, _P, _SZ, _P]
     lib.pkv_mixed_workspace_bytes.restype = _SZ
     lib.pkv_mixed_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
+    lib.pkv_decode_attn_prefix.restype = ctypes.c_int
+    lib.pkv_decode_attn_prefix.argtypes = [_P, PkvCache, _P, _I32, _P, _I32, _I32, _I32,
+                                           ctypes.c_float, _P, _P, _I32, _I32, _P, _P, _SZ, _I32,
+                                           _P]
+    lib.pkv_decode_prefix_workspace_bytes.restype = _SZ
+    lib.pkv_decode_prefix_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32]
+    lib.pkv_prefix_groups.restype = ctypes.c_int
+    lib.pkv_prefix_groups.argtypes = [_P, _I32, _P, _I32, _I32, _P, _P, _P, _P]
     lib.pkv_kv_bytes.restype = ctypes.c_uint64
     lib.pkv_kv_bytes.argtypes = [_I32, _I32, _I32, _I64, _I32]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -420,6 +429,79 @@ def pkv_mixed_attn(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens,
                               int(max_new_len), int(max_context_len), hq, float(scale),
                               out.data_ptr(), ws_ptr, ws_bytes, _stream(q, stream)),
            "pkv_mixed_attn")
+    return out
+
+
+def pkv_decode_prefix_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                      head_dim: int, max_context_len: int,
+                                      partition_tokens: int = 0) -> int:
+    return int(load().pkv_decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                        head_dim, max_context_len,
+                                                        partition_tokens))
+
+
+def pkv_prefix_groups(block_tables, context_lens, min_prefix_tokens: int = 16):
+    """Groups of consecutive sequences that share leading blocks, from host
+    (numpy int32) block tables [S][max_blocks] and context lengths [S]:
+    returns (group_starts [G+1], prefix_lens [G], max_group_size)."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.ndim != 2 or ctx.ndim != 1 or bt.shape[0] != ctx.shape[0]:
+        raise ValueError(f"block_tables {bt.shape} / context_lens {ctx.shape}")
+    s = ctx.shape[0]
+    starts = np.zeros(s + 1, dtype=np.int32)
+    plens = np.zeros(max(s, 1), dtype=np.int32)
+    ng, mg = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(load().pkv_prefix_groups(_np_ptr(bt), bt.shape[1], _np_ptr(ctx), s,
+                                    int(min_prefix_tokens), _np_ptr(starts), _np_ptr(plens),
+                                    ctypes.byref(ng), ctypes.byref(mg)), "pkv_prefix_groups")
+    return starts[: ng.value + 1].copy(), plens[: ng.value].copy(), mg.value
+
+
+def pkv_decode_attn_prefix(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                           group_starts, prefix_lens, max_group_size: int,
+                           max_context_len: Optional[int] = None, workspace=None,
+                           partition_tokens: int = 0, stream=None):
+    """pkv_decode_attn for a batch whose consecutive-sequence groups share
+    prefix blocks: group_starts [G+1] and prefix_lens [G] are int32 device
+    tensors (see pkv_prefix_groups), ``max_group_size`` a host int bounding
+    the sizes of groups with a prefix; other tensors as for pkv_decode_attn.
+    ``workspace``: uint8 device tensor, allocated here when None."""
+    import torch
+
+    lib = load()
+    cache = _cache(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(group_starts, "group_starts", torch.int32, 1)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1)
+    s, hq, d = q.shape
+    if tuple(out.shape) != (s, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables / context_lens do not match q's sequence count")
+    ng = prefix_lens.shape[0]
+    if group_starts.shape[0] != ng + 1:
+        raise ValueError(f"group_starts has {group_starts.shape[0]} entries, {ng + 1} expected")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * cache.block_size
+    if workspace is None:
+        need = pkv_decode_prefix_workspace_bytes(s, hq, cache.num_kv_heads, d,
+                                                 int(max_context_len), int(partition_tokens))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib.pkv_decode_attn_prefix(q.data_ptr(), cache, block_tables.data_ptr(), max_blocks,
+                                      context_lens.data_ptr(), s, int(max_context_len), hq,
+                                      float(scale), group_starts.data_ptr(),
+                                      prefix_lens.data_ptr(), ng, int(max_group_size),
+                                      out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      int(partition_tokens), _stream(q, stream)),
+           "pkv_decode_attn_prefix")
     return out
 
 

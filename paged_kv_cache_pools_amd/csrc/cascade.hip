@@ -1,0 +1,307 @@
+// cascade.hip -- decode attention for a batch whose sequences share prompt
+// prefixes through identical physical blocks.
+//
+// Requests that share a system prompt point their block tables at the same
+// physical blocks, so the prefix is stored once ("Nano-vLLM engine
+// deep-dive", section 2.2; "LLM basics primer" part 4, sections 17.6-17.7).
+// Plain decode still reads those blocks once per sequence.  Here a group's
+// decode queries attend to its shared prefix together, reading it once: for a
+// group of n sequences and one KV head, the n x G query rows against the
+// prefix keys form a small matrix product, run as the MFMA query tile of
+// prefill_tile.h in its cross-attention mode (no causal mask: the prefix
+// precedes every query).  Each sequence's own tail -- its tokens after the
+// prefix -- runs as split-KV decode units (decode_wave.h).  Both write
+// unnormalised partial results (O, m, l) into one workspace row per
+// (sequence, query head), and a second launch merges them:
+//   out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p,
+// the merge of split-KV decode, so the result is the sequence's attention
+// over its whole context up to fp32 rounding.
+//
+// Groups are ranges of consecutive sequences: group g is sequences
+// group_starts[g] .. group_starts[g + 1] - 1, sharing their first
+// prefix_lens[g] tokens (whole blocks); a sequence outside every group, or in
+// a group of prefix 0, is all tail.
+//
+// Workspace row of (sequence s, query head h), slots = max_parts + kMaxSegments:
+// slots 0 .. max_parts - 1 hold the tail partitions (partition_tokens tokens
+// each, counted from the prefix end), slots max_parts .. the prefix segments
+// (the prefix tile splits its keys into up to kMaxSegments ranges of at least
+// 512 keys).  Which slots are written follows from the context length and the
+// group's prefix alone, so the merge recomputes it.
+//
+// Dispatch order: all prefix tiles first, then the tail workgroups.  The
+// dispatcher hands an XCD's workgroups to its compute units breadth first, so
+// as long as there are at most 256 tiles no compute unit runs two of them.
+// (Alternating the kinds in short runs instead aliases with the dispatcher's
+// walk over the shader engines and piles the tiles onto half of them --
+// measured.)
+#include "decode_wave.h"
+#include "prefill_tile.h"
+
+namespace pkv {
+
+namespace {
+
+struct GroupView {
+    int begin, end, prefix;  // sequences [begin, end), shared prefix tokens (0 for none)
+};
+
+// Group g with its range clamped to [0, num_seqs] and its prefix to whole
+// blocks within ctx_cap.
+__device__ __forceinline__ GroupView group_view(const int32_t *__restrict__ group_starts,
+                                                const int32_t *__restrict__ prefix_lens, int g,
+                                                int num_seqs, int ctx_cap) {
+    GroupView v;
+    v.begin = min(max(group_starts[g], 0), num_seqs);
+    v.end = min(max(group_starts[g + 1], v.begin), num_seqs);
+    v.prefix = min(max(prefix_lens[g], 0), ctx_cap) / kBlockTokens * kBlockTokens;
+    return v;
+}
+
+// The group holding sequence s (the last g with group_starts[g] <= s, by
+// binary search, checked against the group's end), or a view of prefix 0
+// when no group does.  Per thread.
+__device__ __forceinline__ GroupView group_of(const int32_t *__restrict__ group_starts,
+                                              const int32_t *__restrict__ prefix_lens,
+                                              int num_groups, int num_seqs, int ctx_cap, int s) {
+    if (num_groups <= 0) return GroupView{s, s + 1, 0};
+    int lo = 0, hi = num_groups - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (group_starts[mid] <= s)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    GroupView v = group_view(group_starts, prefix_lens, lo, num_seqs, ctx_cap);
+    if (s < v.begin || s >= v.end) v = GroupView{s, s + 1, 0};
+    return v;
+}
+
+// Partitions of a tail of `tail` tokens.
+__device__ __forceinline__ int tail_parts(int tail, int partition_tokens) {
+    return tail > 0 ? (tail + partition_tokens - 1) / partition_tokens : 0;
+}
+
+constexpr int kTailWaves = 4;  // partitions of a tail workgroup (one per wave)
+
+// Prefix tiles split their keys into segments of at least this many 64-key
+// chunks (512 keys), up to kMaxSegments.
+constexpr int kPrefixSegmentChunks = 8;
+
+// Key segments of a prefix of `keys` tokens (0 without one): the split the
+// prefix tile makes of its 64-key chunks.
+__device__ __forceinline__ int prefix_segments(int keys) {
+    return keys > 0 ? prefill_segments((keys + 63) / 64, kMaxSegments, kPrefixSegmentChunks) : 0;
+}
+
+}  // namespace
+
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cascade_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
+    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    const int32_t *__restrict__ group_starts, const int32_t *__restrict__ prefix_lens,
+    int32_t num_groups, int32_t prefix_qblocks, int32_t partition_tokens, int32_t max_parts,
+    float scale_log2, float *__restrict__ ws_out, float *__restrict__ ws_ml) {
+    using Geo = PrefillGeom<D, G>;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Geo::BUF];
+    const int slots = max_parts + kMaxSegments;
+    const int ctx_cap = min(max_context_len, max_blocks_per_seq * kBlockTokens);
+    const int pf_units = num_groups * prefix_qblocks * kMaxSegments * num_kv_heads;
+
+    if ((int)blockIdx.x < pf_units) {
+        // a prefix tile: idx = ((g * prefix_qblocks + qb) * kMaxSegments + seg) * H_kv + kvh
+        int idx = blockIdx.x;
+        const int kvh = idx % num_kv_heads;
+        idx /= num_kv_heads;
+        SplitSlot split;
+        split.seg = idx % kMaxSegments;
+        split.slots = kMaxSegments;
+        split.min_chunks = kPrefixSegmentChunks;
+        split.ws_out = ws_out;
+        split.ws_ml = ws_ml;
+        split.ws_slots = slots;
+        split.slot0 = max_parts;
+        idx /= kMaxSegments;
+        const int qb = idx % prefix_qblocks;
+        const int g = idx / prefix_qblocks;
+        const GroupView v = group_view(group_starts, prefix_lens, g, num_seqs, ctx_cap);
+        CrossGeom cross;
+        cross.row0 = v.begin;
+        cross.n = v.end - v.begin;
+        cross.keys = v.prefix;
+        cross.bt = block_tables + (size_t)v.begin * max_blocks_per_seq;
+        prefill_unit<D, G, true, true>(q, k_cache, v_cache, block_tables, nullptr, nullptr,
+                                       max_blocks_per_seq, max_context_len, num_blocks,
+                                       num_q_heads, num_kv_heads, scale_log2, nullptr, 0, qb, kvh,
+                                       lds, split, cross);
+        return;
+    }
+
+    // a tail workgroup: one wave per partition of partition_tokens tokens of
+    // sequence s's tail, for KV head kvh; the 4 waves take 4 consecutive
+    // partitions.  The KV head is innermost, then the sequence, then the
+    // partition group, so the 8 XCDs (dealt workgroups round-robin) see the
+    // same work, and the late, mostly empty partition groups come last.
+    const int idx = blockIdx.x - pf_units;
+    const int kvh = idx % num_kv_heads;
+    const int s = (idx / num_kv_heads) % num_seqs;
+    const int part = (idx / (num_kv_heads * num_seqs)) * kTailWaves + wave_id_uniform();
+    const int ctx = min(context_lens[s], ctx_cap);
+    if (part * partition_tokens >= ctx) return;  // uniform: empty however long the prefix
+    const GroupView v = group_of(group_starts, prefix_lens, num_groups, num_seqs, ctx_cap, s);
+    const int t_begin = v.prefix + part * partition_tokens;
+    if (t_begin >= ctx) return;
+    const int t_end = min(t_begin + partition_tokens, ctx);
+    constexpr int LPR = D / 8, TPL = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int row = lane / LPR;
+    const int c = lane % LPR;
+    float acc[G][8], mg[G], lg[G];
+    wave_attend<D, G, false>(q, k_cache, v_cache, nullptr, nullptr,
+                             block_tables + (size_t)s * max_blocks_per_seq, num_blocks, num_q_heads,
+                             num_kv_heads, scale_log2, s, kvh, t_begin, t_end, NewToken{}, Rope{},
+                             acc, mg, lg);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (g % TPL == row) {
+            const size_t r = ((size_t)s * num_q_heads + kvh * G + g) * slots + part;
+            float4 *dst = reinterpret_cast<float4 *>(ws_out + r * D + c * 8);
+            dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+            dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
+            if (c == 0) {
+                ws_ml[r * 2 + 0] = mg[g];
+                ws_ml[r * 2 + 1] = lg[g];
+            }
+        }
+    }
+}
+
+// Merge the partial results of every (sequence, query head): one wavefront
+// each, its tail partitions then its prefix segments, in slot order.  A row
+// whose inputs break the call's preconditions -- a prefix longer than the
+// sequence's context, or a group member past the prefix_rows the launch's
+// tiles cover -- is written as NaN.
+template <int D>
+__global__ __launch_bounds__(256) void cascade_reduce_kernel(
+    const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
+    int32_t num_seqs, int32_t num_q_heads, const int32_t *__restrict__ group_starts,
+    const int32_t *__restrict__ prefix_lens, int32_t num_groups, int32_t prefix_rows,
+    int32_t partition_tokens, int32_t max_parts, const float *__restrict__ ws_out,
+    const float *__restrict__ ws_ml, uint16_t *__restrict__ out) {
+    constexpr int E = D / 64;  // elements per lane
+    const int lane = threadIdx.x & 63;
+    const int row_id = blockIdx.x * (blockDim.x >> 6) + wave_id_uniform();
+    if (row_id >= num_seqs * num_q_heads) return;
+    const int s = row_id / num_q_heads;
+    const int slots = max_parts + kMaxSegments;
+    const int ctx_cap = min(max_context_len, max_blocks_per_seq * kBlockTokens);
+    const int ctx = min(context_lens[s], ctx_cap);
+    const GroupView v = group_of(group_starts, prefix_lens, num_groups, num_seqs, ctx_cap, s);
+    const int prefix = v.prefix;
+    uint16_t *o = out + (size_t)row_id * D + lane * E;
+    if (prefix > 0 && (prefix > ctx || s - v.begin >= prefix_rows)) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = 0x7fc0;  // bf16 NaN: undefined for these inputs
+        return;
+    }
+    if (ctx <= 0) {  // an empty context is 0
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = 0;
+        return;
+    }
+    const int nparts = tail_parts(ctx - prefix, partition_tokens);
+    const int n = nparts + prefix_segments(prefix);
+    auto slot_of = [&](int i) { return i < nparts ? i : max_parts + (i - nparts); };
+
+    // online over batches of 8 slots: every load of a batch is issued before
+    // the first is used; the running maximum M rescales what came before
+    const float *ml = ws_ml + (size_t)row_id * slots * 2;
+    const float *po = ws_out + (size_t)row_id * slots * D + lane * E;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    float M = -INFINITY, L = 0.f;
+    for (int i0 = 0; i0 < n; i0 += 8) {
+        float m8[8], l8[8], v8[8][E];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int sl = slot_of(min(i0 + j, n - 1));
+            m8[j] = i0 + j < n ? ml[sl * 2] : -INFINITY;
+            l8[j] = ml[sl * 2 + 1];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v8[j][e] = po[(size_t)sl * D + e];
+        }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, m8[j]);
+        const float r = (Mn == -INFINITY) ? 1.f : fast_exp2(M - Mn);
+        L *= r;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float w = (m8[j] == -INFINITY) ? 0.f : fast_exp2(m8[j] - Mn);
+            L = fmaf(w, l8[j], L);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(w, v8[j][e], acc[e]);
+        }
+        M = Mn;
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = (uint16_t)f32_to_bf16_rne(acc[e] * inv);
+}
+
+template <int D, int G>
+static hipError_t launch_cascade_t(const CascadeArgs &a, hipStream_t stream) {
+    using Geo = PrefillGeom<D, G>;
+    const int prefix_qblocks = cascade_prefix_qblocks(a.max_group_size, G);
+    const int64_t pf_units = (int64_t)a.num_groups * prefix_qblocks * kMaxSegments * a.num_kv_heads;
+    const int64_t tail_units =
+        (int64_t)(a.max_parts + kTailWaves - 1) / kTailWaves * a.num_seqs * a.num_kv_heads;
+    const float scale_log2 = a.scale * 1.4426950408889634f;
+    hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)(pf_units + tail_units)),
+                       dim3(Geo::THREADS), 0, stream, (const uint16_t *)a.q,
+                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.block_tables,
+                       a.context_lens, a.max_blocks_per_seq, a.max_context_len, a.num_blocks,
+                       a.num_seqs, a.num_q_heads, a.num_kv_heads, a.group_starts, a.prefix_lens,
+                       a.num_groups, prefix_qblocks, a.partition_tokens, a.max_parts, scale_log2,
+                       a.ws_out, a.ws_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rows = a.num_seqs * a.num_q_heads;
+    hipLaunchKernelGGL((cascade_reduce_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+                       a.context_lens, a.max_blocks_per_seq, a.max_context_len, a.num_seqs,
+                       a.num_q_heads, a.group_starts, a.prefix_lens, a.num_groups,
+                       prefix_qblocks * Geo::TWG, a.partition_tokens, a.max_parts, a.ws_out,
+                       a.ws_ml, (uint16_t *)a.out);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_cascade_d(const CascadeArgs &a, hipStream_t stream) {
+    switch (a.num_q_heads / a.num_kv_heads) {
+        case 1: return launch_cascade_t<D, 1>(a, stream);
+        case 2: return launch_cascade_t<D, 2>(a, stream);
+        case 4: return launch_cascade_t<D, 4>(a, stream);
+        case 8: return launch_cascade_t<D, 8>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_cascade(const CascadeArgs &a, hipStream_t stream) {
+    if (a.num_seqs == 0) return hipSuccess;
+    return a.head_dim == 64 ? launch_cascade_d<64>(a, stream) : launch_cascade_d<128>(a, stream);
+}
+
+// Query blocks of the prefix tiles: a tile holds 4 waves x 32 / G sequences.
+int cascade_prefix_qblocks(int32_t max_group_size, int32_t group) {
+    const int twg = 4 * (32 / group);
+    return max_group_size <= 0 ? 0 : (max_group_size + twg - 1) / twg;
+}
+
+}  // namespace pkv

@@ -106,10 +106,12 @@ int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 // Partition length for split-KV decode: aim for about 16 wavefronts per CU
 // (256 CUs) if every sequence had the longest context; never shorter than 4
 // blocks (the fixed cost of a unit is a q load and a cross-row merge) and
-// never longer than 64 blocks (so a long-context straggler is split enough).
+// never longer than 32 blocks (so a long-context straggler is split enough:
+// measured on 256 sequences of lognormal length, 512 tokens ran 10-12%
+// faster than 1024).
 int32_t partition_for(int64_t units, int32_t max_context_len) {
     constexpr int64_t kTargetWaves = 4096;
-    constexpr int32_t kMin = 64, kMax = 1024;
+    constexpr int32_t kMin = 64, kMax = 512;
     if (max_context_len <= 0) return kMin;
     int64_t want = ((int64_t)max_context_len * units + kTargetWaves - 1) / kTargetWaves;
     int32_t p = kMin;
@@ -123,15 +125,20 @@ int32_t partition_for(int64_t units, int32_t max_context_len) {
 // workgroup per unit is not a straggler; it then gives each unit enough waves
 // for kTargetWaves in all (1024 = four per CU for bf16; the FP8 path, with
 // twice the arithmetic per byte, runs best at 2048 = two per SIMD), at least
-// one block per wave.
+// one block per wave.  A wave of the longest context must not walk more than
+// kMaxWaveTokens: with many units of mixed lengths the choice would be one
+// wave per unit, and the longest sequence's lone wave the whole launch
+// (measured: 256 lognormal contexts up to 6565 tokens, 361 us single-pass
+// against 175 us split).
 int32_t fused_waves_for(int64_t units, int32_t max_context_len, int64_t kTargetWaves) {
     constexpr int64_t kMinUnits = 128;
-    constexpr int32_t kMaxContext = 8192, kMaxWaves = 8;
+    constexpr int32_t kMaxContext = 8192, kMaxWaves = 8, kMaxWaveTokens = 1024;
     if (units < kMinUnits || max_context_len <= 0 || max_context_len > kMaxContext) return 0;
     int32_t w = (int32_t)((kTargetWaves + units - 1) / units);
     w = w < 1 ? 1 : (w > kMaxWaves ? kMaxWaves : w);
     const int32_t blocks = (max_context_len + kBlock - 1) / kBlock;
-    return w > blocks ? blocks : w;
+    w = w > blocks ? blocks : w;
+    return ceil_div(max_context_len, w) > kMaxWaveTokens ? 0 : w;
 }
 
 }  // namespace
@@ -569,6 +576,177 @@ int pkv_prefill_attn(const void *q, pkv_cache cache, const int32_t *block_tables
     a.scale = scale;
     a.out = out;
     return hip_status(pkv::launch_prefill(a, stream), "pkv_prefill_attn launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Tail partition length of pkv_decode_attn_prefix (one wave's work for one
+// KV head): the split-KV choice for the longest context, at most 512 tokens
+// (a tail is usually much shorter than its context).
+int32_t prefix_partition_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+    return std::min<int32_t>(512, partition_for((int64_t)num_seqs * num_kv_heads, max_context_len));
+}
+
+int32_t prefix_parts(int32_t max_context_len, int32_t p) {
+    return max_context_len > 0 ? ceil_div(max_context_len, p) : 0;
+}
+
+// Leading block-table entries rows a and b share, among the first `limit`.
+int32_t common_blocks(const int32_t *a, const int32_t *b, int32_t limit) {
+    int32_t i = 0;
+    while (i < limit && a[i] == b[i]) ++i;
+    return i;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || partition_tokens < 0 || partition_tokens % kBlock != 0)
+        return 0;
+    const int32_t p = partition_tokens
+                          ? partition_tokens
+                          : prefix_partition_for(num_seqs, num_kv_heads, max_context_len);
+    const int32_t parts = prefix_parts(max_context_len, p);
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)(parts + pkv::kMaxSegments);
+    return rows * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                           float scale, const int32_t *group_starts, const int32_t *prefix_lens,
+                           int32_t num_groups, int32_t max_group_size, void *out, void *workspace,
+                           size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
+    if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || num_groups < 0 ||
+        max_group_size < 0)
+        return fail(PKV_ERR_SHAPE,
+                    "num_seqs %d, max_context_len %d, max_blocks_per_seq %d, num_groups %d, "
+                    "max_group_size %d",
+                    num_seqs, max_context_len, max_blocks_per_seq, num_groups, max_group_size);
+    if (num_seqs == 0) return ok();
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+        return fail(PKV_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq %d x 16",
+                    max_context_len, max_blocks_per_seq);
+    if (max_context_len > 0 && cache.num_blocks == 0)
+        return fail(PKV_ERR_SHAPE, "an empty pool cannot hold a context of %d tokens",
+                    max_context_len);
+    if (max_group_size > num_seqs)
+        return fail(PKV_ERR_SHAPE, "max_group_size %d exceeds num_seqs %d", max_group_size,
+                    num_seqs);
+    if (!q || !out || !context_lens || (max_blocks_per_seq > 0 && !block_tables))
+        return fail(PKV_ERR_NULL, "q, out, context_lens or block_tables is null");
+    if (num_groups > 0 && (!group_starts || !prefix_lens))
+        return fail(PKV_ERR_NULL, "group_starts or prefix_lens is null");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
+    if (partition_tokens < 0 || partition_tokens % kBlock != 0)
+        return fail(PKV_ERR_SHAPE, "partition_tokens %d is neither 0 nor a positive multiple of 16",
+                    partition_tokens);
+    const int32_t p = partition_tokens
+                          ? partition_tokens
+                          : prefix_partition_for(num_seqs, cache.num_kv_heads, max_context_len);
+    const int32_t parts = prefix_parts(max_context_len, p);
+    const size_t need = pkv_decode_prefix_workspace_bytes(
+        num_seqs, num_q_heads, cache.num_kv_heads, cache.head_dim, max_context_len, p);
+    if (!workspace || workspace_bytes < need)
+        return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+    // the grid: tail workgroups (4 partitions each) plus prefix tiles (a tile
+    // holds at least 16 sequences, group size 8); 256 threads per workgroup
+    const int64_t qblocks = ((int64_t)max_group_size + 15) / 16;
+    const int64_t wgs = ((int64_t)parts + 3) / 4 * num_seqs * cache.num_kv_heads +
+                        (int64_t)num_groups * qblocks * pkv::kMaxSegments * cache.num_kv_heads;
+    if (wgs >= (int64_t)1 << 24 || (int64_t)num_seqs * num_q_heads >= (int64_t)1 << 26)
+        return fail(PKV_ERR_SHAPE, "%d sequences of up to %d tokens in %d groups exceed one launch's grid",
+                    num_seqs, max_context_len, num_groups);
+    pkv::CascadeArgs a{};
+    a.q = q;
+    a.k_cache = cache.k;
+    a.v_cache = cache.v;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_context_len = max_context_len;
+    a.num_blocks = cache.num_blocks;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache.num_kv_heads;
+    a.head_dim = cache.head_dim;
+    a.group_starts = group_starts;
+    a.prefix_lens = prefix_lens;
+    a.num_groups = num_groups;
+    a.max_group_size = max_group_size;
+    a.partition_tokens = p;
+    a.max_parts = parts;
+    a.scale = scale;
+    a.out = out;
+    float *ws = static_cast<float *>(workspace);
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)(parts + pkv::kMaxSegments);
+    a.ws_out = ws;
+    a.ws_ml = ws + rows * cache.head_dim;
+    return hip_status(pkv::launch_cascade(a, stream), "pkv_decode_attn_prefix launch");
+}
+
+int pkv_prefix_groups(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t min_prefix_tokens,
+                      int32_t *group_starts, int32_t *prefix_lens, int32_t *num_groups,
+                      int32_t *max_group_size) {
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || min_prefix_tokens < 0)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d, max_blocks_per_seq %d, min_prefix_tokens %d",
+                    num_seqs, max_blocks_per_seq, min_prefix_tokens);
+    if (!group_starts || !prefix_lens || !num_groups || !max_group_size ||
+        (num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables))))
+        return fail(PKV_ERR_NULL, "a required pointer is null");
+    // whole blocks of a sequence's context that a prefix may cover
+    auto full_blocks = [&](int32_t s) {
+        const int32_t c = context_lens[s] < 0 ? 0 : context_lens[s];
+        return std::min(c / kBlock, max_blocks_per_seq);
+    };
+    auto row = [&](int32_t s) { return block_tables + (size_t)s * max_blocks_per_seq; };
+    const int32_t min_blocks = std::max(1, (min_prefix_tokens + kBlock - 1) / kBlock);
+    int32_t g = 0, biggest = 0;
+    bool open_plain = false;  // the last group written shares nothing and may grow
+    group_starts[0] = 0;
+    for (int32_t s = 0; s < num_seqs;) {
+        // the run starting at s: its prefix is what s and s + 1 share; each
+        // later sequence joins while it shares at least that much with s
+        int32_t e = s + 1, common = 0;
+        if (e < num_seqs) {
+            common = common_blocks(row(s), row(e), std::min(full_blocks(s), full_blocks(e)));
+            if (common >= min_blocks) {
+                ++e;
+                while (e < num_seqs &&
+                       common_blocks(row(s), row(e), std::min(common, full_blocks(e))) == common)
+                    ++e;
+            }
+        }
+        if (e - s >= 2) {
+            prefix_lens[g] = common * kBlock;
+            group_starts[++g] = e;
+            biggest = std::max(biggest, e - s);
+            open_plain = false;
+        } else if (open_plain) {
+            group_starts[g] = e;  // extend the open group of sequences that share nothing
+        } else {
+            prefix_lens[g] = 0;
+            group_starts[++g] = e;
+            open_plain = true;
+        }
+        s = e;
+    }
+    *num_groups = g;
+    *max_group_size = biggest;
+    return ok();
 }
 
 }  // extern "C"

@@ -92,6 +92,28 @@ hipError_t launch_mixed(const MixedArgs &a, hipStream_t stream);
 int mixed_query_blocks(int32_t max_new_len, int32_t group);
 size_t mixed_partial_bytes(int32_t head_dim);
 
+// Decode with shared prefixes (cascade.hip): group g = sequences
+// group_starts[g] .. group_starts[g + 1] - 1 sharing their first
+// prefix_lens[g] tokens; the tails run as partitions of partition_tokens.
+struct CascadeArgs {
+    const void *q;
+    const void *k_cache, *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    int32_t max_blocks_per_seq, num_seqs, max_context_len;
+    int32_t num_blocks, num_q_heads, num_kv_heads, head_dim;
+    const int32_t *group_starts;  // device [num_groups + 1]
+    const int32_t *prefix_lens;   // device [num_groups]
+    int32_t num_groups, max_group_size;
+    int32_t partition_tokens, max_parts;
+    float scale;
+    void *out;
+    float *ws_out;  // [num_seqs][num_q_heads][max_parts + kMaxSegments][head_dim]
+    float *ws_ml;   // [num_seqs][num_q_heads][max_parts + kMaxSegments][2]
+};
+hipError_t launch_cascade(const CascadeArgs &a, hipStream_t stream);
+int cascade_prefix_qblocks(int32_t max_group_size, int32_t group);
+
 // Whole-block copies (copy.hip).
 constexpr int kMaxCopyPools = 64;  // pool pointers per launch (kernel arguments)
 struct CopyArgs {

@@ -46,6 +46,7 @@
 #pragma once
 
 #include <math.h>
+#include <stdint.h>
 
 #include <type_traits>
 
@@ -155,16 +156,31 @@ constexpr int prefill_partial_floats() {
 constexpr int kMinSegmentChunks = 8;
 
 // Where a split unit keeps its partial results: `slots` segments' partials
-// (prefill_partial_floats each).
+// (prefill_partial_floats each), or -- when ws_out is set -- one row per
+// (query row, head) of a split-KV workspace, slot slot0 + seg of ws_slots:
+// unnormalised O in ws_out [rows][heads][ws_slots][D], (m, l) in ws_ml
+// [rows][heads][ws_slots][2], written even when the unit does not split.
 struct SplitSlot {
     float *partials = nullptr;
     int seg = 0;    // this workgroup's segment
     int slots = 1;  // most segments the unit may use
+    int min_chunks = kMinSegmentChunks;  // fewest key chunks of a segment
+    float *ws_out = nullptr, *ws_ml = nullptr;
+    int ws_slots = 0, slot0 = 0;
+};
+
+// Cross attention over a prefix that several sequences share: n query tokens
+// at q rows row0 .. row0 + n - 1 attend to every key in [0, keys) of the
+// block-table row bt, with no causal mask (the prefix precedes all of them).
+struct CrossGeom {
+    int row0 = 0, n = 0, keys = 0;
+    const int32_t *bt = nullptr;
 };
 
 // Segments a split unit of nchunks key chunks uses (0 .. slots).
-__device__ __forceinline__ int prefill_segments(int nchunks, int slots) {
-    return max(1, min(slots, nchunks / kMinSegmentChunks));
+__device__ __forceinline__ int prefill_segments(int nchunks, int slots,
+                                                int min_chunks = kMinSegmentChunks) {
+    return max(1, min(slots, nchunks / min_chunks));
 }
 
 // One work unit of chunked prefill -- prompt p, KV head kvh, query block qb
@@ -172,19 +188,22 @@ __device__ __forceinline__ int prefill_segments(int nchunks, int slots) {
 // workgroup of 4 waves (every thread must call).  `lds` holds 2 * BUF bytes.
 //
 // SPLIT: the unit's key chunks are divided among up to split.slots
-// workgroups (segments of at least kMinSegmentChunks chunks, evenly; a
+// workgroups (segments of at least split.min_chunks chunks, evenly; a
 // workgroup whose segment is empty returns at once).  When the unit has more
 // than one segment, each writes its unnormalised (O, m, l) to its slot and
 // prefill_merge, run by a later launch, combines them; a unit of one segment
 // writes its output directly.
-template <int D, int G, bool SPLIT = false>
+//
+// CROSS: the unit's queries and keys come from `cross` instead of prompt p
+// (p, cu_new_lens and context_lens are not read).
+template <int D, int G, bool SPLIT = false, bool CROSS = false>
 __device__ __forceinline__ void prefill_unit(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ cu_new_lens, const int32_t *__restrict__ context_lens,
     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks, int32_t num_q_heads,
     int32_t num_kv_heads, float scale_log2, uint16_t *__restrict__ out, int p, int qb, int kvh,
-    unsigned char *lds, const SplitSlot &split = SplitSlot{}) {
+    unsigned char *lds, const SplitSlot &split = SplitSlot{}, const CrossGeom &cross = CrossGeom{}) {
     using Geo = PrefillGeom<D, G>;
     constexpr int TW = Geo::TW, TWG = Geo::TWG, KC = Geo::KC, KSTEPS = Geo::KSTEPS, NT = Geo::NT;
     constexpr int MT = Geo::MT, KROW = Geo::KROW, VROW = Geo::VROW, CPR = Geo::CPR;
@@ -197,18 +216,31 @@ __device__ __forceinline__ void prefill_unit(
     const int a = lane >> 4;    // 16-lane group
     const int col = lane & 15;  // column within an N-tile
 
-    const int row0 = cu_new_lens[p];
-    int ctx = context_lens[p];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
-    const int n = min(cu_new_lens[p + 1] - row0, ctx);
-    const int c = ctx - n;
+    int row0, ctx, n, c;
+    const int32_t *bt;
+    if constexpr (CROSS) {
+        row0 = cross.row0;
+        n = cross.n;
+        ctx = cross.keys;
+        c = 0;
+        bt = cross.bt;
+        if (ctx <= 0) return;  // uniform: no prefix
+    } else {
+        row0 = cu_new_lens[p];
+        ctx = context_lens[p];
+        ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+        n = min(cu_new_lens[p + 1] - row0, ctx);
+        c = ctx - n;
+        bt = block_tables + (size_t)p * max_blocks_per_seq;
+    }
     const int T0 = qb * TWG;
     if (n <= 0 || T0 >= n) return;  // uniform over the workgroup
-    const int kend = c + min(T0 + TWG, n);  // keys [0, kend) are visible to someone here
+    // keys [0, kend) are visible to some query here
+    const int kend = CROSS ? ctx : c + min(T0 + TWG, n);
     const int nchunks = (kend + KC - 1) / KC;
     int j_begin = 0, j_end = nchunks, nseg = 1;
     if constexpr (SPLIT) {
-        nseg = prefill_segments(nchunks, split.slots);
+        nseg = prefill_segments(nchunks, split.slots, split.min_chunks);
         if (split.seg >= nseg) return;  // uniform: no segment for this workgroup
         j_begin = split.seg * nchunks / nseg;
         j_end = (split.seg + 1) * nchunks / nseg;
@@ -230,7 +262,7 @@ __device__ __forceinline__ void prefill_unit(
         const int tok = T0 + w * TW + j / G;
         const int h = kvh * G + j % G;
         live[nt] = tok < n;
-        pos[nt] = c + tok;
+        pos[nt] = CROSS ? INT32_MAX : c + tok;  // cross attention: every key is before the query
         const uint4 *src = reinterpret_cast<const uint4 *>(
             q + ((size_t)(row0 + min(tok, n - 1)) * num_q_heads + h) * D);
 #pragma unroll
@@ -255,11 +287,10 @@ __device__ __forceinline__ void prefill_unit(
     }
     // positions of this wave's first and last live token: chunks wholly below
     // the first need no causal mask, chunks wholly above the last are skipped
-    const int wave_min_pos = c + T0 + w * TW;
-    const int wave_max_pos = c + min(T0 + (w + 1) * TW, n) - 1;
+    const int wave_min_pos = CROSS ? INT32_MAX : c + T0 + w * TW;
+    const int wave_max_pos = CROSS ? ctx - 1 : c + min(T0 + (w + 1) * TW, n) - 1;
     const bool wave_live = T0 + w * TW < n;
 
-    const int32_t *bt = block_tables + (size_t)p * max_blocks_per_seq;
     const size_t tile = (size_t)kBlockTokens * D;
 
     // ---- staging of one key chunk.  K goes global -> LDS directly (16-byte
@@ -514,6 +545,24 @@ __device__ __forceinline__ void prefill_unit(
     }
 
     if constexpr (SPLIT) {
+        if (split.ws_out != nullptr) {  // uniform: rows of a split-KV workspace
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (!live[nt]) continue;
+                const int j = nt * 16 + col;
+                const int tok = T0 + w * TW + j / G;
+                const size_t r = ((size_t)(row0 + tok) * num_q_heads + kvh * G + j % G) * split.ws_slots +
+                                 split.slot0 + split.seg;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    *reinterpret_cast<f32x4_t *>(split.ws_out + r * D + mt * 16 + a * 4) = o[mt][nt];
+                if (a == 0) {
+                    split.ws_ml[r * 2] = m[nt];
+                    split.ws_ml[r * 2 + 1] = lt[nt];
+                }
+            }
+            return;
+        }
         if (nseg > 1) {
             // publish this segment: o[mt][nt][r] is O^T[d = 16 mt + 4 a + r][column]
             constexpr int COLF = prefill_partial_col_floats(D);

@@ -58,11 +58,18 @@ def test_partition_heuristic(lib):
     # the 32 x 4096 GQA batch: 256 (seq, kv head) units -> single pass, 4 waves each
     assert B.pkv_decode_partition_tokens(32, 8, 4096) == -4
     # many units with long contexts, or few units: two-pass split-KV
-    assert B.pkv_decode_partition_tokens(256, 8, 32768) == 1024
+    assert B.pkv_decode_partition_tokens(256, 8, 32768) == 512
+    # many units whose longest context would leave one wave walking 6565
+    # tokens alone: two-pass split-KV, not single pass with one wave each
+    assert B.pkv_decode_partition_tokens(256, 8, 6565) > 0
+    # the 16-sequence MHA batch (512 units, up to 2048 tokens): 2 waves of 1024
+    assert B.pkv_decode_partition_tokens(16, 32, 2048) == -2
     for s, h, ctx in ((1, 1, 1), (2, 2, 37), (256, 8, 32768), (16, 32, 2048), (1, 1, 1 << 20),
-                      (32, 8, 4096), (64, 8, 16)):
+                      (32, 8, 4096), (64, 8, 16), (256, 8, 6565)):
         p = B.pkv_decode_partition_tokens(s, h, ctx)
-        assert (p % 16 == 0 and 64 <= p <= 1024) or (-8 <= p <= -1), (s, h, ctx, p)
+        assert (p % 16 == 0 and 64 <= p <= 512) or (-8 <= p <= -1), (s, h, ctx, p)
+        if p < 0:  # no wave walks more than 1024 tokens
+            assert -(-ctx // -p) <= 1024
         if p < 0:  # at least one block per wave
             assert -p <= -(-ctx // 16)
     assert B.pkv_decode_partition_tokens(-1, 8, 10) == 0
@@ -227,3 +234,36 @@ def test_fp8_partition_heuristic(lib):
         if p > 0:  # the P = 0 workspace bound covers the FP8 choice too
             assert B.pkv_decode_workspace_bytes(s, 4 * h, 128, ctx, p) <= \
                 B.pkv_decode_workspace_bytes(s, 4 * h, 128, ctx, 0)
+
+
+def test_prefix_decode_validation(lib):
+    # every call here fails before a launch
+    pd = lambda s=40, mc=37, mb=3, hq=4, c=None, q=FAKE, gs=FAKE, pl=FAKE, ng=2, mg=8, ws=FAKE, \
+        wsb=1 << 30, p=0: lib.pkv_decode_attn_prefix(
+            q, c or cache(), FAKE, mb, FAKE, s, mc, hq, ctypes.c_float(0.125), gs, pl, ng, mg, FAKE,
+            ws, wsb, p, None)
+    assert pd(s=-1) == 2 and pd(ng=-1) == 2 and pd(mg=-1) == 2
+    assert pd(mg=41) == 2                   # a group larger than the batch
+    assert pd(mc=80) == 2                   # beyond max_blocks * 16
+    assert pd(q=0) == 1 and pd(gs=0) == 1 and pd(pl=0) == 1
+    assert pd(q=FAKE + 8) == 4
+    assert pd(hq=6) == 3 and pd(c=cache(d=96)) == 3 and pd(c=cache(bs=32)) == 3
+    assert pd(p=24) == 2 and pd(p=-16) == 2  # partitions: 0 or a positive multiple of 16
+    assert pd(ws=0) == 5 and pd(wsb=64) == 5
+    assert pd(ws=FAKE + 4) == 4
+    assert B.pkv_last_error() != ""
+
+
+def test_prefix_decode_workspace_sizing(lib):
+    # rows x (tail partitions + 8 prefix segments) x (d + 2) floats
+    assert B.pkv_decode_prefix_workspace_bytes(256, 32, 8, 128, 32768, 512) == \
+        256 * 32 * (64 + 8) * 130 * 4
+    assert B.pkv_decode_prefix_workspace_bytes(3, 4, 2, 64, 0, 16) == 3 * 4 * 8 * 66 * 4
+    assert B.pkv_decode_prefix_workspace_bytes(3, 1, 2, 64, 33, 16) == 3 * 1 * (3 + 8) * 66 * 4
+    # automatic partitions: the split-KV choice, at most 512 tokens
+    assert B.pkv_decode_prefix_workspace_bytes(256, 32, 8, 128, 32768, 0) == \
+        256 * 32 * (64 + 8) * 130 * 4
+    assert B.pkv_decode_prefix_workspace_bytes(1, 32, 8, 128, 32768, 0) == \
+        32 * (32768 // B.pkv_decode_partition_tokens(1, 8, 32768) + 8) * 130 * 4
+    assert B.pkv_decode_prefix_workspace_bytes(0, 32, 8, 128, 100, 0) == 0
+    assert B.pkv_decode_prefix_workspace_bytes(4, 32, 8, 128, 100, 24) == 0
