@@ -28,7 +28,15 @@
 // The decode and prefill lists are interleaved in groups of 8 workgroups
 // (decode, prefill, decode, ...) while both last, which keeps that alignment
 // and gives every XCD both kinds, so bandwidth-bound and compute-bound work
-// overlap on each.
+// overlap on each.  When the whole launch is resident at once (at most two
+// workgroups per compute unit) and the prefill units are split by key range
+// (so the decode units are the longest), the decode list goes first instead:
+// an XCD's dispatcher fills its compute units breadth first, walking its
+// shader engines in turn, so the period-2 interleave would put two decode
+// units on each compute unit of half the engines; decode first gives each
+// compute unit at most one (measured on 32 x 4096 decode + one split 64-token
+// chunk: 103 against 124-128 us).  Unsplit, the few long prefill units are
+// the longest, and the interleave serves them better (185 against 224 us).
 //
 // A prefill unit may run as several workgroups, each over a contiguous
 // segment of its key chunks (prefill_tile.h, SPLIT): a chunk of a prompt with
@@ -81,7 +89,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int dec_units = num_decode * num_kv_heads;
     const int pf_units = num_prefill * num_kv_heads * num_qblocks * seg_slots;  // workgroups
     const int unit = blockIdx.x;
-    const int m8 = min(dec_units, pf_units) / 8 * 8;  // units of each list interleaved
+    // when every workgroup of the launch is resident at once and the prefill
+    // units are split into short segments, the decode units -- then the
+    // longest -- go first: the dispatcher gives each compute unit one before
+    // any gets a second workgroup, so no decode unit shares a compute unit
+    // with another
+    const int m8 = (seg_slots > 1 && dec_units + pf_units <= kResidentWorkgroups)
+                       ? 0
+                       : min(dec_units, pf_units) / 8 * 8;  // units of each list interleaved
     bool is_decode;
     int idx;
     if (unit < 2 * m8) {

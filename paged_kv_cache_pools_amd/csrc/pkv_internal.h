@@ -81,6 +81,9 @@ constexpr int kMaxSegments = 8;
 // Mixed decode + prefill step (mixed.hip): sequences 0 .. num_decode-1 are
 // decode sequences; max_new_len bounds the others' new tokens.
 constexpr int kMixedWaves = 4;  // waves of a mixed-step workgroup (either kind)
+// Workgroups of 4 waves MI355X holds at once: 256 compute units, two each at
+// the mixed kernel's register and LDS use.
+constexpr int kResidentWorkgroups = 512;
 struct MixedArgs : PrefillArgs {
     int32_t num_decode;
     int32_t seg_slots = 1;       // workgroups a prefill unit may split into
