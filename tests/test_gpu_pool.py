@@ -81,6 +81,7 @@ class Engine:
         self.kc = [x.cuda() for x in self.kc]
         self.vc = [x.cuda() for x in self.vc]
         self.maxb = 16
+        self.shared_groups = 0  # groups with a shared prefix the decode steps met
 
     def rand(self, *shape):
         return torch.randn(shape, generator=self.gen).to(torch.bfloat16)
@@ -144,10 +145,21 @@ class Engine:
                                     self.kc[l], self.vc[l], torch.from_numpy(bt).cuda(),
                                     torch.from_numpy(ctx).cuda(), self.scale, out,
                                     max_context_len=int(ctx.max()))
+            # the same step through the shared-prefix decode, with the groups
+            # the pool's tables hold (the caches now include the new tokens)
+            starts, plens, mg = B.pkv_prefix_groups(bt, ctx)
+            out2 = torch.empty_like(out)
+            B.pkv_decode_attn_prefix(q.cuda(), self.kc[l], self.vc[l], torch.from_numpy(bt).cuda(),
+                                     torch.from_numpy(ctx).cuda(), self.scale, out2,
+                                     torch.from_numpy(starts).cuda(), torch.from_numpy(plens).cuda(),
+                                     mg, max_context_len=int(ctx.max()), partition_tokens=16)
             torch.cuda.synchronize()
+            self.shared_groups += int((plens > 0).sum())
             orc().store(bits(k), bits(v), slots, self.hk[l], self.hv[l])
             ref = orc().decode(bits(q), self.hk[l], self.hv[l], bt, ctx, self.scale)
             compare(out, ref, f"pool decode layer {l} ctx {ctx.tolist()}")
+            compare(out2, ref, f"pool shared-prefix decode layer {l} groups {starts.tolist()} "
+                               f"prefixes {plens.tolist()}")
         self.check_caches("decode")
         return copies
 
@@ -177,6 +189,10 @@ def test_pool_driven_serving_steps():
     prompts = {4: system + rng.integers(0, 1000, 40).tolist()}
     assert eng.prefill(prompts) == {4: 32}
     eng.decode([0, 1, 3, 4], [5, 6, 7, 8])
+    # the fork next to its parent: they share every full block of seq 0 from
+    # before the fork; then seqs 1 and 4 share the system prompt
+    eng.decode([0, 3, 1, 4], [9, 10, 11, 12])
+    assert eng.shared_groups > 0
     for s in (0, 1, 3, 4):
         eng.pool.free_seq(s)
     assert eng.pool.num_free() == 48
