@@ -387,10 +387,13 @@ def main():
 
 def bench_fp8(args, torch, B, W, dev):
     """The same decode step over FP8 caches (OCP E4M3 codes + one fp32 scale per
-    token and KV head): per layer, pkv_store_fp8 of the 32 new tokens then
-    pkv_decode_attn_fp8.  The pools hold random codes and scales (32 layers,
-    8.3 GB); timing as for the bf16 step (a timed region without per-launch
-    events, then a pass with events around each decode launch)."""
+    token and KV head): per layer, one pkv_store_decode_attn_fp8 launch that
+    quantizes and stores the 32 new tokens and attends over the cache
+    including them (``--separate``: pkv_store_fp8 then pkv_decode_attn_fp8;
+    the other form is timed beside it either way).  The pools hold random
+    codes and scales (32 layers, 8.3 GB); timing as for the bf16 step (a timed
+    region without per-launch events, then a pass with events around each
+    timed launch)."""
     L = args.layers
     wl = W.mistral_gqa(seed=args.seed, num_layers=L)
     S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
@@ -418,27 +421,40 @@ def bench_fp8(args, torch, B, W, dev):
                               max_context_len=wl.max_context_len, workspace=ws,
                               partition_tokens=P)
 
-    for _ in range(args.warmup):
-        for l in range(L):
-            store(l)
-            decode(l)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(args.steps):
-        for l in range(L):
-            store(l)
-            decode(l)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = a.elapsed_time(b) / args.steps
+    def fused(l):
+        B.pkv_store_decode_attn_fp8(kn[l], vn[l], slots, q[l], *pools[l], bt, ctx, wl.scale,
+                                    outs[l], max_context_len=wl.max_context_len, workspace=ws,
+                                    partition_tokens=P)
+
+    def separate(l):
+        store(l)
+        decode(l)
+
+    def timed_step(fn):
+        for _ in range(args.warmup):
+            for l in range(L):
+                fn(l)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            for l in range(L):
+                fn(l)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    main, other = (separate, fused) if args.separate else (fused, separate)
+    ms_per_step = timed_step(main)
+    other_ms = timed_step(other)
     pairs = []
     for _ in range(args.steps):
         for l in range(L):
-            store(l)
+            if args.separate:  # time the decode launch only
+                store(l)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            decode(l)
+            decode(l) if args.separate else fused(l)
             e1.record(stream)
             pairs.append((e0, e1))
     torch.cuda.synchronize()
@@ -450,23 +466,30 @@ def bench_fp8(args, torch, B, W, dev):
     # store: bf16 k/v in, codes + scales out, slots
     st_bytes = S * 2 * Hkv * D * 2 + S * 2 * Hkv * (D + 4) + 4 * S
     step_gbs = L * (dec_bytes + st_bytes) / (ms_per_step * 1e-3) / 1e9
-    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    launch_bytes = dec_bytes if args.separate else dec_bytes + st_bytes
+    achieved = launch_bytes / (dec_ms * 1e-3) / 1e9
+    kernel = f"decode_fused_kernel<{D},{Hq // Hkv},fp8>" if P < 0 else \
+        f"decode_split_kernel<{D},{Hq // Hkv},fp8>+decode_reduce_kernel<{D}>"
     del pools, q, kn, vn, outs
     torch.cuda.empty_cache()
     return {
         "workload": "the same 32 seqs x 4096 tokens, 32q/8kv, d 128, 32 layers, over FP8 (E4M3 + "
-                    "fp32 scale per token and KV head) caches: pkv_store_fp8 + pkv_decode_attn_fp8",
+                    "fp32 scale per token and KV head) caches: "
+                    + ("pkv_store_fp8 + pkv_decode_attn_fp8" if args.separate
+                       else "pkv_store_decode_attn_fp8 (store fused)"),
         "work_split": (f"single pass, {-P} waves per (seq, kv head)" if P < 0
                        else f"split-KV, {P}-token partitions + merge"),
         "ms_per_step": round(ms_per_step, 4),
+        ("fused_ms_per_step" if args.separate else "separate_ms_per_step"): round(other_ms, 4),
         "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
         "kv_gbs": round(step_gbs, 2), "hbm_peak_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "decode_us_per_layer": round(dec_ms * 1e3, 2),
-        "roofline": {"bound": "hbm", "kernel": f"decode_fused_kernel<{D},{Hq // Hkv},fp8>",
+        "decode_us_per_layer": round(dec_ms * 1e3, 2),  # the timed launch (see kernel)
+        "roofline": {"bound": "hbm",
+                     "kernel": kernel + ("" if args.separate else " (fused store)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(f"decode_fused_kernel<{D},{Hq // Hkv},fp8>"),
-                     "algorithmic_bytes_per_launch": dec_bytes, "launch_timing": dec_stats},
+                     "traffic": recorded_traffic(kernel + ("" if args.separate else " (fused store)")),
+                     "algorithmic_bytes_per_launch": launch_bytes, "launch_timing": dec_stats},
     }
 
 

@@ -396,6 +396,25 @@ int pkv_decode_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block
                         hipStream_t stream);
 
 /*
+ * pkv_store_decode_attn_fp8 -- pkv_store_decode_attn over an FP8 cache: the
+ * store of each sequence's new token, quantized exactly as pkv_store_fp8 does
+ * (codes and scale to slot_mapping[s]'s row), followed by pkv_decode_attn_fp8
+ * over the cache including it, in one launch.  Equivalent to
+ *   pkv_store_fp8(k, v, slot_mapping, num_seqs, cache, stream);
+ *   pkv_decode_attn_fp8(q, cache, ..., stream);
+ * bit for bit: where the attention takes the last position's K/V from k[s],
+ * v[s] instead of the cache, it uses the quantized codes and scale it stores.
+ * Arguments, work split, workspace and precondition as for
+ * pkv_store_decode_attn.
+ */
+int pkv_store_decode_attn_fp8(const void *k, const void *v, const int32_t *slot_mapping,
+                              const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                              float scale, void *out, void *workspace, size_t workspace_bytes,
+                              int32_t partition_tokens, hipStream_t stream);
+
+/*
  * pkv_kv_bytes -- KV-cache bytes for `tokens` cached tokens:
  *   2 (K and V) x layers x kv_heads x head_dim x tokens x bytes_per_elem
  * ([LLM4] §17.3 and §17.6: KV heads, not query heads; tokens summed over

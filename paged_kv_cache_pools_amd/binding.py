@@ -25,7 +25,8 @@ PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_CAPACITY, PKV_ERR_SEQUENCE = 5, 6, 7, 8
 EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
             "pkv_decode_attn", "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
             "pkv_prefill_attn", "pkv_mixed_attn", "pkv_mixed_workspace_bytes", "pkv_store_fp8",
-            "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_kv_bytes",
+            "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_store_decode_attn_fp8",
+            "pkv_kv_bytes",
             "pkv_status_string", "pkv_last_error",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
             "pkv_pool_fork", "pkv_pool_free_seq", "pkv_pool_block_tables", "pkv_pool_num_free",
@@ -92,6 +93,9 @@ def load(path: str = LIB_PATH):
     lib.pkv_decode_attn_fp8.restype = ctypes.c_int
     lib.pkv_decode_attn_fp8.argtypes = [_P, PkvCacheFp8, _P, _I32, _P, _I32, _I32, _I32,
                                         ctypes.c_float, _P, _P, _SZ, _I32, _P]
+    lib.pkv_store_decode_attn_fp8.restype = ctypes.c_int
+    lib.pkv_store_decode_attn_fp8.argtypes = [_P, _P, _P, _P, PkvCacheFp8, _P, _I32, _P, _I32,
+                                              _I32, _I32, ctypes.c_float, _P, _P, _SZ, _I32, _P]
     lib.pkv_prefill_attn.restype = ctypes.c_int
     lib.pkv_prefill_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                      ctypes.c_float, _P, _P]
@@ -554,6 +558,52 @@ def pkv_decode_attn_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, con
                                    float(scale), out.data_ptr(), workspace.data_ptr(),
                                    workspace.numel(), int(p), _stream(q, stream)),
            "pkv_decode_attn_fp8")
+    return out
+
+
+def pkv_store_decode_attn_fp8(k, v, slot_mapping, q, k_codes, v_codes, k_scale, v_scale,
+                              block_tables, context_lens, scale, out,
+                              max_context_len: Optional[int] = None, workspace=None,
+                              partition_tokens: int = 0, stream=None):
+    """pkv_store_fp8 then pkv_decode_attn_fp8 in one launch: k/v [S][Hkv][d]
+    bf16 (one new token per sequence), slot_mapping [S] int32; the rest as for
+    pkv_decode_attn_fp8."""
+    import torch
+
+    lib = load()
+    cache = _cache_fp8(k_codes, v_codes, k_scale, v_scale)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(k, "k", torch.bfloat16, 3)
+    _need(v, "v", torch.bfloat16, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    s, hq, d = q.shape
+    if tuple(out.shape) != (s, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    want = (s, cache.num_kv_heads, cache.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want or slot_mapping.shape[0] != s:
+        raise ValueError(f"k/v must be {want} and slot_mapping [{s}], got {tuple(k.shape)}, "
+                         f"{tuple(v.shape)}, {tuple(slot_mapping.shape)}")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables / context_lens do not match q's sequence count")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * cache.block_size
+    p = partition_tokens or pkv_decode_partition_tokens_fp8(s, cache.num_kv_heads,
+                                                            max_context_len)
+    need = pkv_decode_workspace_bytes(s, hq, d, max_context_len, p)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib.pkv_store_decode_attn_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(),
+                                         q.data_ptr(), cache, block_tables.data_ptr(),
+                                         max_blocks, context_lens.data_ptr(), s,
+                                         int(max_context_len), hq, float(scale), out.data_ptr(),
+                                         workspace.data_ptr(), workspace.numel(), int(p),
+                                         _stream(q, stream)),
+           "pkv_store_decode_attn_fp8")
     return out
 
 

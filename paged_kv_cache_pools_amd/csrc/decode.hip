@@ -7,6 +7,23 @@
 
 namespace pkv {
 
+// The fused store's new token in the cache's own format: bf16 rows, or FP8
+// codes plus their scales (k_store / v_store are the code pools then, and
+// ks_store / vs_store the scale arrays).
+template <int D, bool FP8>
+__device__ __forceinline__ NewToken make_new_token(const uint16_t *k_new, const uint16_t *v_new,
+                                                   const int32_t *slots, void *k_store,
+                                                   void *v_store, float *ks_store, float *vs_store,
+                                                   const int32_t *bt_row, int32_t num_blocks,
+                                                   int32_t num_kv_heads, int s, int kvh, int ctx) {
+    if constexpr (FP8)
+        return new_token_fp8<D>(k_new, v_new, slots, (uint8_t *)k_store, (uint8_t *)v_store,
+                                ks_store, vs_store, bt_row, num_blocks, num_kv_heads, s, kvh, ctx);
+    else
+        return new_token<D>(k_new, v_new, slots, (uint16_t *)k_store, (uint16_t *)v_store, bt_row,
+                            num_blocks, num_kv_heads, s, kvh, ctx);
+}
+
 // Split-KV decode: one wavefront per (sequence, KV head, partition of
 // partition_tokens tokens).  A sequence that fits one partition is written
 // directly; otherwise each partition writes (m, l, acc) for the merge pass.
@@ -27,8 +44,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     int32_t partition_tokens, int32_t max_parts, float scale_log2, uint16_t *__restrict__ out,
     float *__restrict__ ws_out,
     float *__restrict__ ws_ml, const uint16_t *__restrict__ k_new,
-    const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, uint16_t *k_store,
-    uint16_t *v_store, const float *__restrict__ rope_table, int32_t rope_positions) {
+    const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, void *k_store,
+    void *v_store, float *ks_store, float *vs_store, const float *__restrict__ rope_table,
+    int32_t rope_positions) {
     constexpr int LPR = D / 8, TPL = 64 / LPR;
     const int lane = threadIdx.x & 63;
     const int kvh = blockIdx.x % num_kv_heads;
@@ -44,8 +62,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     if (ctx <= 0) {
         if (part == 0) {
             write_zero_rows<D, G>(out, num_q_heads, s, kvh);
-            store_only<D>(new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks,
-                                       num_kv_heads, s, kvh, ctx),
+            store_only<D>(make_new_token<D, FP8>(k_new, v_new, slots, k_store, v_store, ks_store,
+                                                 vs_store, bt_row, num_blocks, num_kv_heads, s,
+                                                 kvh, ctx),
                           rope_at<D>(rope_table, rope_positions, ctx));
         }
         return;
@@ -57,8 +76,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     // the partition holding the last position carries the fused store
     NewToken nt;
     if (t_end == ctx)
-        nt = new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks, num_kv_heads,
-                          s, kvh, ctx);
+        nt = make_new_token<D, FP8>(k_new, v_new, slots, k_store, v_store, ks_store, vs_store,
+                                    bt_row, num_blocks, num_kv_heads, s, kvh, ctx);
 
     float acc[G][8], mg[G], lg[G];
     wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
@@ -104,8 +123,9 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
     const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, float scale_log2,
     uint16_t *__restrict__ out, const uint16_t *__restrict__ k_new,
-    const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, uint16_t *k_store,
-    uint16_t *v_store, const float *__restrict__ rope_table, int32_t rope_positions) {
+    const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, void *k_store,
+    void *v_store, float *ks_store, float *vs_store, const float *__restrict__ rope_table,
+    int32_t rope_positions) {
     extern __shared__ float smem[];  // [W][G][D] acc, then [W][G] m, then [W][G] l
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
@@ -117,8 +137,8 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
         q + row, k_cache, v_cache, k_scale, v_scale, bt_row, ctx, num_blocks, num_q_heads,
         num_kv_heads, scale_log2, out + row, kvh, blockDim.x >> 6, smem,
         [&]() {
-            return new_token<D>(k_new, v_new, slots, k_store, v_store, bt_row, num_blocks,
-                                num_kv_heads, s, kvh, ctx);
+            return make_new_token<D, FP8>(k_new, v_new, slots, k_store, v_store, ks_store,
+                                          vs_store, bt_row, num_blocks, num_kv_heads, s, kvh, ctx);
         },
         rope_at<D>(rope_table, rope_positions, ctx));
 }
@@ -175,8 +195,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                            a.k_scale, a.v_scale, a.block_tables, a.context_lens, a.max_blocks_per_seq,
                            a.max_context_len, a.num_blocks, a.num_q_heads, a.num_kv_heads,
                            scale_log2, (uint16_t *)a.out, (const uint16_t *)a.k_new,
-                           (const uint16_t *)a.v_new, a.slots, (uint16_t *)a.k_store,
-                           (uint16_t *)a.v_store, a.rope_table, a.rope_positions);
+                           (const uint16_t *)a.v_new, a.slots, a.k_store, a.v_store,
+                           a.k_scale_store, a.v_scale_store, a.rope_table, a.rope_positions);
         return hipGetLastError();
     }
     const int waves = a.max_parts >= 4 ? 4 : (a.max_parts >= 2 ? 2 : 1);
@@ -188,8 +208,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
                        a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.num_seqs,
                        a.num_q_heads, a.num_kv_heads, a.partition_tokens, a.max_parts, scale_log2,
                        (uint16_t *)a.out, a.ws_out, a.ws_ml, (const uint16_t *)a.k_new,
-                       (const uint16_t *)a.v_new, a.slots, (uint16_t *)a.k_store,
-                       (uint16_t *)a.v_store, a.rope_table, a.rope_positions);
+                       (const uint16_t *)a.v_new, a.slots, a.k_store, a.v_store,
+                       a.k_scale_store, a.v_scale_store, a.rope_table, a.rope_positions);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1) return e;
     const int rows = a.num_seqs * a.num_q_heads;

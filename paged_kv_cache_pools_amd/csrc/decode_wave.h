@@ -204,10 +204,17 @@ __device__ __forceinline__ float row_bcast(float x, int row_base) {
 // `dst_v` at its cache row (null when the slot is skipped), and `pos` is the
 // position whose cached K/V the row replaces in this wave's arithmetic (-1
 // when the slot is not that position's).
+// Most wavefronts a decode workgroup has (the single-pass kernel's bound).
+constexpr int kMaxDecodeWaves = 8;
+
 struct NewToken {
     const uint4 *src_k = nullptr, *src_v = nullptr;
     uint4 *dst_k = nullptr, *dst_v = nullptr;
     int pos = -1;
+    // FP8 cache: the row's code destinations (8 codes per lane) and its scale
+    // slots; the row is quantized as the FP8 store does
+    uint2 *dst_kq = nullptr, *dst_vq = nullptr;
+    float *dst_ks = nullptr, *dst_vs = nullptr;
 };
 
 // Rotary position embedding of a sequence's new token: the fp32 table row
@@ -248,6 +255,28 @@ __device__ __forceinline__ uint4 rope8(const uint4 &u, const uint4 &pair, const 
         o[e] = first ? __fsub_rn(a, b) : __fadd_rn(a, b);
     }
     return pack8(o);
+}
+
+// FP8 patch of a loaded block: the token row that holds the new token (load
+// `load`, lanes with `here_row`) takes the codes and scales staged in LDS
+// (codes[0] K, codes[1] V, 8 per lane of the row's LPR lanes).
+template <int NL, int LPR>
+__device__ __forceinline__ void patch_fp8_row(uint2 (&kt)[NL], uint2 (&vt)[NL], float (&ks)[NL],
+                                              float (&vs)[NL], const uint2 (&codes)[2][LPR],
+                                              const float (&scales)[2], int load, bool here_row) {
+    const int c = (threadIdx.x & 63) % LPR;
+    const uint2 kq = codes[0][c], vq = codes[1][c];
+    const float ksc = scales[0], vsc = scales[1];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const bool here = j == load && here_row;
+        kt[j].x = here ? kq.x : kt[j].x;
+        kt[j].y = here ? kq.y : kt[j].y;
+        vt[j].x = here ? vq.x : vt[j].x;
+        vt[j].y = here ? vq.y : vt[j].y;
+        ks[j] = here ? ksc : ks[j];
+        vs[j] = here ? vsc : vs[j];
+    }
 }
 
 // One wavefront's attention over tokens [t_begin, t_end) (t_begin < t_end,
@@ -360,13 +389,40 @@ __device__ __forceinline__ void wave_attend(
     const int patch_load = (nt.pos % kBlockTokens) / TPL;
     const bool patch_row = row == (nt.pos % kBlockTokens) % TPL;
     uint4 kn = make_uint4(0u, 0u, 0u, 0u), vn = kn;
+    // FP8: the new row's codes and scales wait in LDS for the patch, one slot
+    // per wave, instead of holding registers through the loop.  Every token
+    // row of the wave quantizes the same row (the group shuffles stay within
+    // a row), so every lane writes the slot word it later reads itself.
+    __shared__ uint2 nt_codes[FP8 ? kMaxDecodeWaves : 1][2][LPR];
+    __shared__ float nt_scales[FP8 ? kMaxDecodeWaves : 1][2];
     if (nt.src_k != nullptr) {  // uniform: only the wave holding the last position
-        kn = nt.src_k[c];
-        vn = nt.src_v[c];
-        if (rope.row != nullptr) kn = rope8<D>(kn, kn, rope.row, c);  // rotated before it is stored
-        if (nt.dst_k != nullptr && row == 0) {
-            nt.dst_k[c] = kn;
-            nt.dst_v[c] = vn;
+        if constexpr (FP8) {
+            if (nt.dst_kq != nullptr) {
+                float ksc, vsc;
+                const uint2 kq = quantize8<LPR>(nt.src_k[c], ksc);
+                const uint2 vq = quantize8<LPR>(nt.src_v[c], vsc);
+                if (row == 0) {  // row 0 stores it
+                    nt.dst_kq[c] = kq;
+                    nt.dst_vq[c] = vq;
+                    if (c == 0) {
+                        *nt.dst_ks = ksc;
+                        *nt.dst_vs = vsc;
+                    }
+                }
+                const int w = wave_id_uniform();
+                nt_codes[w][0][c] = kq;
+                nt_codes[w][1][c] = vq;
+                nt_scales[w][0] = ksc;
+                nt_scales[w][1] = vsc;
+            }
+        } else {
+            kn = nt.src_k[c];
+            vn = nt.src_v[c];
+            if (rope.row != nullptr) kn = rope8<D>(kn, kn, rope.row, c);  // rotated before it is stored
+            if (nt.dst_k != nullptr && row == 0) {
+                nt.dst_k[c] = kn;
+                nt.dst_v[c] = vn;
+            }
         }
     }
     auto patch = [&](uint4 &x, const uint4 &y, bool here) {
@@ -376,12 +432,19 @@ __device__ __forceinline__ void wave_attend(
         x.w = here ? y.w : x.w;
     };
 
-    auto process = [&](Tile (&kt)[NL], Tile (&vt)[NL], const float (&ks)[NL],
-                       const float (&vs)[NL], int b) {
+    // (the scales are written only by the FP8 patch; bf16 keeps const arrays)
+    using Scales = typename std::conditional<FP8, float[NL], const float[NL]>::type;
+    auto process = [&](Tile (&kt)[NL], Tile (&vt)[NL], Scales &ks, Scales &vs, int b) {
         const int tb = b * kBlockTokens;
         const bool partial = tb + kBlockTokens > t_end;
         uint4 kb[NL];  // K as bf16 pairs
         if constexpr (FP8) {
+            // (this names no variable the bf16 branch does not name first:
+            // the closure's capture order, and with it the bf16 kernels'
+            // register allocation, stays as it is without the FP8 patch)
+            if (b == patch_block)  // uniform
+                patch_fp8_row<NL>(kt, vt, ks, vs, nt_codes[wave_id_uniform()],
+                                  nt_scales[wave_id_uniform()], patch_load, patch_row);
 #pragma unroll
             for (int j = 0; j < NL; ++j) kb[j] = fp8x8_to_bf16(kt[j]);
         } else {
@@ -555,6 +618,36 @@ __device__ __forceinline__ NewToken new_token(const uint16_t *k_new, const uint1
     return t;
 }
 
+// The new token of a fused FP8 store + decode: as new_token, with the
+// destinations in the FP8 code pools (one byte per element) and their scale
+// arrays [block][kv head][16].
+template <int D>
+__device__ __forceinline__ NewToken new_token_fp8(const uint16_t *k_new, const uint16_t *v_new,
+                                                  const int32_t *slots, uint8_t *k_codes,
+                                                  uint8_t *v_codes, float *k_scale, float *v_scale,
+                                                  const int32_t *bt_row, int32_t num_blocks,
+                                                  int32_t num_kv_heads, int s, int kvh, int ctx) {
+    NewToken t;
+    if (slots == nullptr) return t;
+    const size_t src = ((size_t)s * num_kv_heads + kvh) * D;
+    t.src_k = reinterpret_cast<const uint4 *>(k_new + src);
+    t.src_v = reinterpret_cast<const uint4 *>(v_new + src);
+    const int slot = slots[s];
+    if (slot < 0 || slot / kBlockTokens >= num_blocks) return t;  // skipped: nothing written
+    const size_t row =
+        ((size_t)(slot / kBlockTokens) * num_kv_heads + kvh) * kBlockTokens + slot % kBlockTokens;
+    t.dst_kq = reinterpret_cast<uint2 *>(k_codes + row * D);
+    t.dst_vq = reinterpret_cast<uint2 *>(v_codes + row * D);
+    t.dst_ks = k_scale + row;
+    t.dst_vs = v_scale + row;
+    if (ctx > 0) {
+        const int last = ctx - 1;
+        if ((int64_t)bt_row[last / kBlockTokens] * kBlockTokens + last % kBlockTokens == slot)
+            t.pos = last;
+    }
+    return t;
+}
+
 // The rotation for a sequence whose context (the new token included) holds
 // ctx tokens: the table row of position ctx - 1, clamped into the table (a
 // position past it is a caller error).  Empty when the launch has no table.
@@ -572,6 +665,20 @@ __device__ __forceinline__ void store_only(const NewToken &t, const Rope &rope) 
     const int c = lane % (D / 8);
     if (t.src_k == nullptr) return;  // uniform
     uint4 kk = t.src_k[c];
+    if (t.dst_kq != nullptr) {  // uniform: an FP8 cache; every lane shuffles in quantize8
+        float ksc, vsc;
+        const uint2 kq = quantize8<D / 8>(kk, ksc);
+        const uint2 vq = quantize8<D / 8>(t.src_v[c], vsc);
+        if (lane < D / 8) {
+            t.dst_kq[lane] = kq;
+            t.dst_vq[lane] = vq;
+            if (lane == 0) {
+                *t.dst_ks = ksc;
+                *t.dst_vs = vsc;
+            }
+        }
+        return;
+    }
     if (rope.row != nullptr) kk = rope8<D>(kk, kk, rope.row, c);  // all lanes shuffle
     if (t.dst_k != nullptr && lane < D / 8) {
         t.dst_k[lane] = kk;

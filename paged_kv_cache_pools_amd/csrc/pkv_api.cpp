@@ -447,6 +447,8 @@ int decode_call(const void *q, const CacheDesc &cache, const int32_t *block_tabl
         a.slots = slots;
         a.k_store = cache.k;
         a.v_store = cache.v;
+        a.k_scale_store = cache.k_scale;
+        a.v_scale_store = cache.v_scale;
     }
     return hip_status(pkv::launch_decode(a, stream), what);
 }
@@ -511,6 +513,22 @@ int pkv_decode_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block
                        num_seqs, max_context_len, num_q_heads, scale, out, workspace,
                        workspace_bytes, partition_tokens, stream, nullptr, nullptr, nullptr,
                        "pkv_decode_attn_fp8 launch");
+}
+
+int pkv_store_decode_attn_fp8(const void *k, const void *v, const int32_t *slot_mapping,
+                              const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *context_lens,
+                              int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                              float scale, void *out, void *workspace, size_t workspace_bytes,
+                              int32_t partition_tokens, hipStream_t stream) {
+    if (num_seqs > 0 && (!k || !v || !slot_mapping))
+        return fail(PKV_ERR_NULL, "k, v or slot_mapping is null");
+    if (!aligned16(k) || !aligned16(v))
+        return fail(PKV_ERR_ALIGN, "k / v must be 16-byte aligned");
+    return decode_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                       workspace_bytes, partition_tokens, stream, k, v, slot_mapping,
+                       "pkv_store_decode_attn_fp8 launch");
 }
 
 int pkv_store_fp8(const void *k, const void *v, const int32_t *slot_mapping, int32_t num_tokens,

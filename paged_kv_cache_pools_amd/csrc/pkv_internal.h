@@ -55,6 +55,9 @@ struct DecodeArgs {
     // [num_blocks][num_kv_heads][16]
     bool fp8 = false;
     const float *k_scale = nullptr, *v_scale = nullptr;
+    // fused store into an FP8 cache: the scale arrays written (the same
+    // arrays as k_scale / v_scale); k_store / v_store are the code pools
+    float *k_scale_store = nullptr, *v_scale_store = nullptr;
     // rotary embedding of q and the stored token at each sequence's last
     // position: fp32 table [rope_positions][head_dim] (cos, then sin), or null
     const float *rope_table = nullptr;

@@ -51,39 +51,8 @@ __global__ __launch_bounds__(256) void store_kernel(const uint4 *__restrict__ k,
     }
 }
 
-// ---- FP8 cache: OCP E4M3 codes with one fp32 scale per (token, KV head) ----
-//
-// The LLM primer (part 4, §17.6) counts an FP8 KV cache at one byte per
-// element.  Each (token, KV head) row of head_dim values is quantized on its
-// own: scale = amax / 448 (448 = the largest finite E4M3 magnitude; 1 when
-// the row is all zero) and code = E4M3(x / scale), rounded to nearest even,
-// with x / scale clamped to [-448, 448] first so the conversion never
-// saturates.  Both divisions are correctly rounded fp32.  A group of D/8
-// lanes owns a row (8 values per lane, one 16-byte load); the row's amax is
-// an all-reduce over the group.
-
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-    uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
-}
-
-// Quantize this lane's 8 values of a row whose group is LPR lanes wide; every
-// lane of the wave must call it (it shuffles across the group).
-template <int LPR>
-__device__ __forceinline__ uint2 quantize8(const uint4 &u, float &scale) {
-    float f[8];
-    unpack8(u, f);
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-    scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(__fdiv_rn(f[i], scale), -448.f), 448.f);
-    return make_uint2(fp8x4(y[0], y[1], y[2], y[3]), fp8x4(y[4], y[5], y[6], y[7]));
-}
+// ---- FP8 cache: OCP E4M3 codes with one fp32 scale per (token, KV head),
+// quantized by quantize8 (pkv_device.h) ----
 
 template <int D>
 __global__ __launch_bounds__(256) void store_fp8_kernel(

@@ -222,6 +222,14 @@ def test_fp8_validation(lib):
                                             ctypes.c_float(0.125), FAKE, FAKE, 1 << 30, 0, None)
     assert dec(c8(ks=0)) == 1
     assert dec(c8(vs=FAKE + 8)) == 4
+    sd = lambda c=None, k=FAKE, v=FAKE, sl=FAKE, s=2, q=FAKE: lib.pkv_store_decode_attn_fp8(
+        k, v, sl, q, c or c8(), FAKE, 3, FAKE, s, 37, 4, ctypes.c_float(0.125), FAKE, FAKE,
+        1 << 30, 0, None)
+    assert sd(s=0) == 0                     # empty batch: nothing launched
+    assert sd(k=0) == 1 and sd(v=0) == 1 and sd(sl=0) == 1
+    assert sd(v=FAKE + 4) == 4
+    assert sd(c=c8(ks=0)) == 1 and sd(c=c8(d=96)) == 3
+    assert sd(q=0) == 1                     # the decode checks still apply
     assert B.pkv_last_error() != ""
 
 

@@ -609,6 +609,71 @@ def test_store_then_decode_fp8():
     compare(out, ref, "store + decode fp8", plus_floor=True)
 
 
+def fused_fp8_vs_separate(wl, partition_tokens=0, slots=None, what=None, nan_fill=True):
+    """pkv_store_decode_attn_fp8 against pkv_store_fp8 + pkv_decode_attn_fp8
+    on copies of the same pools: codes, scales and output bit for bit."""
+    c = Case(wl)
+    host, dev = fp8_case(wl, nan_fill=nan_fill)
+    dev2 = [x.clone() for x in dev]
+    d = c.dev
+    slot_t = d["slot_mapping"] if slots is None else torch.from_numpy(slots).cuda()
+    say(f"[gpu] fused fp8 store+decode {what or wl.name}: S={wl.num_seqs} "
+        f"G={wl.num_q_heads // wl.num_kv_heads} d={wl.head_dim} P={partition_tokens or 'auto'}")
+    B.pkv_store_fp8(d["k_new"], d["v_new"], slot_t, *dev)
+    out_sep = torch.empty_like(d["q"])
+    B.pkv_decode_attn_fp8(d["q"], *dev, d["block_tables"], d["context_lens"], wl.scale, out_sep,
+                          max_context_len=wl.max_context_len, partition_tokens=partition_tokens)
+    out = torch.empty_like(d["q"])
+    B.pkv_store_decode_attn_fp8(d["k_new"], d["v_new"], slot_t, d["q"], *dev2,
+                                d["block_tables"], d["context_lens"], wl.scale, out,
+                                max_context_len=wl.max_context_len,
+                                partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    for a, b, name in zip(dev2, dev, ("k codes", "v codes", "k scales", "v scales")):
+        assert np.array_equal(a.cpu().numpy().view(np.uint8), b.cpu().numpy().view(np.uint8)), \
+            f"fused store differs ({name})"
+    assert np.array_equal(bits(out), bits(out_sep)), "fused attention differs"
+    return c, host, dev2, out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 4, 8])
+@pytest.mark.parametrize("part", [16, 64, 0, -1, -3])
+def test_fused_store_decode_fp8_matches_separate(d, g, part):
+    lens = [1, 15, 16, 17, 63, 64, 65, 129, 0, 300]
+    wl = W.make_decode(f"fused_fp8_d{d}_g{g}", lens, 2 * g, 2, d, 500 + d + g, spare_blocks=2)
+    c, host, dev, out = fused_fp8_vs_separate(wl, part)
+    orc().store_fp8(c.h["k_new"], c.h["v_new"], wl.slot_mapping, *host)
+    for got, ref, name in zip(dev, host, ("k codes", "v codes", "k scales", "v scales")):
+        assert np.array_equal(got.cpu().numpy().view(np.uint8), ref.view(np.uint8)), name
+    ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
+    compare(out, ref, f"fused fp8 store+decode d{d} g{g} P{part}", plus_floor=True)
+
+
+def test_fused_store_decode_fp8_skips_and_strays():
+    """slot -1 stores nothing (the last position keeps its cached codes); a
+    slot in an unreferenced block is stored but not attended; a sequence with
+    no context only stores; a slot outside the pool is not written."""
+    wl = W.make_decode("fused_fp8_edges", [20, 33, 7, 0, 40, 9], 8, 2, 128, 64, spare_blocks=2)
+    spare = sorted(set(range(wl.num_blocks)) - set(wl.used_blocks().tolist()))
+    slots = wl.slot_mapping.copy()
+    slots[1] = -1
+    slots[2] = spare[0] * 16 + 3
+    slots[3] = spare[1] * 16 + 0
+    slots[5] = wl.num_blocks * 16 + 1
+    # no NaN fill: the last positions of sequences 1 and 2 are not stored in
+    # this step, so they must already hold a token (random codes here)
+    c, host, dev, out = fused_fp8_vs_separate(wl, 0, slots=slots, what="edges", nan_fill=False)
+    assert np.all(to_f64(out)[3] == 0.0)
+    slots_oracle = slots.copy()
+    slots_oracle[5] = -1  # the oracle rejects out-of-pool slots
+    orc().store_fp8(c.h["k_new"], c.h["v_new"], slots_oracle, *host)
+    for got, ref, name in zip(dev, host, ("k codes", "v codes", "k scales", "v scales")):
+        assert np.array_equal(got.cpu().numpy().view(np.uint8), ref.view(np.uint8)), name
+    ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
+    compare(out, ref, "fused fp8 store+decode edges", plus_floor=True)
+
+
 def test_decode_fp8_mistral_full_size():
     """32 x 4096 GQA over FP8 pools in the benchmark's launch configuration;
     the oracle checks sampled sequences on compacted copies."""
