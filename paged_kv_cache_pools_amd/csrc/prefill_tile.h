@@ -38,8 +38,15 @@
 // wave), so O^T is rescaled on a few chunks instead of every one; weights are
 // then at most 2^8, far from fp32 or bf16 overflow, and the final division by
 // the weight sum, accumulated with the same stale maximum, is exact algebra.
-// For the P V product each weight is split into bf16 hi + lo parts (two
-// MFMAs), so P carries about 16 significant bits into the matrix cores.
+// The weights enter the P V product rounded to bf16 (nearest even), and the
+// weight sum is taken from those same rounded weights by one more MFMA whose
+// A operand is all ones, so the normalisation is consistent with what was
+// multiplied into V: out is a convex combination of V rows whose weights are
+// off by at most 2^-9 relative, and a row dominated by one key returns that
+// key's V with no weight error at all.  Waves whose rows see few keys
+// (kPreciseKeys) split each weight into bf16 hi + lo parts and run P V on
+// both: such rows can average a handful of V values into an output near 2,
+// where half a bf16 ulp already takes most of a 1e-2 absolute budget.
 //
 // Keys at or past the context end are zero in LDS (V) or masked by select (S),
 // so NaN bits in unused slots never reach the output.
@@ -70,12 +77,17 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
-// Split two finite fp32 softmax weights into bf16 hi and lo parts with
-// p == hi + lo to about 2^-16 relative: hi is p truncated to bf16 (its upper
-// half), lo is the exact remainder p - hi rounded to bf16.  P V is computed as
-// hi V + lo V, which keeps the weights' rounding far below the bf16 rounding
-// of the output: with bf16 weights alone a row of a few keys whose output is
-// near 2 can miss a 1e-2 absolute bound.
+// bf16 ones in both halves of a dword: the A operand that turns the P V MFMA
+// into the column sums of P
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
+
+// A wave whose last query sees fewer keys than this carries the weights in
+// two bf16 parts.
+constexpr int kPreciseKeys = 128;
+
+// Split two finite fp32 weights into bf16 hi and lo parts with p == hi + lo
+// to about 2^-16 relative: hi is p truncated to bf16 (its upper half), lo the
+// remainder p - hi (exact in fp32) rounded to bf16.
 __device__ __forceinline__ void split2_bf16(float p0, float p1, uint32_t &hi, uint32_t &lo) {
     const uint32_t b0 = __float_as_uint(p0), b1 = __float_as_uint(p1);
     hi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);  // (b0 >> 16) | (b1 & 0xffff0000)
@@ -92,13 +104,6 @@ __device__ __forceinline__ float max_xor16(float x) {
 __device__ __forceinline__ float max_xor32(float x) {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-// sums in the same order on every lane: (row 0 + row 1) + (row 2 + row 3)
-__device__ __forceinline__ float sum_rows(float x) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 // The running maximum is raised only when it grows by more than this (log2
@@ -279,17 +284,22 @@ __device__ __forceinline__ void prefill_unit(
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[NT], l[NT];  // running max (log2 domain, shared by the column's lanes), partial sums
+    // running max (log2 domain, shared by the column's lanes) and the column's
+    // weight sum, which arrives in all 4 rows of ol[nt] (every lane holds it)
+    float m[NT];
+    f32x4_t ol[NT];
+    const uint4 ones = make_uint4(kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         m[nt] = kNegInf;
-        l[nt] = 0.f;
+        ol[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     // positions of this wave's first and last live token: chunks wholly below
     // the first need no causal mask, chunks wholly above the last are skipped
     const int wave_min_pos = CROSS ? INT32_MAX : c + T0 + w * TW;
     const int wave_max_pos = CROSS ? ctx - 1 : c + min(T0 + (w + 1) * TW, n) - 1;
     const bool wave_live = T0 + w * TW < n;
+    const bool precise = wave_max_pos < kPreciseKeys;  // wave-uniform
 
     const size_t tile = (size_t)kBlockTokens * D;
 
@@ -442,15 +452,15 @@ __device__ __forceinline__ void prefill_unit(
                 for (int nt = 0; nt < NT; ++nt) {
                     const float alpha = (mc[nt] == kNegInf) ? 1.f : exp2f(m[nt] - mc[nt]);
                     m[nt] = mc[nt];
-                    l[nt] *= alpha;
+                    ol[nt] *= alpha;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
                 }
             }
 
-            // weights, their partial sums, and P^T as the B operand (bf16).  Key
-            // permutation sigma: MFMA k-slot (a, 0..3) <- keys 4a..4a+3 of the
-            // half's first 16, k-slot (a, 4..7) <- keys 16+4a..16+4a+3
+            // weights and P^T as the B operand (bf16).  Key permutation sigma:
+            // MFMA k-slot (a, 0..3) <- keys 4a..4a+3 of the half's first 16,
+            // k-slot (a, 4..7) <- keys 16+4a..16+4a+3
             uint4 ph[NT], pl[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -472,18 +482,22 @@ __device__ __forceinline__ void prefill_unit(
                         for (int r = 0; r < 4; ++r)
                             s[t][nt][r] = (dead >> ((t * NT + nt) * 4 + r)) & 1u ? 0.f : s[t][nt][r];
             }
+            if (precise) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                float psum = 0.f;
+                for (int nt = 0; nt < NT; ++nt) {
+                    split2_bf16(s[0][nt][0], s[0][nt][1], ph[nt].x, pl[nt].x);
+                    split2_bf16(s[0][nt][2], s[0][nt][3], ph[nt].y, pl[nt].y);
+                    split2_bf16(s[1][nt][0], s[1][nt][1], ph[nt].z, pl[nt].z);
+                    split2_bf16(s[1][nt][2], s[1][nt][3], ph[nt].w, pl[nt].w);
+                }
+            } else {
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) psum += s[t][nt][r];
-                l[nt] += psum;
-                split2_bf16(s[0][nt][0], s[0][nt][1], ph[nt].x, pl[nt].x);
-                split2_bf16(s[0][nt][2], s[0][nt][3], ph[nt].y, pl[nt].y);
-                split2_bf16(s[1][nt][0], s[1][nt][1], ph[nt].z, pl[nt].z);
-                split2_bf16(s[1][nt][2], s[1][nt][3], ph[nt].w, pl[nt].w);
+                for (int nt = 0; nt < NT; ++nt) {
+                    ph[nt].x = cvt_pk_bf16(s[0][nt][0], s[0][nt][1]);
+                    ph[nt].y = cvt_pk_bf16(s[0][nt][2], s[0][nt][3]);
+                    ph[nt].z = cvt_pk_bf16(s[1][nt][0], s[1][nt][1]);
+                    ph[nt].w = cvt_pk_bf16(s[1][nt][2], s[1][nt][3]);
+                }
             }
 
             // O^T += V^T P^T over the half's 32 keys, two head_dim tiles at a
@@ -504,11 +518,29 @@ __device__ __forceinline__ void prefill_unit(
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt)
                         o[mt + u][nt] = mfma16x16x32(vf[u], ph[nt], o[mt + u][nt]);
+            }
+            // the weight sums of the half, from the same bf16 weights
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
+            for (int nt = 0; nt < NT; ++nt) ol[nt] = mfma16x16x32(ones, ph[nt], ol[nt]);
+            if (precise) {  // the lo parts, into O and the sums alike
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        o[mt + u][nt] = mfma16x16x32(vf[u], pl[nt], o[mt + u][nt]);
+                for (int mt = 0; mt < MT; mt += 2) {
+                    uint4 vf[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const unsigned char *vrow = lv + ((mt + u) * 16 + col) * VROW;
+                        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + a * 4) * 2);
+                        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + 16 + a * 4) * 2);
+                        vf[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+#pragma unroll
+                        for (int nt = 0; nt < NT; ++nt)
+                            o[mt + u][nt] = mfma16x16x32(vf[u], pl[nt], o[mt + u][nt]);
+                }
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) ol[nt] = mfma16x16x32(ones, pl[nt], ol[nt]);
             }
         }
     };
@@ -537,12 +569,10 @@ __device__ __forceinline__ void prefill_unit(
         __syncthreads();
     }
 
-    // ---- the column sums of the weights (each lane holds 4 rows' share)
+    // ---- the column sums of the weights (each lane holds its column's)
     float lt[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        lt[nt] = sum_rows(l[nt]);
-    }
+    for (int nt = 0; nt < NT; ++nt) lt[nt] = ol[nt][0];
 
     if constexpr (SPLIT) {
         if (split.ws_out != nullptr) {  // uniform: rows of a split-KV workspace
