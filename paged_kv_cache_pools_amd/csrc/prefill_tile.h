@@ -400,16 +400,32 @@ __device__ __forceinline__ void prefill_unit(
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) s[t][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // the half's K fragments, all read before its first MFMA
+            uint4 kfr[KSTEPS][2];
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int r = (2 * hf + t) * 16 + col;
+                    kfr[ks][t] = *reinterpret_cast<const uint4 *>(lk + r * KROW + Geo::kslot(r, ks * 4 + a) * 16);
+                }
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    const int r = (2 * hf + t) * 16 + col;
-                    const uint4 kf = *reinterpret_cast<const uint4 *>(
-                        lk + r * KROW + Geo::kslot(r, ks * 4 + a) * 16);
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) s[t][nt] = mfma16x16x32(kf, qf[nt][ks], s[t][nt]);
+                    for (int nt = 0; nt < NT; ++nt) s[t][nt] = mfma16x16x32(kfr[ks][t], qf[nt][ks], s[t][nt]);
                 }
+            }
+
+            // V^T fragments of the half, read now so the softmax hides their latency
+            uint4 vfr[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const unsigned char *vrow = lv + (mt * 16 + col) * VROW;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + a * 4) * 2);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + 16 + a * 4) * 2);
+                vfr[mt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
 
             // the causal and context-end mask, for the chunks that cross either
@@ -505,14 +521,7 @@ __device__ __forceinline__ void prefill_unit(
             // the one that reads its result
 #pragma unroll
             for (int mt = 0; mt < MT; mt += 2) {
-                uint4 vf[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const unsigned char *vrow = lv + ((mt + u) * 16 + col) * VROW;
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + a * 4) * 2);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + 16 + a * 4) * 2);
-                    vf[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                }
+                const uint4 vf[2] = {vfr[mt], vfr[mt + 1]};
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -525,14 +534,7 @@ __device__ __forceinline__ void prefill_unit(
             if (precise) {  // the lo parts, into O and the sums alike
 #pragma unroll
                 for (int mt = 0; mt < MT; mt += 2) {
-                    uint4 vf[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const unsigned char *vrow = lv + ((mt + u) * 16 + col) * VROW;
-                        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + a * 4) * 2);
-                        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (hf * 32 + 16 + a * 4) * 2);
-                        vf[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    }
+                    const uint4 vf[2] = {vfr[mt], vfr[mt + 1]};
 #pragma unroll
                     for (int u = 0; u < 2; ++u)
 #pragma unroll
