@@ -125,20 +125,33 @@ int32_t partition_for(int64_t units, int32_t max_context_len) {
 // workgroup per unit is not a straggler; it then gives each unit enough waves
 // for kTargetWaves in all (1024 = four per CU for bf16; the FP8 path, with
 // twice the arithmetic per byte, runs best at 2048 = two per SIMD), at least
+// four (one per SIMD of the compute unit a workgroup lands on) and at least
 // one block per wave.  A wave of the longest context must not walk more than
 // kMaxWaveTokens: with many units of mixed lengths the choice would be one
 // wave per unit, and the longest sequence's lone wave the whole launch
 // (measured: 256 lognormal contexts up to 6565 tokens, 361 us single-pass
-// against 175 us split).
+// against 175 us split).  With more units than compute units, several
+// workgroups share each one and the longest unit's waves set the launch
+// time, so they get up to 8 waves and must walk at most kShortWaveTokens
+// (measured, store + decode, us: 16 MHA sequences of U{128..2048} tokens 54.4
+// at 2 waves against 49.8 at 4; 64 x 2048 GQA 100 against 88.5; 64 GQA
+// sequences of U{128..4096} tokens 115 split against 110.7 at 8 waves; the
+// 32 x 4096 GQA batch, 256 units, stays at 4 waves: 85.5 against 86.5 at 8).
 int32_t fused_waves_for(int64_t units, int32_t max_context_len, int64_t kTargetWaves) {
-    constexpr int64_t kMinUnits = 128;
-    constexpr int32_t kMaxContext = 8192, kMaxWaves = 8, kMaxWaveTokens = 1024;
+    constexpr int64_t kMinUnits = 128, kComputeUnits = 256;
+    constexpr int32_t kMaxContext = 8192, kMinWaves = 4, kMaxWaves = 8, kMaxWaveTokens = 1024,
+                      kShortWaveTokens = 512;
     if (units < kMinUnits || max_context_len <= 0 || max_context_len > kMaxContext) return 0;
     int32_t w = (int32_t)((kTargetWaves + units - 1) / units);
-    w = w < 1 ? 1 : (w > kMaxWaves ? kMaxWaves : w);
+    w = w < kMinWaves ? kMinWaves : (w > kMaxWaves ? kMaxWaves : w);
+    int32_t limit = kMaxWaveTokens;
+    if (units > kComputeUnits) {
+        limit = kShortWaveTokens;
+        if (ceil_div(max_context_len, w) > limit) w = kMaxWaves;
+    }
     const int32_t blocks = (max_context_len + kBlock - 1) / kBlock;
     w = w > blocks ? blocks : w;
-    return ceil_div(max_context_len, w) > kMaxWaveTokens ? 0 : w;
+    return ceil_div(max_context_len, w) > limit ? 0 : w;
 }
 
 }  // namespace

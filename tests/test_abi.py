@@ -62,14 +62,20 @@ def test_partition_heuristic(lib):
     # many units whose longest context would leave one wave walking 6565
     # tokens alone: two-pass split-KV, not single pass with one wave each
     assert B.pkv_decode_partition_tokens(256, 8, 6565) > 0
-    # the 16-sequence MHA batch (512 units, up to 2048 tokens): 2 waves of 1024
-    assert B.pkv_decode_partition_tokens(16, 32, 2048) == -2
+    # the 16-sequence MHA batch (512 units, up to 2048 tokens): 4 waves of 512
+    assert B.pkv_decode_partition_tokens(16, 32, 2048) == -4
+    # more units than compute units and up to 4096 tokens: 8 waves of 512
+    assert B.pkv_decode_partition_tokens(64, 8, 4096) == -8
+    # many short units: still 4 waves each (one per SIMD)
+    assert B.pkv_decode_partition_tokens(256, 8, 512) == -4
+    # more units than compute units with contexts past 4096: split-KV
+    assert B.pkv_decode_partition_tokens(64, 8, 4200) > 0
     for s, h, ctx in ((1, 1, 1), (2, 2, 37), (256, 8, 32768), (16, 32, 2048), (1, 1, 1 << 20),
                       (32, 8, 4096), (64, 8, 16), (256, 8, 6565)):
         p = B.pkv_decode_partition_tokens(s, h, ctx)
         assert (p % 16 == 0 and 64 <= p <= 512) or (-8 <= p <= -1), (s, h, ctx, p)
-        if p < 0:  # no wave walks more than 1024 tokens
-            assert -(-ctx // -p) <= 1024
+        if p < 0:  # no wave walks more than 1024 tokens (512 with more units than CUs)
+            assert -(-ctx // -p) <= (1024 if s * h <= 256 else 512)
         if p < 0:  # at least one block per wave
             assert -p <= -(-ctx // 16)
     assert B.pkv_decode_partition_tokens(-1, 8, 10) == 0
