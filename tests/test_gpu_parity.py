@@ -119,6 +119,15 @@ def test_decode_partition_sizes(part):
     run_decode_full(wl, partition_tokens=part)
 
 
+def test_decode_auto_many_units():
+    """More (sequence, KV head) units than compute units, contexts up to 4096:
+    the automatic choice is the single-pass kernel with 8 waves per unit."""
+    ctx = np.random.default_rng(56).integers(1000, 4097, 40).tolist()  # 320 units
+    wl = W.make_decode("many_units", ctx, 32, 8, 128, 57)
+    assert B.pkv_decode_partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.max_context_len) == -8
+    run_decode_full(wl)
+
+
 def test_decode_loose_max_context_len():
     """A host bound larger than any context only adds empty partitions."""
     wl = W.make_decode("loose", [100, 37], 8, 2, 128, 54)
