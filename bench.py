@@ -368,6 +368,10 @@ def main():
                 "v_caches": [x.cpu() for x in t["v_caches"][:2]]}
     del t
     torch.cuda.empty_cache()
+    probe = bench_read_probe(torch, B, dev)
+    result["read_probe"] = probe
+    result["roofline"]["measured_read_gbs"] = probe["gbs"]
+    result["roofline"]["frac_of_measured_read"] = round(achieved / probe["gbs"], 4)
     if not args.no_fp8:
         result["fp8"] = bench_fp8(args, torch, B, W, dev)
     if not args.no_prefill:
@@ -383,6 +387,57 @@ def main():
     if host is not None:
         result["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bench_read_probe(torch, B, dev, gib=4, iters=10):
+    """The second denominator beside the nominal 8 TB/s: one streaming read
+    kernel (pkv_read_probe: whole 4 KiB tiles per wave, as decode reads them,
+    16-byte nontemporal loads) over a 4 GiB buffer, far past the L2 and the
+    256 MB last-level cache, timed in this run (median of 10 launches, HIP
+    events)."""
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        B.pkv_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        B.pkv_read_probe(buf, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    med = float(np.median(ms))
+    del buf
+    torch.cuda.empty_cache()
+    gbs = nbytes / (med * 1e-3) / 1e9
+    return {"kernel": "pkv_read_probe (whole 4 KiB tiles per wave, 16-byte nontemporal loads)", "bytes": nbytes,
+            "ms": round(med, 4), "gbs": round(gbs, 1),
+            "frac_of_nominal": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def mfma_peak_rocminfo():
+    """Dense bf16 MFMA peak recomputed from rocminfo: compute units x maximum
+    clock x 4096 flops per compute unit per cycle (4 SIMDs, each retiring a
+    16x16x32 bf16 MFMA, 16384 flops, every 16 cycles).  None when rocminfo is
+    unavailable."""
+    import re
+    try:
+        text = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in text.split("*******"):
+        if not re.search(r"Name:\s+gfx950", agent):
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        if cu and mhz:
+            return {"compute_units": int(cu.group(1)), "max_clock_mhz": int(mhz.group(1)),
+                    "tflops": round(int(cu.group(1)) * int(mhz.group(1)) * 1e6 * 4096 / 1e12, 1)}
+    return None
 
 
 def bench_fp8(args, torch, B, W, dev):
@@ -793,11 +848,14 @@ def bench_prefill(args, torch, B, W, dev):
     at_ms = float(np.median([b.elapsed_time(c) for _, b, c in evs]))
     fl = prefill_flops(wl)
     tf = fl / (at_ms * 1e-3) / 1e12
+    peak = mfma_peak_rocminfo()
     return {
         "workload": "chunked causal prefill: 8 prompts x 2048 new tokens, cached U{0..4096}, "
                     "32q/8kv, d 128",
         "attn_ms": round(at_ms, 4), "attn_tflops": round(tf, 2),
         "mfma_peak_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+        "mfma_peak_rocminfo": peak,
+        "mfma_frac_rocminfo": round(tf / peak["tflops"], 4) if peak else None,
         "causal_gflop": round(fl / 1e9, 2),
         "store_ms": round(st_ms, 4),
         "store_gbs": round(store_bytes(wl) / (st_ms * 1e-3) / 1e9, 2),

@@ -423,6 +423,20 @@ int pkv_store_decode_attn_fp8(const void *k, const void *v, const int32_t *slot_
 uint64_t pkv_kv_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim, int64_t tokens,
                       int32_t bytes_per_elem);
 
+/*
+ * pkv_read_probe -- a measurement aid, not part of the attention path: one
+ * kernel that streams `bytes` of device memory at `buf` with 16-byte
+ * nontemporal loads, so that a benchmark can time the HBM read rate this GPU
+ * reaches in the same run as the kernels it rates.
+ *   buf    device pointer, 16-byte aligned; bytes a multiple of 16 (0: nothing)
+ *   sink   device pointer to one uint32; written only in the unlikely case
+ *          that the folded contents equal a fixed pattern (the value is of no
+ *          use; it keeps the loads from being optimised away)
+ * Errors: PKV_ERR_NULL, PKV_ERR_ALIGN, PKV_ERR_SHAPE (bytes not a multiple
+ * of 16), PKV_ERR_HIP.  Enqueued on `stream`.
+ */
+int pkv_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Static, human-readable name of a pkv_status value. */
 const char *pkv_status_string(int status);
 

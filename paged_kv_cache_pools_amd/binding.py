@@ -26,7 +26,7 @@ EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_by
             "pkv_decode_attn", "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
             "pkv_prefill_attn", "pkv_mixed_attn", "pkv_mixed_workspace_bytes", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_store_decode_attn_fp8",
-            "pkv_kv_bytes",
+            "pkv_kv_bytes", "pkv_read_probe",
             "pkv_status_string", "pkv_last_error",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
             "pkv_pool_fork", "pkv_pool_free_seq", "pkv_pool_block_tables", "pkv_pool_num_free",
@@ -121,6 +121,8 @@ def load(path: str = LIB_PATH):
     lib.pkv_pool_seq_len.argtypes = [_P, _I64]
     lib.pkv_copy_blocks.restype = ctypes.c_int
     lib.pkv_copy_blocks.argtypes = [_P, _I32, _SZ, _I32, _P, _I32, _P]
+    lib.pkv_read_probe.restype = ctypes.c_int
+    lib.pkv_read_probe.argtypes = [_P, _SZ, _P, _P]
     lib.pkv_mixed_attn.restype = ctypes.c_int
     lib.pkv_mixed_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                    ctypes.c_float, _P, _P, _SZ, _P]
@@ -745,3 +747,16 @@ def pkv_copy_blocks(pools, copies, stream=None):
     _check(lib.pkv_copy_blocks(ctypes.cast(ptrs, ctypes.c_void_p), len(pools), bb, nb,
                                copies.data_ptr(), copies.shape[0], _stream(copies, stream)),
            "pkv_copy_blocks")
+
+
+def pkv_read_probe(buf, sink, stream=None):
+    """Stream every byte of the contiguous device tensor ``buf`` through one
+    read kernel (a measurement aid: the HBM read rate of this GPU).  ``sink``:
+    a device tensor of at least 4 bytes that the kernel may write."""
+    lib = load()
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda:
+        raise TypeError("buf and sink must be device tensors, buf contiguous")
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink must hold at least 4 bytes")
+    _check(lib.pkv_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                              _stream(buf, stream)), "pkv_read_probe")

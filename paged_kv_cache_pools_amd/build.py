@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 SOURCES = ["pkv_api.cpp", "pool.cpp", "store.hip", "decode.hip", "prefill.hip", "copy.hip",
-           "mixed.hip", "cascade.hip"]
+           "mixed.hip", "cascade.hip", "probe.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 arithmetic is switched off for every device pass; the host pass

@@ -273,6 +273,14 @@ int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
     return hip_status(pkv::launch_mixed(a, stream), "pkv_mixed_attn launch");
 }
 
+int pkv_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    if (bytes == 0) return ok();
+    if (!buf || !sink) return fail(PKV_ERR_NULL, "buf or sink is null");
+    if (!aligned16(buf)) return fail(PKV_ERR_ALIGN, "buf must be 16-byte aligned");
+    if (bytes % 16 != 0) return fail(PKV_ERR_SHAPE, "bytes %zu is not a multiple of 16", bytes);
+    return hip_status(pkv::launch_read_probe(buf, bytes, sink, stream), "pkv_read_probe launch");
+}
+
 int pkv_copy_blocks(void *const *pools, int32_t num_pools, size_t block_bytes, int32_t num_blocks,
                     const int32_t *copies, int32_t num_copies, hipStream_t stream) {
     if (num_pools < 0 || num_blocks < 0 || num_copies < 0)

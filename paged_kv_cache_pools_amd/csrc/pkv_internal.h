@@ -133,4 +133,8 @@ struct CopyArgs {
 };
 hipError_t launch_copy_blocks(const CopyArgs &a);
 
+// Streaming read of `bytes` (a multiple of 16) at `buf`; writes at most one
+// word to `sink`.
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 }  // namespace pkv

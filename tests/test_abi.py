@@ -281,3 +281,13 @@ def test_prefix_decode_workspace_sizing(lib):
         32 * (32768 // B.pkv_decode_partition_tokens(1, 8, 32768) + 8) * 130 * 4
     assert B.pkv_decode_prefix_workspace_bytes(0, 32, 8, 128, 100, 0) == 0
     assert B.pkv_decode_prefix_workspace_bytes(4, 32, 8, 128, 100, 24) == 0
+
+
+def test_read_probe_validation(lib):
+    FAKE = 1 << 20  # never dereferenced: every call below fails on the host or launches nothing
+    assert lib.pkv_read_probe(None, 0, None, None) == 0          # nothing to read
+    assert lib.pkv_read_probe(None, 64, FAKE, None) == 1         # null buffer
+    assert lib.pkv_read_probe(FAKE, 64, None, None) == 1         # null sink
+    assert lib.pkv_read_probe(FAKE + 8, 64, FAKE, None) == 4     # misaligned
+    assert lib.pkv_read_probe(FAKE, 72, FAKE, None) == 2         # not a multiple of 16
+    assert "16" in B.pkv_last_error()

@@ -705,3 +705,16 @@ def test_decode_fp8_mistral_full_size():
     q = bits(t["q"][seqs])
     ref = orc().decode_fp8(q, *host, bt, wl.context_lens[seqs], wl.scale)
     compare(out[seqs], ref, "decode fp8 full size", plus_floor=True)
+
+
+def test_read_probe_reads_only():
+    """The bench's read probe streams a buffer and changes nothing but, at
+    most, the first word of its sink."""
+    buf = torch.arange(1 << 20, dtype=torch.int32, device="cuda")  # 4 MiB
+    before = buf.clone()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    B.pkv_read_probe(buf, sink)
+    B.pkv_read_probe(buf[:4], sink)  # one 16-byte chunk
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+    assert int(sink[1:].abs().sum()) == 0
