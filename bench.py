@@ -175,6 +175,11 @@ def cpu_baseline(wl, t, seconds):
         spent += time.perf_counter() - t0
         layers_done += 1
     per_layer = spent / layers_done
+    # the same layer's decode on one thread
+    kc, vc = pools[0]
+    t0 = time.perf_counter()
+    orc.decode(q, kc, vc, wl.block_tables, wl.context_lens, wl.scale, nthreads=1)
+    one_thread = time.perf_counter() - t0
     return {
         "value": wl.num_seqs / per_layer, "unit": "tokens/s per layer", "cores": threads,
         "kind": "oracle",
@@ -183,7 +188,51 @@ def cpu_baseline(wl, t, seconds):
                   f"pools), fp64 C oracle on {threads} threads, {per_layer * 1e3:.1f} ms per "
                   f"layer, {spent:.1f} s in total",
         "kv_gbs": decode_bytes(wl) / per_layer / 1e9,
+        "one_thread": {"tokens_per_s_per_layer": round(wl.num_seqs / one_thread, 1),
+                       "ms_per_layer": round(one_thread * 1e3, 1)},
+        "host": {"cpu_model": cpu_model(), "nproc": os.cpu_count()},
+        "prefill": cpu_prefill_sample(orc, threads),
     }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_prefill_sample(orc, threads, cached=2048, new=128):
+    """The oracle's chunked prefill on a bounded sample shaped like one prompt
+    of the 8 x 2048 workload: 2048 cached + 128 new tokens, 32 query / 8 KV
+    heads, d 128 (seeded N(0,1) bf16 on the host), on all threads; the rate
+    in fp64 GFLOP/s of causal pairs and the time it implies for the whole
+    8 x 2048 launch (859.53 GFLOP)."""
+    import torch
+
+    g = torch.Generator().manual_seed(5)
+    hq, hkv, d = 32, 8, 128
+    nb = (cached + new + 15) // 16
+
+    def bits(*shape):
+        x = torch.randn(*shape, generator=g).to(torch.bfloat16)
+        return x.view(torch.int16).numpy().view(np.uint16)
+
+    kc, vc, q = bits(nb, hkv, 16, d), bits(nb, hkv, 16, d), bits(new, hq, d)
+    bt = np.arange(nb, dtype=np.int32)[None]
+    cu = np.array([0, new], np.int32)
+    ctx = np.array([cached + new], np.int32)
+    t0 = time.perf_counter()
+    orc.prefill(q, kc, vc, bt, cu, ctx, 1.0 / np.sqrt(d), nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * d * hq * (new * cached + new * (new + 1) / 2)
+    rate = flops / dt
+    return {"sample": f"1 prompt: {cached} cached + {new} new tokens, 32q/8kv, d 128, "
+                      f"{threads} threads", "seconds": round(dt, 3),
+            "gflops": round(rate / 1e9, 2), "implied_ms_8x2048": round(859.53e9 / rate * 1e3, 1)}
 
 
 def main():
