@@ -235,6 +235,24 @@ def test_prefill_small(d, g):
     compare(out, c.oracle_prefill(), f"prefill {wl.name}")
 
 
+@pytest.mark.parametrize("g", [1, 4])
+def test_prefill_precise_boundary(g):
+    """Waves whose last query sees under 128 keys carry P as bf16 hi + lo; the
+    rest use P rounded to bf16 with the weight sum from the same rounded
+    weights.  Prompts whose waves straddle 128 keys (0 cached and 200 new;
+    100 cached and 60 new; 127 cached and 2 new) check both kinds against the
+    oracle, including the rows just past the boundary."""
+    wl = W.make_prefill(f"prefill_boundary_g{g}", [0, 100, 127], [200, 60, 2], 8 * g, 8, 128,
+                        300 + g, spare_blocks=1)
+    c = Case(wl)
+    say(f"[gpu] prefill precise boundary G={g}")
+    c.gpu_store()
+    out = c.gpu_prefill()
+    torch.cuda.synchronize()
+    c.oracle_store()
+    compare(out, c.oracle_prefill(), f"prefill boundary G={g}")
+
+
 def test_prefill_chunked_full_size():
     """The 8 x 2048-token chunked prefill; the oracle checks sampled query rows
     (row i of prompt p is decode attention over keys 0 .. c_p + i)."""
