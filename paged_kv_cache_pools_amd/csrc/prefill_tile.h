@@ -29,8 +29,9 @@
 // block table: while a chunk is computed from one LDS buffer, the next one is
 // loaded into registers and written to the other buffer afterwards, so global
 // latency hides behind the MFMAs and one barrier per chunk suffices.  K is
-// stored row-major (one padded row per key), V transposed (one padded row per
-// head_dim element) so the A operand of P V is two 8-byte LDS reads.
+// stored row-major (one row per key, its 16-byte chunks XOR-swizzled), V
+// transposed (one padded row per head_dim element) so the A operand of P V is
+// two 8-byte LDS reads.
 //
 // Softmax: scores stay fp32; the scale (log2 e folded in) is applied in the
 // FMA that feeds exp2.  The running maximum is raised only when a chunk's
@@ -81,8 +82,8 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // into the column sums of P
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
-// A wave whose last query sees fewer keys than this carries the weights in
-// two bf16 parts.
+// A wave whose last query sits below this position (so that every row it
+// holds sees at most this many keys) carries the weights in two bf16 parts.
 constexpr int kPreciseKeys = 128;
 
 // Split two finite fp32 weights into bf16 hi and lo parts with p == hi + lo

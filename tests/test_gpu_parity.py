@@ -237,7 +237,7 @@ def test_prefill_small(d, g):
 
 @pytest.mark.parametrize("g", [1, 4])
 def test_prefill_precise_boundary(g):
-    """Waves whose last query sees under 128 keys carry P as bf16 hi + lo; the
+    """Waves whose last query sits below position 128 carry P as bf16 hi + lo; the
     rest use P rounded to bf16 with the weight sum from the same rounded
     weights.  Prompts whose waves straddle 128 keys (0 cached and 200 new;
     100 cached and 60 new; 127 cached and 2 new) check both kinds against the
