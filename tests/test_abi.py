@@ -274,9 +274,9 @@ def test_prefix_decode_workspace_sizing(lib):
         256 * 32 * (64 + 8) * 130 * 4
     assert B.pkv_decode_prefix_workspace_bytes(3, 4, 2, 64, 0, 16) == 3 * 4 * 8 * 66 * 4
     assert B.pkv_decode_prefix_workspace_bytes(3, 1, 2, 64, 33, 16) == 3 * 1 * (3 + 8) * 66 * 4
-    # automatic partitions: the split-KV choice, at most 512 tokens
+    # automatic partitions: the split-KV choice, at most 256 tokens
     assert B.pkv_decode_prefix_workspace_bytes(256, 32, 8, 128, 32768, 0) == \
-        256 * 32 * (64 + 8) * 130 * 4
+        256 * 32 * (128 + 8) * 130 * 4
     assert B.pkv_decode_prefix_workspace_bytes(1, 32, 8, 128, 32768, 0) == \
         32 * (32768 // B.pkv_decode_partition_tokens(1, 8, 32768) + 8) * 130 * 4
     assert B.pkv_decode_prefix_workspace_bytes(0, 32, 8, 128, 100, 0) == 0
