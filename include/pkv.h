@@ -15,8 +15,8 @@
  * §05.2) but not their order.  This library takes, per layer:
  *   k_cache, v_cache  bf16 [num_blocks][num_kv_heads][block_size][head_dim]
  *                     contiguous; one (block, kv head) tile is one run of
- *                     block_size * head_dim elements.  block_size is 16
- *                     ("e.g. 16 tokens per block", [NVE] §2.2).
+ *                     block_size * head_dim elements.  block_size is 16,
+ *                     the block size [NVE] §2.2 gives as its example.
  *   k, v (new tokens) bf16 [num_tokens][num_kv_heads][head_dim]
  *   slot_mapping      int32 [num_tokens]; slot = physical_block * 16 + offset
  *                     ([NVE] §2.2: the cache is managed by block or by slot).

@@ -1,9 +1,10 @@
 // store.hip -- slot-mapping scatter of new tokens' K/V into the paged pools.
 //
 // Each new token's K and V are appended to the cache at the slot the block
-// manager assigned (Nano-vLLM engine deep-dive, §2.1 "append" and §2.2
-// "manage by block or by slot"; Nano-vLLM Part 2, §05.3: a kernel writes the
-// new K/V into the cache).  A pure bit copy, bound by HBM bandwidth.
+// manager assigned (Nano-vLLM engine deep-dive, §2.1: each step appends the
+// new token's K/V to the cache; §2.2: the cache is addressed per block and
+// per slot; Nano-vLLM Part 2, §05.3: a kernel writes the new K/V into the
+// cache).  A pure bit copy, bound by HBM bandwidth.
 //
 // One thread moves one 16-byte chunk (8 bf16) of K and the matching chunk of
 // V.  Source rows [token][kv_head][head_dim] and destination rows

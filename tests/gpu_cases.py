@@ -34,9 +34,13 @@ def compare(got, ref, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS, plus_floor=False
     """got: bf16 torch tensor (GPU), ref: float64 numpy.  Returns the stats.
 
     With ``plus_floor`` each element may also differ by its own bf16 rounding
-    (|bf16(ref) - ref|) on top of ``max_abs``: outputs of magnitude 4 or more
-    cannot be held to 1e-2 by any bf16 result (half an ulp there is 0.0156),
-    which only sharpened scales produce."""
+    (|bf16(ref) - ref|) on top of ``max_abs``.  A bf16 output of magnitude 2 to
+    4 is already up to 7.8e-3 from the exact value by its own rounding, and one
+    of magnitude 4 or more up to 1.56e-2, so no bf16 result holds 1e-2 there.
+    Such outputs need a row dominated by one or two keys with |V| near 4 or
+    above: sharpened or zero scales, and FP8 caches of uniformly random codes
+    (|V| up to about 5).  Only those tests take the allowance; every test on
+    N(0,1) data at the configured 1/sqrt(d) scale is held to the plain bound."""
     g = to_f64(got)
     assert g.shape == ref.shape, (g.shape, ref.shape)
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
@@ -153,4 +157,58 @@ def compact_for_oracle(wl, t, seqs, layer=0):
     else:
         q = bits(t["q"].index_select(0, tok_t))
     return dict(kc=kc, vc=vc, bt=bt, ctx=ctx, new_lens=new_lens, slots=new_slots, k_new=k_new,
-                v_new=v_new, q=q, tok=tok)
+                v_new=v_new, q=q, tok=tok, ids=ids)
+
+
+def assert_pool_matches(dev_pool, ids, host_pool, what):
+    """The GPU pool's blocks ``ids`` (the compacted copy's block i is pool block
+    ids[i]) equal the oracle's pool bit for bit."""
+    idx = torch.from_numpy(np.asarray(ids, np.int64)).to(dev_pool.device)
+    got = dev_pool.index_select(0, idx)
+    if got.dtype == torch.bfloat16:
+        g = bits(got)
+    else:
+        g = got.cpu().numpy()
+    assert np.array_equal(g.view(np.uint8), host_pool.view(np.uint8)), what
+
+
+# ---------------------------------------------------------------------------
+# FP8 pools filled from N(0,1) data the way serving fills them: every cached
+# token's bf16 K/V row quantized by the FP8 store.  The GPU pools go through
+# pkv_store_fp8, the host pools through the oracle's store, from the same bf16
+# bits; neither side's codes or scales come from the other.
+# ---------------------------------------------------------------------------
+
+FP8_NAN = 0x7F  # an E4M3 NaN code: slots no store wrote keep it (and a NaN scale)
+
+
+def fp8_nan_pools(wl):
+    """Host FP8 pools (k codes, v codes, k scales, v scales) holding only NaN."""
+    shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    codes = [np.full(shape, FP8_NAN, np.uint8) for _ in range(2)]
+    scales = [np.full(shape[:3], np.nan, np.float32) for _ in range(2)]
+    return codes + scales
+
+
+def fp8_quantized_pools(wl, k_cache, v_cache):
+    """Quantize every cached token (pre-store live slots) of the bf16 pools
+    ``k_cache`` / ``v_cache`` (torch, any device) into FP8 pools: returns
+    (host pools written by the oracle, GPU pools written by pkv_store_fp8).
+    The two are compared bit for bit before they are returned."""
+    live = W.live_slot_mask(wl, pre_store=True)
+    slots = np.flatnonzero(live.reshape(-1)).astype(np.int32)  # slot = block * 16 + offset
+    host = fp8_nan_pools(wl)
+    dev = [torch.from_numpy(x).cuda() for x in host]
+    if slots.size:
+        nb, hkv, bs, d = k_cache.shape
+        idx = torch.from_numpy(slots.astype(np.int64)).to(k_cache.device)
+        rows_k = k_cache.permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).index_select(0, idx)
+        rows_v = v_cache.permute(0, 2, 1, 3).reshape(nb * bs, hkv, d).index_select(0, idx)
+        B.pkv_store_fp8(rows_k.cuda().contiguous(), rows_v.cuda().contiguous(),
+                        torch.from_numpy(slots).cuda(), *dev)
+        orc().store_fp8(bits(rows_k), bits(rows_v), slots, *host)
+        torch.cuda.synchronize()
+        for g, h, what in zip(dev, host, ("k codes", "v codes", "k scales", "v scales")):
+            assert np.array_equal(g.cpu().numpy().view(np.uint8), h.view(np.uint8)), \
+                f"FP8 fill differs ({what})"
+    return host, dev

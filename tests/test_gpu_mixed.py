@@ -139,11 +139,11 @@ def test_mixed_split_matches_oracle(d, g):
 
 def test_mixed_step_full_size():
     """The benchmark's iteration: 32 x 4096 decode + 4 chunks of 496 new
-    tokens; the oracle checks sampled sequences of both kinds."""
+    tokens; the oracle checks every row of both kinds."""
     wl = W.mixed_step()
     nd = 32
-    seqs = [0, 31, 32, 33]
-    say(f"[gpu] mixed step full size, oracle on seqs {seqs}")
+    seqs = range(wl.num_seqs)
+    say("[gpu] mixed step full size, oracle on every sequence")
     t = W.make_tensors(wl, device="cuda", nan_fill=True)
     h = compact_for_oracle(wl, t, seqs)
     dev = {k: t[k] for k in ("q", "k_new", "v_new", "slot_mapping", "block_tables",
@@ -165,16 +165,16 @@ def test_mixed_step_full_size():
 
 def test_mixed_tail_full_size_split():
     """The last 64-token chunk of a 4096-token prompt beside the 32 x 4096
-    decode batch: its units split by key range; the oracle checks a decode
-    sequence and the chunk."""
+    decode batch: its units split by key range; the oracle checks every
+    decode sequence and the chunk."""
     wl = W.mixed_tail()
     nd = 32
-    seqs = [5, 32]
+    seqs = range(wl.num_seqs)
     mnl, mcl = 64, int(wl.context_lens.max())
     need = B.pkv_mixed_workspace_bytes(wl.num_seqs, nd, mnl, mcl, wl.num_q_heads,
                                        wl.num_kv_heads, wl.head_dim)
     assert need > 0
-    say(f"[gpu] mixed tail full size (split, workspace {need} B), oracle on seqs {seqs}")
+    say(f"[gpu] mixed tail full size (split, workspace {need} B), oracle on every sequence")
     t = W.make_tensors(wl, device="cuda", nan_fill=True)
     h = compact_for_oracle(wl, t, seqs)
     B.pkv_store(t["k_new"], t["v_new"], t["slot_mapping"], t["k_caches"][0], t["v_caches"][0])

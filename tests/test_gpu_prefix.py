@@ -128,10 +128,11 @@ def test_prefix_precondition_rows_are_nan():
     compare(out[valid], ref[valid], "prefix decode, valid rows")
 
 
-def run_prefix_sampled(wl, seqs, what):
+def run_prefix_full(wl, what):
+    seqs = range(wl.num_seqs)
     starts, plens, mg = B.pkv_prefix_groups(wl.block_tables, wl.context_lens)
     say(f"[gpu] {what}: S={wl.num_seqs} max_ctx={wl.max_context_len}; groups "
-        f"{list(starts)} prefixes {list(plens)}; oracle on seqs {list(seqs)}")
+        f"{list(starts)} prefixes {list(plens)}; oracle on every sequence")
     t = W.make_tensors(wl, device="cuda", nan_fill=True)
     h = compact_for_oracle(wl, t, seqs)
     B.pkv_store(t["k_new"], t["v_new"], t["slot_mapping"], t["k_caches"][0], t["v_caches"][0])
@@ -143,17 +144,14 @@ def run_prefix_sampled(wl, seqs, what):
     torch.cuda.synchronize()
     orc().store(h["k_new"], h["v_new"], h["slots"], h["kc"], h["vc"])
     ref = orc().decode(h["q"], h["kc"], h["vc"], h["bt"], h["ctx"], wl.scale)
-    compare(out[list(seqs)], ref, what)
-    assert not torch.isnan(out).any()
+    compare(out, ref, what)
     return starts, plens
 
 
 def test_prefix_cont_batch_full_size():
     """256 sequences in 8 groups of 32 sharing a 2048-token prefix."""
     wl = W.cont_batch()
-    long_seq = int(np.argmax(wl.context_lens))
-    starts, plens = run_prefix_sampled(wl, sorted({0, 1, 31, 32, 100, 200, 255, long_seq}),
-                                       "prefix decode cont_batch")
+    starts, plens = run_prefix_full(wl, "prefix decode cont_batch")
     assert list(plens) == [2048] * 8
 
 
@@ -167,5 +165,5 @@ def test_prefix_cont_batch_reading_b_sorted():
     wl.block_tables = np.ascontiguousarray(bt[order])
     wl.context_lens = np.ascontiguousarray(wl.context_lens[order])
     wl.slot_mapping = np.ascontiguousarray(wl.slot_mapping[order])
-    starts, plens = run_prefix_sampled(wl, [0, 50, 128, 200, 255], "prefix decode cont_batch B")
+    starts, plens = run_prefix_full(wl, "prefix decode cont_batch B")
     assert (plens > 0).any()
