@@ -156,6 +156,29 @@ int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
                     hipStream_t stream);
 
 /*
+ * pkv_decode_attn_noalloc -- pkv_decode_attn for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments minus the workspace, same kernels and
+ * arithmetic (the output is bit-identical to pkv_decode_attn with the same
+ * partition_tokens).  The split-KV partials go to a scratch array the library
+ * owns on each GPU (a static device array of pkv_decode_noalloc_max_bytes()
+ * bytes, held until the process ends); nothing is allocated or freed, and the
+ * scratch needs no clearing (every partial is written before it is read).
+ * Returns PKV_ERR_WORKSPACE, before any launch, when the split would need
+ * more partials than the scratch holds (pkv_decode_workspace_bytes() >
+ * pkv_decode_noalloc_max_bytes()); the single-pass split (partition_tokens <
+ * 0) needs none.  All calls on one GPU share its scratch: calls that overlap
+ * in time on one GPU (other streams, other threads) race on it.
+ */
+int pkv_decode_attn_noalloc(const void *q, pkv_cache cache, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                            float scale, void *out, int32_t partition_tokens,
+                            hipStream_t stream);
+/* Bytes of the per-GPU scratch behind pkv_decode_attn_noalloc (64 MiB). */
+size_t pkv_decode_noalloc_max_bytes(void);
+
+/*
  * pkv_store_decode_attn -- one decode step of a layer in one launch: the
  * store of each sequence's new token followed by decode attention over the
  * cache including it.  Equivalent to

@@ -23,7 +23,8 @@ PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_CAPACITY, PKV_ERR_SEQUENCE = 5, 6, 7, 8
 
 # every symbol include/pkv.h and include/pkv_pool.h declare
 EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
-            "pkv_decode_attn", "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
+            "pkv_decode_attn", "pkv_decode_attn_noalloc", "pkv_decode_noalloc_max_bytes",
+            "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
             "pkv_prefill_attn", "pkv_mixed_attn", "pkv_mixed_workspace_bytes", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_store_decode_attn_fp8",
             "pkv_kv_bytes", "pkv_read_probe",
@@ -82,6 +83,11 @@ def load(path: str = LIB_PATH):
     lib.pkv_decode_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _I32, _I32, _I32, ctypes.c_float,
                                     _P, _P, _SZ, _I32, _P]
     lib.pkv_store_decode_attn.restype = ctypes.c_int
+    lib.pkv_decode_attn_noalloc.restype = ctypes.c_int
+    lib.pkv_decode_attn_noalloc.argtypes = [_P, PkvCache, _P, _I32, _P, _I32, _I32, _I32,
+                                            ctypes.c_float, _P, _I32, _P]
+    lib.pkv_decode_noalloc_max_bytes.restype = _SZ
+    lib.pkv_decode_noalloc_max_bytes.argtypes = []
     lib.pkv_store_decode_attn.argtypes = [_P, _P, _P, _P, PkvCache, _P, _I32, _P, _I32, _I32, _I32,
                                           ctypes.c_float, _P, _P, _SZ, _I32, _P]
     lib.pkv_store_decode_attn_rope.restype = ctypes.c_int
@@ -274,6 +280,41 @@ def pkv_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out,
                                workspace.numel(), int(p), _stream(q, stream)),
            "pkv_decode_attn")
     return out
+
+
+def pkv_decode_attn_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                            max_context_len: Optional[int] = None, partition_tokens: int = 0,
+                            stream=None):
+    """pkv_decode_attn without a workspace: the split-KV partials go to the
+    library's own per-GPU scratch, so nothing is allocated here or in the
+    library.  Raises PkvError (PKV_ERR_WORKSPACE) when the split needs more
+    than pkv_decode_noalloc_max_bytes()."""
+    import torch
+
+    lib = load()
+    cache = _cache(k_cache, v_cache)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    s, hq, d = q.shape
+    if tuple(out.shape) != (s, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    if block_tables.shape[0] != s or context_lens.shape[0] != s:
+        raise ValueError("block_tables / context_lens do not match q's sequence count")
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * cache.block_size
+    _check(lib.pkv_decode_attn_noalloc(q.data_ptr(), cache, block_tables.data_ptr(), max_blocks,
+                                       context_lens.data_ptr(), s, int(max_context_len), hq,
+                                       float(scale), out.data_ptr(), int(partition_tokens),
+                                       _stream(q, stream)),
+           "pkv_decode_attn_noalloc")
+    return out
+
+
+def pkv_decode_noalloc_max_bytes() -> int:
+    return int(load().pkv_decode_noalloc_max_bytes())
 
 
 def pkv_store_decode_attn(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,

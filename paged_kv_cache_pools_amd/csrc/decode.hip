@@ -3,9 +3,38 @@
 // attention itself -- scaled dot-product attention of one query token per
 // sequence over its paged K/V cache, grouped-query heads sharing a KV head --
 // is in decode_wave.h.
+#include <mutex>
+
 #include "decode_wave.h"
 
 namespace pkv {
+
+// Library-owned scratch for the entry point that allocates nothing
+// (pkv_decode_attn_noalloc): the split-KV partials live here instead of in a
+// caller's workspace.  Every GPU the library runs on holds its own copy of
+// this array until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): it
+// passes the device address noalloc_scratch() looks up.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+hipError_t noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {  // once per device, with that device current
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 // The fused store's new token in the cache's own format: bf16 rows, or FP8
 // codes plus their scales (k_store / v_store are the code pools then, and

@@ -396,7 +396,7 @@ int decode_call(const void *q, const CacheDesc &cache, const int32_t *block_tabl
                 void *workspace, size_t workspace_bytes, int32_t partition_tokens,
                 hipStream_t stream, const void *k_new, const void *v_new, const int32_t *slots,
                 const char *what, const float *rope_table = nullptr,
-                int32_t rope_positions = 0) {
+                int32_t rope_positions = 0, bool library_scratch = false) {
     int rc = check_cache(cache);
     if (rc) return rc;
     if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
@@ -426,6 +426,17 @@ int decode_call(const void *q, const CacheDesc &cache, const int32_t *block_tabl
     const int32_t parts = fused ? 1 : (max_context_len > 0 ? ceil_div(max_context_len, p) : 1);
     const size_t need =
         fused ? 0 : pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache.head_dim, max_context_len, p);
+    if (library_scratch && need > 0) {  // the partials go to the library's own array
+        if (need > pkv::kNoAllocScratchBytes)
+            return fail(PKV_ERR_WORKSPACE,
+                        "the split needs %zu bytes of partials, more than the library's %zu-byte "
+                        "scratch: use pkv_decode_attn with a workspace, or longer partitions",
+                        need, pkv::kNoAllocScratchBytes);
+        hipError_t e = pkv::noalloc_scratch(&workspace);
+        if (e != hipSuccess)
+            return fail(PKV_ERR_HIP, "%s: scratch address: %s", what, hipGetErrorString(e));
+        workspace_bytes = pkv::kNoAllocScratchBytes;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (need > 0 && !aligned16(workspace))
@@ -488,6 +499,19 @@ int pkv_decode_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
                        workspace_bytes, partition_tokens, stream, nullptr, nullptr, nullptr,
                        "pkv_decode_attn launch");
 }
+
+int pkv_decode_attn_noalloc(const void *q, pkv_cache cache, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                            float scale, void *out, int32_t partition_tokens,
+                            hipStream_t stream) {
+    return decode_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, out, nullptr, 0,
+                       partition_tokens, stream, nullptr, nullptr, nullptr,
+                       "pkv_decode_attn_noalloc launch", nullptr, 0, true);
+}
+
+size_t pkv_decode_noalloc_max_bytes(void) { return pkv::kNoAllocScratchBytes; }
 
 int pkv_store_decode_attn(const void *k, const void *v, const int32_t *slot_mapping,
                           const void *q, pkv_cache cache, const int32_t *block_tables,

@@ -65,6 +65,11 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 
+// Size of the file-scope device scratch of decode.hip, and its address on the
+// current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 struct PrefillArgs {
     const void *q;
     const void *k_cache, *v_cache;
