@@ -5,15 +5,20 @@
 
 namespace pkv {
 
+// Waves per workgroup: 8 at head_dim 128 (two per SIMD, one workgroup per
+// compute unit; every staged key chunk feeds 256 query columns), 4 at 64.
+template <int D>
+constexpr int prefill_waves() { return D == 128 ? 8 : 4; }
+
 template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ cu_new_lens, const int32_t *__restrict__ context_lens,
     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t num_qblocks, float scale_log2,
     uint16_t *__restrict__ out) {
-    using Geo = PrefillGeom<D, G>;
+    using Geo = PrefillGeom<D, G, prefill_waves<D>()>;
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Geo::BUF];
 
     // ---- work unit.  Workgroups are dealt to the 8 XCDs round-robin by their
@@ -32,14 +37,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int qb = num_qblocks - 1 - unit % num_qblocks;
     const int p = (unit / num_qblocks) % num_seqs;
     const int kvh = unit / (num_qblocks * num_seqs);
-    prefill_unit<D, G>(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens,
-                       max_blocks_per_seq, max_context_len, num_blocks, num_q_heads, num_kv_heads,
-                       scale_log2, out, p, qb, kvh, lds);
+    prefill_unit<D, G, false, false, prefill_waves<D>()>(
+        q, k_cache, v_cache, block_tables, cu_new_lens, context_lens, max_blocks_per_seq,
+        max_context_len, num_blocks, num_q_heads, num_kv_heads, scale_log2, out, p, qb, kvh, lds);
 }
 
 template <int D, int G>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
-    using Geo = PrefillGeom<D, G>;
+    using Geo = PrefillGeom<D, G, prefill_waves<D>()>;
     const int nqb = (a.max_new_len + Geo::TWG - 1) / Geo::TWG;
     const int64_t units = (int64_t)nqb * a.num_kv_heads * a.num_seqs;
     const float scale_log2 = a.scale * 1.4426950408889634f;

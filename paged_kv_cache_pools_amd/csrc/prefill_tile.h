@@ -20,8 +20,8 @@
 // shuffle (the order of the contraction index inside an MFMA is free, so both
 // operands use the same key permutation sigma below).
 //
-// Work split: a workgroup (4 wavefronts) owns one (prompt, KV head, block of
-// query tokens); each wave owns 32 query columns = 32/G tokens x the G query
+// Work split: a workgroup (NW = 4 or 8 wavefronts) owns one (prompt, KV head,
+// block of query tokens); each wave owns 32 query columns = 32/G tokens x the G query
 // heads that share the KV head, so every K/V fragment read from LDS feeds 2
 // MFMAs.  32 columns keep a wave's O^T, Q^T, scores and staging within 256
 // registers, so two workgroups share a CU and one's softmax overlaps the
@@ -115,9 +115,9 @@ constexpr float kRescaleLog2 = 8.0f;
 // their maxima (no wait on them).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <int D, int G>
+template <int D, int G, int NW = 4>
 struct PrefillGeom {
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = NW;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int COLS = 32;              // query columns per wave
     static constexpr int NT = COLS / 16;         // 16-column MFMA tiles per wave
@@ -191,7 +191,10 @@ __device__ __forceinline__ int prefill_segments(int nchunks, int slots,
 
 // One work unit of chunked prefill -- prompt p, KV head kvh, query block qb
 // (tokens qb * TWG .. +TWG of the prompt's new ones) -- run by the calling
-// workgroup of 4 waves (every thread must call).  `lds` holds 2 * BUF bytes.
+// workgroup of NW waves (every thread must call).  `lds` holds 2 * BUF bytes.
+// Eight waves share each staged key chunk between twice the query columns of
+// four, halving the staging work per matrix operation; the split and shared
+// prefix launches, whose partial results are laid out per 4-wave unit, use 4.
 //
 // SPLIT: the unit's key chunks are divided among up to split.slots
 // workgroups (segments of at least split.min_chunks chunks, evenly; a
@@ -202,7 +205,7 @@ __device__ __forceinline__ int prefill_segments(int nchunks, int slots,
 //
 // CROSS: the unit's queries and keys come from `cross` instead of prompt p
 // (p, cu_new_lens and context_lens are not read).
-template <int D, int G, bool SPLIT = false, bool CROSS = false>
+template <int D, int G, bool SPLIT = false, bool CROSS = false, int NW = 4>
 __device__ __forceinline__ void prefill_unit(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
@@ -210,7 +213,8 @@ __device__ __forceinline__ void prefill_unit(
     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks, int32_t num_q_heads,
     int32_t num_kv_heads, float scale_log2, uint16_t *__restrict__ out, int p, int qb, int kvh,
     unsigned char *lds, const SplitSlot &split = SplitSlot{}, const CrossGeom &cross = CrossGeom{}) {
-    using Geo = PrefillGeom<D, G>;
+    using Geo = PrefillGeom<D, G, NW>;
+    static_assert(!SPLIT || NW == 4, "split units use the 4-wave partial layout");
     constexpr int TW = Geo::TW, TWG = Geo::TWG, KC = Geo::KC, KSTEPS = Geo::KSTEPS, NT = Geo::NT;
     constexpr int MT = Geo::MT, KROW = Geo::KROW, VROW = Geo::VROW, CPR = Geo::CPR;
     constexpr int KLOADS = Geo::KLOADS, VITEMS = Geo::VITEMS;
@@ -447,8 +451,12 @@ __device__ __forceinline__ void prefill_unit(
                             dead |= (keep ? 0u : 1u) << ((t * NT + nt) * 4 + r);
                         }
             }
-            // per column: raw maximum
-            float mc[NT];
+            // per column: is some raw score more than 2^8 above the running
+            // maximum?  Each lane tests its own scores; only when some lane
+            // finds one (rare after the first chunks) are the column maxima
+            // taken across lanes and the maxima raised (and O rescaled), a
+            // wave-wide decision, so the branch is uniform
+            float lmax[NT];
             bool grow = false;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -457,18 +465,17 @@ __device__ __forceinline__ void prefill_unit(
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s[t][nt][r]);
-                bm = max_xor32(max_xor16(bm));
-                const float bms = (bm == kNegInf) ? kNegInf : bm * sl;
-                mc[nt] = fmaxf(m[nt], bms);
-                grow |= mc[nt] > m[nt] + kRescaleLog2;
+                lmax[nt] = bm;
+                grow |= (bm != kNegInf) && (bm * sl > m[nt] + kRescaleLog2);
             }
-            // raise the maxima (and rescale) only when some column outgrew its
-            // maximum by more than 2^8; a wave-wide decision, so the branch is uniform
             if (__any(grow)) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const float alpha = (mc[nt] == kNegInf) ? 1.f : exp2f(m[nt] - mc[nt]);
-                    m[nt] = mc[nt];
+                    const float bm = max_xor32(max_xor16(lmax[nt]));
+                    const float bms = (bm == kNegInf) ? kNegInf : bm * sl;
+                    const float mc = fmaxf(m[nt], bms);
+                    const float alpha = (mc == kNegInf) ? 1.f : exp2f(m[nt] - mc);
+                    m[nt] = mc;
                     ol[nt] *= alpha;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
