@@ -78,7 +78,9 @@ typedef enum {
     PKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
     PKV_ERR_HIP = 6,         /* the HIP runtime reported an error */
     PKV_ERR_CAPACITY = 7,    /* the block pool has too few free blocks */
-    PKV_ERR_SEQUENCE = 8     /* a sequence id is unknown, or already taken */
+    PKV_ERR_SEQUENCE = 8,    /* a sequence id is unknown, or already taken */
+    PKV_ERR_INDEX = 9        /* a block id, context length or slot is out of range, or a
+                                slot repeats (pkv_check_tables, debug-bounds builds) */
 } pkv_status;
 
 /* One layer's K and V pools.  k and v are device pointers to bf16 arrays of
@@ -314,6 +316,35 @@ int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_
                            float scale, const int32_t *group_starts, const int32_t *prefix_lens,
                            int32_t num_groups, int32_t max_group_size, void *out, void *workspace,
                            size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream);
+
+/*
+ * pkv_check_tables -- host-side check of the device-resident indices of one
+ * call, on host copies, before they are handed to a kernel.  The kernels
+ * treat these as caller preconditions: they clamp what breaks them (an
+ * out-of-range block id reads block 0, an out-of-pool slot is skipped, a
+ * context past the table is cut), which keeps every access inside the pools
+ * but gives plausible, wrong attention.  The block table maps each sequence's
+ * logical blocks to physical ones ([NVE] §2.2; [LLM4] §17.7); this checks
+ * that the mapping a batch uses is one the pools can honour:
+ *   - 0 <= context_lens[s] <= max_blocks_per_seq * 16 (and <= max_context_len
+ *     when max_context_len >= 0);
+ *   - every block id a context reaches, block_tables[s][0 .. ceil(ctx/16)-1],
+ *     lies in [0, num_blocks);
+ *   - every slot_mapping[i] (num_tokens of them; slot_mapping may be null when
+ *     num_tokens is 0) is negative (skip) or below num_blocks * 16, and no two
+ *     non-negative slots are equal.
+ * Returns PKV_OK, PKV_ERR_NULL / PKV_ERR_SHAPE for unusable arguments, or
+ * PKV_ERR_INDEX for the first violation found (sequences in order, then
+ * slots), described in pkv_last_error(); *bad_seq and *bad_index (either may
+ * be null) then name it: (s, -1) for a context length, (s, i) for entry i of
+ * row s, (-1, i) for slot i.  All pointers are host memory; nothing is
+ * launched.  Cost: O(sum of blocks reached + num_tokens) plus a sort of the
+ * slots.
+ */
+int pkv_check_tables(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                     const int32_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                     int32_t *bad_seq, int32_t *bad_index);
 
 /* Workspace bytes pkv_decode_attn_prefix needs for these sizes (0 on invalid
  * arguments). */

@@ -17,9 +17,10 @@ LIB_PATH = os.path.join(HERE, "libpkv.so")
 PKV_OK = 0
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
                 4: "PKV_ERR_ALIGN", 5: "PKV_ERR_WORKSPACE", 6: "PKV_ERR_HIP",
-                7: "PKV_ERR_CAPACITY", 8: "PKV_ERR_SEQUENCE"}
+                7: "PKV_ERR_CAPACITY", 8: "PKV_ERR_SEQUENCE", 9: "PKV_ERR_INDEX"}
 PKV_ERR_NULL, PKV_ERR_SHAPE, PKV_ERR_UNSUPPORTED, PKV_ERR_ALIGN = 1, 2, 3, 4
 PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_CAPACITY, PKV_ERR_SEQUENCE = 5, 6, 7, 8
+PKV_ERR_INDEX = 9
 
 # every symbol include/pkv.h and include/pkv_pool.h declare
 EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_bytes",
@@ -32,7 +33,8 @@ EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_by
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
             "pkv_pool_fork", "pkv_pool_free_seq", "pkv_pool_block_tables", "pkv_pool_num_free",
             "pkv_pool_refcount", "pkv_pool_seq_len", "pkv_copy_blocks",
-            "pkv_decode_attn_prefix", "pkv_decode_prefix_workspace_bytes", "pkv_prefix_groups"]
+            "pkv_decode_attn_prefix", "pkv_decode_prefix_workspace_bytes", "pkv_prefix_groups",
+            "pkv_check_tables"]
 
 
 class PkvError(RuntimeError):
@@ -143,6 +145,8 @@ def load(path: str = LIB_PATH):
     lib.pkv_prefix_groups.restype = ctypes.c_int
     lib.pkv_prefix_groups.argtypes = [_P, _I32, _P, _I32, _I32, _P, _P, _P, _P]
     lib.pkv_kv_bytes.restype = ctypes.c_uint64
+    lib.pkv_check_tables.restype = ctypes.c_int
+    lib.pkv_check_tables.argtypes = [_P, _I32, _P, _I32, _I32, _P, _I32, _I32, _P, _P]
     lib.pkv_kv_bytes.argtypes = [_I32, _I32, _I32, _I64, _I32]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [ctypes.c_int]
@@ -505,6 +509,33 @@ def pkv_prefix_groups(block_tables, context_lens, min_prefix_tokens: int = 16):
                                     int(min_prefix_tokens), _np_ptr(starts), _np_ptr(plens),
                                     ctypes.byref(ng), ctypes.byref(mg)), "pkv_prefix_groups")
     return starts[: ng.value + 1].copy(), plens[: ng.value].copy(), mg.value
+
+
+def pkv_check_tables(block_tables, context_lens, num_blocks: int, slot_mapping=None,
+                     max_context_len: int = -1):
+    """Check a call's indices on host (numpy int32) copies: block_tables
+    [S][max_blocks], context_lens [S], optional slot_mapping [T].  Returns
+    None when every context, reached block id and slot is in range and no slot
+    repeats; raises PkvError (PKV_ERR_INDEX) naming the first violation
+    otherwise, with ``bad_seq`` / ``bad_index`` set on the exception."""
+    import numpy as np
+
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.ndim != 2 or ctx.ndim != 1 or bt.shape[0] != ctx.shape[0]:
+        raise ValueError(f"block_tables {bt.shape} / context_lens {ctx.shape}")
+    slots = (np.zeros(1, np.int32) if slot_mapping is None
+             else np.ascontiguousarray(slot_mapping, dtype=np.int32))
+    t = 0 if slot_mapping is None else slots.shape[0]
+    bs, bi = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    lib = load()
+    st = lib.pkv_check_tables(_np_ptr(bt), bt.shape[1], _np_ptr(ctx), ctx.shape[0],
+                              int(max_context_len), _np_ptr(slots), t, int(num_blocks),
+                              ctypes.byref(bs), ctypes.byref(bi))
+    if st != 0:
+        err = PkvError(st, "pkv_check_tables", lib.pkv_last_error().decode())
+        err.bad_seq, err.bad_index = bs.value, bi.value
+        raise err
 
 
 def pkv_decode_attn_prefix(q, k_cache, v_cache, block_tables, context_lens, scale, out,

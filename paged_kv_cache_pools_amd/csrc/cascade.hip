@@ -299,9 +299,5 @@ hipError_t launch_cascade(const CascadeArgs &a, hipStream_t stream) {
 }
 
 // Query blocks of the prefix tiles: a tile holds 4 waves x 32 / G sequences.
-int cascade_prefix_qblocks(int32_t max_group_size, int32_t group) {
-    const int twg = 4 * (32 / group);
-    return max_group_size <= 0 ? 0 : (max_group_size + twg - 1) / twg;
-}
 
 }  // namespace pkv

@@ -202,15 +202,11 @@ static hipError_t launch_mixed_t(const MixedArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-int mixed_query_blocks(int32_t max_new_len, int32_t group) {
-    return (max_new_len + 4 * (32 / group) - 1) / (4 * (32 / group));  // TWG = 4 waves x 32/G tokens
-}
-
-size_t mixed_partial_bytes(int32_t head_dim) {
-    // every group size gives a wave 32 columns, so the size depends on D only
-    return (head_dim == 64 ? (size_t)prefill_partial_floats<64, 1>()
-                           : (size_t)prefill_partial_floats<128, 1>()) * sizeof(float);
-}
+static_assert(PrefillGeom<128, 1>::WAVES == kTileWaves && PrefillGeom<128, 1>::COLS == kTileCols,
+              "the host sizes the mixed launch for this tile");
+static_assert(mixed_partial_bytes(64) == prefill_partial_floats<64, 1>() * sizeof(float) &&
+                  mixed_partial_bytes(128) == prefill_partial_floats<128, 1>() * sizeof(float),
+              "partial result size");
 
 template <int D>
 static hipError_t launch_mixed_d(const MixedArgs &a, hipStream_t stream) {

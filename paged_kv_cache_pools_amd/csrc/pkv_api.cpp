@@ -9,6 +9,8 @@
 #include <stdarg.h>
 
 #include <algorithm>
+#include <utility>
+#include <vector>
 #include <stdio.h>
 #include <string.h>
 
@@ -316,6 +318,8 @@ const char *pkv_status_string(int status) {
         case PKV_ERR_HIP: return "PKV_ERR_HIP: the HIP runtime reported an error";
         case PKV_ERR_CAPACITY: return "PKV_ERR_CAPACITY: not enough free blocks in the pool";
         case PKV_ERR_SEQUENCE: return "PKV_ERR_SEQUENCE: unknown or duplicate sequence id";
+        case PKV_ERR_INDEX:
+            return "PKV_ERR_INDEX: a block id, context length or slot is out of range, or a slot repeats";
         default: return "unknown pkv status";
     }
 }
@@ -812,6 +816,68 @@ int pkv_prefix_groups(const int32_t *block_tables, int32_t max_blocks_per_seq,
     }
     *num_groups = g;
     *max_group_size = biggest;
+    return ok();
+}
+
+int pkv_check_tables(const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                     const int32_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                     int32_t *bad_seq, int32_t *bad_index) {
+    auto report = [&](int32_t s, int32_t i) {
+        if (bad_seq) *bad_seq = s;
+        if (bad_index) *bad_index = i;
+    };
+    report(-1, -1);
+    if (num_seqs < 0 || max_blocks_per_seq < 0 || num_tokens < 0 || num_blocks < 0)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d, max_blocks_per_seq %d, num_tokens %d, num_blocks %d",
+                    num_seqs, max_blocks_per_seq, num_tokens, num_blocks);
+    if ((num_seqs > 0 && (!context_lens || (max_blocks_per_seq > 0 && !block_tables))) ||
+        (num_tokens > 0 && !slot_mapping))
+        return fail(PKV_ERR_NULL, "context_lens, block_tables or slot_mapping is null");
+    const int64_t table_tokens = (int64_t)max_blocks_per_seq * kBlock;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t ctx = context_lens[s];
+        if (ctx < 0 || ctx > table_tokens || (max_context_len >= 0 && ctx > max_context_len)) {
+            report(s, -1);
+            return fail(PKV_ERR_INDEX,
+                        "context_lens[%d] = %d is outside [0, %lld] (table of %d blocks, "
+                        "max_context_len %d)",
+                        s, ctx, (long long)table_tokens, max_blocks_per_seq, max_context_len);
+        }
+        const int32_t *row = block_tables + (size_t)s * max_blocks_per_seq;
+        const int32_t nb = (ctx + kBlock - 1) / kBlock;
+        for (int32_t i = 0; i < nb; ++i) {
+            if (row[i] < 0 || row[i] >= num_blocks) {
+                report(s, i);
+                return fail(PKV_ERR_INDEX,
+                            "block_tables[%d][%d] = %d is outside the pool of %d blocks "
+                            "(context %d)",
+                            s, i, row[i], num_blocks, ctx);
+            }
+        }
+    }
+    const int64_t pool_slots = (int64_t)num_blocks * kBlock;
+    std::vector<std::pair<int32_t, int32_t>> live;  // (slot, token)
+    live.reserve((size_t)num_tokens);
+    for (int32_t i = 0; i < num_tokens; ++i) {
+        const int32_t slot = slot_mapping[i];
+        if (slot < 0) continue;  // a skipped token
+        if (slot >= pool_slots) {
+            report(-1, i);
+            return fail(PKV_ERR_INDEX, "slot_mapping[%d] = %d is outside the pool of %lld slots", i,
+                        slot, (long long)pool_slots);
+        }
+        live.emplace_back(slot, i);
+    }
+    std::sort(live.begin(), live.end());
+    for (size_t k = 1; k < live.size(); ++k) {
+        if (live[k].first == live[k - 1].first) {
+            const int32_t i = std::max(live[k].second, live[k - 1].second);
+            report(-1, i);
+            return fail(PKV_ERR_INDEX, "slot %d is written by tokens %d and %d", live[k].first,
+                        std::min(live[k].second, live[k - 1].second), i);
+        }
+    }
     return ok();
 }
 

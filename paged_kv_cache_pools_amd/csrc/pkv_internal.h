@@ -100,8 +100,19 @@ struct MixedArgs : PrefillArgs {
 hipError_t launch_mixed(const MixedArgs &a, hipStream_t stream);
 // Prefill query blocks of a mixed launch, and the bytes of one segment's
 // partial result.
-int mixed_query_blocks(int32_t max_new_len, int32_t group);
-size_t mixed_partial_bytes(int32_t head_dim);
+// The prefill query tile of the mixed and shared-prefix launches: 4 waves of
+// 32 columns (32 / group tokens x the group's heads each); one segment's
+// partial result of a split unit holds head_dim + 4 floats per column
+// (prefill_tile.h checks both against its geometry).
+constexpr int kTileWaves = 4;
+constexpr int kTileCols = 32;
+inline int mixed_query_blocks(int32_t max_new_len, int32_t group) {
+    const int twg = kTileWaves * (kTileCols / group);
+    return (max_new_len + twg - 1) / twg;
+}
+constexpr size_t mixed_partial_bytes(int32_t head_dim) {
+    return (size_t)kTileWaves * kTileCols * (size_t)(head_dim + 4) * sizeof(float);
+}
 
 // Decode with shared prefixes (cascade.hip): group g = sequences
 // group_starts[g] .. group_starts[g + 1] - 1 sharing their first
@@ -123,7 +134,10 @@ struct CascadeArgs {
     float *ws_ml;   // [num_seqs][num_q_heads][max_parts + kMaxSegments][2]
 };
 hipError_t launch_cascade(const CascadeArgs &a, hipStream_t stream);
-int cascade_prefix_qblocks(int32_t max_group_size, int32_t group);
+inline int cascade_prefix_qblocks(int32_t max_group_size, int32_t group) {
+    const int twg = kTileWaves * (kTileCols / group);
+    return max_group_size <= 0 ? 0 : (max_group_size + twg - 1) / twg;
+}
 
 // Whole-block copies (copy.hip).
 constexpr int kMaxCopyPools = 64;  // pool pointers per launch (kernel arguments)
