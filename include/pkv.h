@@ -491,6 +491,25 @@ uint64_t pkv_kv_bytes(int32_t layers, int32_t kv_heads, int32_t head_dim, int64_
  */
 int pkv_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
+/*
+ * Debug-bounds builds.  libpkv_debug.so is the same library built with
+ * PKV_DEBUG_BOUNDS: its kernels still clamp a broken device-resident index
+ * (see pkv_check_tables) so that no access leaves the pools, and they also
+ * record the first one they meet.  pkv_debug_status waits for the device
+ * (hipDeviceSynchronize), then fills out[4] with the first violation
+ * recorded since the last clear: out[0] what broke (0 none; 1 a block id
+ * outside [0, num_blocks); 2 a slot past the pool; 3 a context length < 0 or
+ * past the block table or max_context_len; 4 a block-copy pair outside the
+ * pool), out[1] the offending value, out[2] where it was met (the sequence
+ * for 2 and 3 from decode, the token for 2 from the store, the position in
+ * the block-table row for 1, the pair for 4), out[3] the number of reports
+ * (several threads may report one violation).  clear != 0 then resets the
+ * record.  In the normal build it returns PKV_ERR_UNSUPPORTED with out
+ * zeroed.  pkv_debug_bounds_enabled() is 1 in the debug build, else 0.
+ */
+int pkv_debug_bounds_enabled(void);
+int pkv_debug_status(uint32_t out[4], int clear);
+
 /* Static, human-readable name of a pkv_status value. */
 const char *pkv_status_string(int status);
 

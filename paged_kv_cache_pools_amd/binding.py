@@ -7,12 +7,14 @@ library is missing, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpkv.so")
+LIB_DEBUG_PATH = os.path.join(HERE, "libpkv_debug.so")
 
 PKV_OK = 0
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_SHAPE", 3: "PKV_ERR_UNSUPPORTED",
@@ -34,7 +36,7 @@ EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_by
             "pkv_pool_fork", "pkv_pool_free_seq", "pkv_pool_block_tables", "pkv_pool_num_free",
             "pkv_pool_refcount", "pkv_pool_seq_len", "pkv_copy_blocks",
             "pkv_decode_attn_prefix", "pkv_decode_prefix_workspace_bytes", "pkv_prefix_groups",
-            "pkv_check_tables"]
+            "pkv_check_tables", "pkv_debug_bounds_enabled", "pkv_debug_status"]
 
 
 class PkvError(RuntimeError):
@@ -65,6 +67,39 @@ def load(path: str = LIB_PATH):
     global _lib_handle
     if _lib_handle is not None:
         return _lib_handle
+    _lib_handle = _open(path)
+    return _lib_handle
+
+
+def load_debug(path: str = LIB_DEBUG_PATH):
+    """A separate handle on libpkv_debug.so, the debug-bounds build (its
+    kernels also record the first out-of-range index they clamp; read it with
+    pkv_debug_status).  Use it through ``using_library``."""
+    return _open(path)
+
+
+@contextlib.contextmanager
+def using_library(lib):
+    """Route this module's calls to ``lib`` (e.g. load_debug()) inside the block."""
+    global _lib_handle
+    old = _lib_handle
+    _lib_handle = lib
+    try:
+        yield lib
+    finally:
+        _lib_handle = old
+
+
+def pkv_debug_status(clear: bool = True):
+    """(kind, value, where, reports) of the first out-of-range index the
+    kernels of the loaded debug-bounds library recorded; kind 0 = none.
+    Waits for the device."""
+    out = (ctypes.c_uint32 * 4)()
+    _check(load().pkv_debug_status(out, int(bool(clear))), "pkv_debug_status")
+    return (int(out[0]), ctypes.c_int32(out[1]).value, ctypes.c_int32(out[2]).value, int(out[3]))
+
+
+def _open(path: str):
     # torch first: its HIP runtime (same soname as ROCm's) must be the one the
     # process loads, so that libpkv launches on the runtime that owns torch's
     # memory and streams.  Loading libpkv first pulls in a second copy.
@@ -145,6 +180,10 @@ def load(path: str = LIB_PATH):
     lib.pkv_prefix_groups.restype = ctypes.c_int
     lib.pkv_prefix_groups.argtypes = [_P, _I32, _P, _I32, _I32, _P, _P, _P, _P]
     lib.pkv_kv_bytes.restype = ctypes.c_uint64
+    lib.pkv_debug_bounds_enabled.restype = ctypes.c_int
+    lib.pkv_debug_bounds_enabled.argtypes = []
+    lib.pkv_debug_status.restype = ctypes.c_int
+    lib.pkv_debug_status.argtypes = [_P, ctypes.c_int]
     lib.pkv_check_tables.restype = ctypes.c_int
     lib.pkv_check_tables.argtypes = [_P, _I32, _P, _I32, _I32, _P, _I32, _I32, _P, _P]
     lib.pkv_kv_bytes.argtypes = [_I32, _I32, _I32, _I64, _I32]
@@ -152,7 +191,6 @@ def load(path: str = LIB_PATH):
     lib.pkv_status_string.argtypes = [ctypes.c_int]
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_last_error.argtypes = []
-    _lib_handle = lib
     return lib
 
 

@@ -1,6 +1,9 @@
 """Build libpkv.so (HIP, gfx950) in place: hipcc per source, then one link.
+With --debug-bounds the same sources build libpkv_debug.so with
+PKV_DEBUG_BOUNDS defined (kernels record the first out-of-range index they
+clamp; see pkv_debug_status in include/pkv.h).
 
-usage: python -m paged_kv_cache_pools_amd.build [--jobs N]
+usage: python -m paged_kv_cache_pools_amd.build [--jobs N] [--debug-bounds]
 """
 from __future__ import annotations
 
@@ -15,6 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
+BUILD_DEBUG = os.path.join(HERE, "_build_debug")
+LIB_DEBUG = os.path.join(HERE, "libpkv_debug.so")
 SOURCES = ["pkv_api.cpp", "pool.cpp", "store.hip", "decode.hip", "prefill.hip", "copy.hip",
            "mixed.hip", "cascade.hip", "probe.hip"]
 
@@ -31,11 +36,13 @@ def _hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _compile(src: str) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, debug: bool = False) -> str:
+    out_dir = BUILD_DEBUG if debug else BUILD
+    os.makedirs(out_dir, exist_ok=True)
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = ["-DPKV_DEBUG_BOUNDS"] if debug else []
+    cmd = [_hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(x for x in r.stderr.splitlines() if noise not in x)
@@ -46,19 +53,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = True) -> str:
+def build(jobs: int = 4, verbose: bool = True, debug: bool = False) -> str:
+    lib = LIB_DEBUG if debug else LIB
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, debug), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
-    build(ap.parse_args().jobs)
+    ap.add_argument("--debug-bounds", action="store_true")
+    args = ap.parse_args()
+    build(args.jobs, debug=args.debug_bounds)

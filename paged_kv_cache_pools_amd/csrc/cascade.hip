@@ -150,6 +150,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const int kvh = idx % num_kv_heads;
     const int s = (idx / num_kv_heads) % num_seqs;
     const int part = (idx / (num_kv_heads * num_seqs)) * kTailWaves + wave_id_uniform();
+    PKV_DEBUG_CHECK(kvh == 0 && part == 0 && (threadIdx.x & 63) == 0 &&
+                        (context_lens[s] < 0 || context_lens[s] > ctx_cap),
+                    kDbgContext, context_lens[s], s);
     const int ctx = min(context_lens[s], ctx_cap);
     if (part * partition_tokens >= ctx) return;  // uniform: empty however long the prefix
     const GroupView v = group_of(group_starts, prefix_lens, num_groups, num_seqs, ctx_cap, s);
@@ -299,5 +302,7 @@ hipError_t launch_cascade(const CascadeArgs &a, hipStream_t stream) {
 }
 
 // Query blocks of the prefix tiles: a tile holds 4 waves x 32 / G sequences.
+
+PKV_DEBUG_WORD_ACCESS(cascade)
 
 }  // namespace pkv

@@ -18,6 +18,7 @@
 // the kernel arguments, kMaxCopyPools per launch.
 #include <hip/hip_runtime.h>
 
+#include "pkv_device.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -41,6 +42,9 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(PoolPtrs pools, s
     const int32_t src = copies[2 * pair];
     const int32_t dst = copies[2 * pair + 1];
     // uniform over the workgroup: an invalid pair copies nothing
+    PKV_DEBUG_CHECK(((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) &&
+                        chunk == 0 && blockIdx.y == 0 && threadIdx.x == 0,
+                    kDbgCopy, (unsigned)src >= (unsigned)num_blocks ? src : dst, pair);
     if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks || src == dst)
         return;
     unsigned char *pool = pools.p[blockIdx.y];
@@ -93,5 +97,7 @@ hipError_t launch_copy_blocks(const CopyArgs &a) {
     }
     return hipSuccess;
 }
+
+PKV_DEBUG_WORD_ACCESS(copy)
 
 }  // namespace pkv

@@ -17,6 +17,8 @@ namespace pkv {
 // passes the device address noalloc_scratch() looks up.
 static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
 
+PKV_DEBUG_WORD_ACCESS(decode)
+
 hipError_t noalloc_scratch(void **ptr) {
     constexpr int kMaxDevices = 64;
     static std::mutex mu;
@@ -85,8 +87,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int c = lane % LPR;
     const int h0 = kvh * G;
 
-    int ctx = context_lens[s];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int ctx = clamp_context(context_lens[s], max_context_len, max_blocks_per_seq,
+                                  kvh == 0 && part == 0 && lane == 0, s);
     const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;
     if (ctx <= 0) {
         if (part == 0) {
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
     extern __shared__ float smem[];  // [W][G][D] acc, then [W][G] m, then [W][G] l
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
-    int ctx = context_lens[s];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int ctx = clamp_context(context_lens[s], max_context_len, max_blocks_per_seq,
+                                  kvh == 0 && threadIdx.x == 0, s);
     const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;
     const size_t row = (size_t)s * num_q_heads * D;
     attend_unit<D, G, FP8>(
@@ -184,8 +186,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     const int row_id = blockIdx.x * (blockDim.x >> 6) + wave_id_uniform();
     if (row_id >= num_seqs * num_q_heads) return;
     const int s = row_id / num_q_heads;
-    int ctx = context_lens[s];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int ctx = clamp_context(context_lens[s], max_context_len, max_blocks_per_seq, false, s);
     if (ctx <= 0) return;
     const int nparts = (ctx + partition_tokens - 1) / partition_tokens;
     if (nparts <= 1) return;

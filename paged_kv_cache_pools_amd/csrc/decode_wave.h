@@ -352,6 +352,8 @@ __device__ __forceinline__ void wave_attend(
     auto load = [&](Tile (&kb)[NL], Tile (&vb)[NL], float (&ks)[NL], float (&vs)[NL], int b) {
         int pb = bt[min(b, b_last)];
         // an out-of-range id is a caller error; read block 0 instead of faulting
+        PKV_DEBUG_CHECK((unsigned)pb >= (unsigned)num_blocks && lane == 0, kDbgBlockId, pb,
+                        min(b, b_last));
         pb = ((unsigned)pb < (unsigned)num_blocks) ? pb : 0;
         const size_t unit = (size_t)pb * num_kv_heads + kvh;
         const uint32_t bytes = b <= b_last ? (uint32_t)tile : 0u;
@@ -605,6 +607,9 @@ __device__ __forceinline__ NewToken new_token(const uint16_t *k_new, const uint1
     t.src_k = reinterpret_cast<const uint4 *>(k_new + src);
     t.src_v = reinterpret_cast<const uint4 *>(v_new + src);
     const int slot = slots[s];
+    PKV_DEBUG_CHECK(slot >= 0 && slot / kBlockTokens >= num_blocks && kvh == 0 &&
+                        (threadIdx.x & 63) == 0,
+                    kDbgSlot, slot, s);
     if (slot < 0 || slot / kBlockTokens >= num_blocks) return t;  // skipped: nothing written
     const size_t dst =
         (((size_t)(slot / kBlockTokens) * num_kv_heads + kvh) * kBlockTokens + slot % kBlockTokens) * D;
@@ -633,6 +638,9 @@ __device__ __forceinline__ NewToken new_token_fp8(const uint16_t *k_new, const u
     t.src_k = reinterpret_cast<const uint4 *>(k_new + src);
     t.src_v = reinterpret_cast<const uint4 *>(v_new + src);
     const int slot = slots[s];
+    PKV_DEBUG_CHECK(slot >= 0 && slot / kBlockTokens >= num_blocks && kvh == 0 &&
+                        (threadIdx.x & 63) == 0,
+                    kDbgSlot, slot, s);
     if (slot < 0 || slot / kBlockTokens >= num_blocks) return t;  // skipped: nothing written
     const size_t row =
         ((size_t)(slot / kBlockTokens) * num_kv_heads + kvh) * kBlockTokens + slot % kBlockTokens;

@@ -133,8 +133,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
     const int kvh = idx % num_kv_heads;
     const int row0 = cu_new_lens[s];
     const int n = cu_new_lens[s + 1] - row0;
-    int ctx = context_lens[s];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int ctx = clamp_context(context_lens[s], max_context_len, max_blocks_per_seq,
+                                  kvh == 0 && threadIdx.x == 0, s);
     if (n == 1 && ctx >= 1) {
         const size_t row = (size_t)row0 * num_q_heads * D;
         attend_unit<D, G, false>(q + row, k_cache, v_cache, nullptr, nullptr,
@@ -201,6 +201,8 @@ static hipError_t launch_mixed_t(const MixedArgs &a, hipStream_t stream) {
                        nqb, (uint16_t *)a.out, a.partials, a.seg_slots);
     return hipGetLastError();
 }
+
+PKV_DEBUG_WORD_ACCESS(mixed)
 
 static_assert(PrefillGeom<128, 1>::WAVES == kTileWaves && PrefillGeom<128, 1>::COLS == kTileCols,
               "the host sizes the mixed launch for this tile");

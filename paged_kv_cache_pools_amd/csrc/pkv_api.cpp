@@ -819,6 +819,38 @@ int pkv_prefix_groups(const int32_t *block_tables, int32_t max_blocks_per_seq,
     return ok();
 }
 
+int pkv_debug_bounds_enabled(void) {
+#ifdef PKV_DEBUG_BOUNDS
+    return 1;
+#else
+    return 0;
+#endif
+}
+
+int pkv_debug_status(uint32_t out[4], int clear) {
+    if (!out) return fail(PKV_ERR_NULL, "out is null");
+    out[0] = out[1] = out[2] = out[3] = 0u;
+    if (!pkv_debug_bounds_enabled())
+        return fail(PKV_ERR_UNSUPPORTED, "this library was built without PKV_DEBUG_BOUNDS");
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_debug_status: %s", hipGetErrorString(e));
+    hipError_t (*const words[])(uint32_t *, bool) = {
+        pkv::debug_word_store,   pkv::debug_word_decode,  pkv::debug_word_prefill,
+        pkv::debug_word_mixed,   pkv::debug_word_cascade, pkv::debug_word_copy};
+    for (auto word : words) {
+        uint32_t w[4];
+        e = word(w, clear != 0);
+        if (e != hipSuccess) return fail(PKV_ERR_HIP, "pkv_debug_status: %s", hipGetErrorString(e));
+        if (out[0] == 0u && w[0] != 0u) {
+            out[0] = w[0];
+            out[1] = w[1];
+            out[2] = w[2];
+        }
+        out[3] += w[3];
+    }
+    return ok();
+}
+
 int pkv_check_tables(const int32_t *block_tables, int32_t max_blocks_per_seq,
                      const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
                      const int32_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,

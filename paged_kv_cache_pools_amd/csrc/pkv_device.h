@@ -83,4 +83,69 @@ __device__ __forceinline__ int wave_id_uniform() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// ---- debug-bounds builds (compiled with PKV_DEBUG_BOUNDS) ----
+//
+// Device-resident indices (block ids, slots, context lengths, copy pairs) are
+// caller preconditions.  Every kernel clamps a broken one so that no access
+// leaves the pools; a debug-bounds build also records the first one a kernel
+// of this translation unit meets, in the unit's own status word:
+//   [0] what broke (kDbg*), [1] the offending value, [2] where it was met (a
+//   sequence, token, block-table position or copy pair), [3] how many reports
+//   were made in all.
+// The first report takes word 0 with a compare-and-swap; the others only
+// count.  Ordinary vector-memory atomics on global memory.  The host reads and
+// clears the words through pkv_debug_status (pkv_api.cpp).
+constexpr uint32_t kDbgBlockId = 1;  // a block id outside [0, num_blocks)
+constexpr uint32_t kDbgSlot = 2;     // a slot past the pool
+constexpr uint32_t kDbgContext = 3;  // a context length < 0 or past the table / host bound
+constexpr uint32_t kDbgCopy = 4;     // a copy pair with an id outside the pool
+
+#ifdef PKV_DEBUG_BOUNDS
+static __device__ uint32_t g_debug_word[4];
+
+__device__ __noinline__ void debug_report(uint32_t kind, int32_t value, int32_t where) {
+    if (atomicCAS(&g_debug_word[0], 0u, kind) == 0u) {
+        g_debug_word[1] = (uint32_t)value;
+        g_debug_word[2] = (uint32_t)where;
+    }
+    atomicAdd(&g_debug_word[3], 1u);
+}
+#define PKV_DEBUG_CHECK(bad, kind, value, where)             \
+    do {                                                     \
+        if (bad) ::pkv::debug_report((kind), (value), (where)); \
+    } while (0)
+// Host access to this translation unit's word: copy it out, optionally clear.
+#define PKV_DEBUG_WORD_ACCESS(name)                                                          \
+    hipError_t debug_word_##name(uint32_t *out, bool clear) {                                \
+        hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_debug_word), 4 * sizeof(uint32_t), \
+                                           0, hipMemcpyDeviceToHost);                        \
+        if (e == hipSuccess && clear) {                                                      \
+            const uint32_t zero[4] = {0u, 0u, 0u, 0u};                                       \
+            e = hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), zero, sizeof zero, 0,            \
+                                  hipMemcpyHostToDevice);                                    \
+        }                                                                                    \
+        return e;                                                                            \
+    }
+#else
+#define PKV_DEBUG_CHECK(bad, kind, value, where) \
+    do {                                         \
+    } while (0)
+#define PKV_DEBUG_WORD_ACCESS(name)                           \
+    hipError_t debug_word_##name(uint32_t *out, bool) {       \
+        out[0] = out[1] = out[2] = out[3] = 0u;               \
+        return hipSuccess;                                    \
+    }
+#endif
+
+// A context length clamped to the block table and the host-side bound (a
+// length past either is a caller error; a negative one reads as empty).
+// `reporter`: the one thread that reports a clamp in debug-bounds builds.
+__device__ __forceinline__ int clamp_context(int ctx, int32_t max_context_len,
+                                             int32_t max_blocks_per_seq, bool reporter,
+                                             int where) {
+    const int cap = min(max_context_len, max_blocks_per_seq * kBlockTokens);
+    PKV_DEBUG_CHECK(reporter && (ctx < 0 || ctx > cap), kDbgContext, ctx, where);
+    return min(ctx, cap);
+}
+
 }  // namespace pkv

@@ -152,6 +152,15 @@ struct CopyArgs {
 };
 hipError_t launch_copy_blocks(const CopyArgs &a);
 
+// The debug-bounds status words of the kernel translation units (all zero in
+// a build without PKV_DEBUG_BOUNDS): copy out [4] words, optionally clear.
+hipError_t debug_word_store(uint32_t *out, bool clear);
+hipError_t debug_word_decode(uint32_t *out, bool clear);
+hipError_t debug_word_prefill(uint32_t *out, bool clear);
+hipError_t debug_word_mixed(uint32_t *out, bool clear);
+hipError_t debug_word_cascade(uint32_t *out, bool clear);
+hipError_t debug_word_copy(uint32_t *out, bool clear);
+
 // Streaming read of `bytes` (a multiple of 16) at `buf`; writes at most one
 // word to `sink`.
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);

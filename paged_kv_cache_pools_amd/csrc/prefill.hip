@@ -42,6 +42,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void p
         max_context_len, num_blocks, num_q_heads, num_kv_heads, scale_log2, out, p, qb, kvh, lds);
 }
 
+PKV_DEBUG_WORD_ACCESS(prefill)
+
 template <int D, int G>
 static hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t stream) {
     using Geo = PrefillGeom<D, G, prefill_waves<D>()>;

@@ -237,8 +237,8 @@ __device__ __forceinline__ void prefill_unit(
         if (ctx <= 0) return;  // uniform: no prefix
     } else {
         row0 = cu_new_lens[p];
-        ctx = context_lens[p];
-        ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+        ctx = clamp_context(context_lens[p], max_context_len, max_blocks_per_seq,
+                            kvh == 0 && qb == 0 && tid == 0 && (!SPLIT || split.seg == 0), p);
         n = min(cu_new_lens[p + 1] - row0, ctx);
         c = ctx - n;
         bt = block_tables + (size_t)p * max_blocks_per_seq;
@@ -320,6 +320,7 @@ __device__ __forceinline__ void prefill_unit(
         int pb = 0;
         if (lb * kBlockTokens < ctx) {
             pb = bt[lb];
+            PKV_DEBUG_CHECK((unsigned)pb >= (unsigned)num_blocks && lane == 0, kDbgBlockId, pb, lb);
             pb = ((unsigned)pb < (unsigned)num_blocks) ? pb : 0;
         }
         return pb;
@@ -669,8 +670,7 @@ __device__ __forceinline__ void prefill_merge(
     constexpr int COLF = prefill_partial_col_floats(D), SLOT = prefill_partial_floats<D, G>();
     constexpr int SLICES = D / 8, COLS_PER_WG = 256 / SLICES;
     const int row0 = cu_new_lens[p];
-    int ctx = context_lens[p];
-    ctx = min(ctx, min(max_context_len, max_blocks_per_seq * kBlockTokens));
+    const int ctx = clamp_context(context_lens[p], max_context_len, max_blocks_per_seq, false, p);
     const int n = min(cu_new_lens[p + 1] - row0, ctx);
     const int c = ctx - n;
     const int T0 = qb * TWG;

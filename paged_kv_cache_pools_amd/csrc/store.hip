@@ -38,6 +38,7 @@ __global__ __launch_bounds__(256) void store_kernel(const uint4 *__restrict__ k,
         const int32_t block = slot / kBlockTokens;
         // slot < 0 is a padding token; a block past the pool is never written
         if (slot < 0 || block >= num_blocks) {
+            PKV_DEBUG_CHECK(slot >= 0 && rem == 0, kDbgSlot, slot, t);
             asm volatile("" ::"v"(kk.x), "v"(kk.y), "v"(kk.z), "v"(kk.w), "v"(vv.x), "v"(vv.y),
                          "v"(vv.z), "v"(vv.w));
             continue;
@@ -75,6 +76,8 @@ __global__ __launch_bounds__(256) void store_fp8_kernel(
     const uint2 kq = quantize8<LPR>(kk, ksc);
     const uint2 vq = quantize8<LPR>(vv, vsc);
     // slot < 0 is a padding token; a block past the pool is never written
+    PKV_DEBUG_CHECK(in_range && slot >= 0 && slot / kBlockTokens >= num_blocks && h == 0 && c == 0,
+                    kDbgSlot, slot, t);
     if (!in_range || slot < 0 || slot / kBlockTokens >= num_blocks) return;
     const size_t dst_row = ((size_t)(slot / kBlockTokens) * num_kv_heads + h) * kBlockTokens +
                            slot % kBlockTokens;
@@ -103,6 +106,8 @@ hipError_t launch_store_fp8(const StoreFp8Args &a, hipStream_t stream) {
                            a.num_blocks, a.num_kv_heads);
     return hipGetLastError();
 }
+
+PKV_DEBUG_WORD_ACCESS(store)
 
 hipError_t launch_store(const StoreArgs &a, hipStream_t stream) {
     if (a.num_tokens == 0) return hipSuccess;

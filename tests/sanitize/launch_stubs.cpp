@@ -32,3 +32,18 @@ hipError_t noalloc_scratch(void **ptr) {
 }  // namespace pkv
 
 extern "C" const char *hipGetErrorString(hipError_t) { return "hip error (stub)"; }
+
+namespace pkv {
+// the status words of a build without PKV_DEBUG_BOUNDS: always zero
+#define PKV_STUB_WORD(name)                                \
+    hipError_t debug_word_##name(uint32_t *out, bool) {    \
+        out[0] = out[1] = out[2] = out[3] = 0u;            \
+        return hipSuccess;                                 \
+    }
+PKV_STUB_WORD(store)
+PKV_STUB_WORD(decode)
+PKV_STUB_WORD(prefill)
+PKV_STUB_WORD(mixed)
+PKV_STUB_WORD(cascade)
+PKV_STUB_WORD(copy)
+}  // namespace pkv

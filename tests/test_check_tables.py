@@ -120,3 +120,11 @@ def test_random_tables_against_brute_force(seed):
         B.pkv_check_tables(bt, ctx, nb, slots, max_context_len=mcl)
     else:
         expect_bad(*want, bt, ctx, nb, slots, max_context_len=mcl)
+
+
+def test_debug_status_needs_the_debug_build():
+    """The normal build records nothing and says so."""
+    with pytest.raises(B.PkvError) as e:
+        B.pkv_debug_status()
+    assert e.value.status == B.PKV_ERR_UNSUPPORTED
+    assert B.load().pkv_debug_bounds_enabled() == 0
