@@ -111,9 +111,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                                     bt_row, num_blocks, num_kv_heads, s, kvh, ctx);
 
     float acc[G][8], mg[G], lg[G];
-    wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
-                           num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end, nt,
-                           rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
+    if (FP8 && ctx > kExactDecodeKeys)  // uniform: bf16 weights in P V (see wave_attend)
+        wave_attend<D, G, FP8, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
+                                    num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
+                                    nt, rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
+    else
+        wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
+                               num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end, nt,
+                               rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
 
     if (nparts == 1) {
 #pragma unroll
