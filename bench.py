@@ -12,8 +12,10 @@ permutation, resident in HBM before the timed region.
 
 Prints ONE JSON line.  ``value`` is the step's algorithmic KV-cache traffic
 (decode reads plus the store's reads and writes, all layers) / step time, in
-GB/s.  ``roofline`` is the per-layer launch, timed with HIP events on the
-stream it runs on.  The chunked-prefill leg and the fp64 oracle on the host
+GB/s.  ``roofline`` is the per-layer launch: its algorithmic bytes over its
+average duration in the timed region (HIP events on the stream the launches
+run on; the region holds nothing else), with an event-bracketed pass beside
+it.  The chunked-prefill leg and the fp64 oracle on the host
 cores are reported beside it.
 """
 from __future__ import annotations
@@ -368,7 +370,17 @@ def main():
     value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
     # the timed launch per layer: decode alone, or the fused store + decode
     launch_bytes = dbytes if args.separate else dbytes + sbytes
-    achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
+    # The roofline's launch duration: the timed region holds nothing but the
+    # K x L fused launches, so its length over K x L is their average duration
+    # (dispatch gaps between launches included).  With --separate the region
+    # also holds the store launches, and the event-bracketed decode launches
+    # of pass (2) give the duration instead.
+    launch_ms = dec_avg_ms if args.separate else ms_per_step / L
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+    launch_timing = {"source": ("events around each decode launch (pass 2)" if args.separate
+                                else "timed region / launches"),
+                     "timed_region_us_per_launch": round(ms_per_step / L * 1e3, 2),
+                     "event_bracketed": dec_stats}
     kernel = (f"decode_fused_kernel<{D},{Hq // Hkv}>" if P < 0
               else f"decode_split_kernel<{D},{Hq // Hkv}>+decode_reduce_kernel<{D}>")
     if not args.separate:
@@ -396,12 +408,13 @@ def main():
                                           else "pkv_store_decode_attn (store fused)")},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
-        "decode_us_per_layer": round(dec_avg_ms * 1e3, 2),  # the timed launch (see kernel)
+        "decode_us_per_layer": round(launch_ms * 1e3, 2),  # the timed launch (see kernel)
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(kernel),
-                     "algorithmic_bytes_per_launch": launch_bytes, "launch_timing": dec_stats},
+                     "algorithmic_bytes_per_launch": launch_bytes,
+                     "launch_us": round(launch_ms * 1e3, 2), "launch_timing": launch_timing},
         "wall_s_timed": round(wall, 3),
     }
     if rope is not None:
@@ -571,7 +584,14 @@ def bench_fp8(args, torch, B, W, dev):
     st_bytes = S * 2 * Hkv * D * 2 + S * 2 * Hkv * (D + 4) + 4 * S
     step_gbs = L * (dec_bytes + st_bytes) / (ms_per_step * 1e-3) / 1e9
     launch_bytes = dec_bytes if args.separate else dec_bytes + st_bytes
-    achieved = launch_bytes / (dec_ms * 1e-3) / 1e9
+    # as for the bf16 step: the timed region's average launch duration, or the
+    # event-bracketed decode launches with --separate
+    launch_ms = dec_ms if args.separate else ms_per_step / L
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+    launch_timing = {"source": ("events around each decode launch" if args.separate
+                                else "timed region / launches"),
+                     "timed_region_us_per_launch": round(ms_per_step / L * 1e3, 2),
+                     "event_bracketed": dec_stats}
     kernel = f"decode_fused_kernel<{D},{Hq // Hkv},fp8>" if P < 0 else \
         f"decode_split_kernel<{D},{Hq // Hkv},fp8>+decode_reduce_kernel<{D}>"
     del pools, q, kn, vn, outs
@@ -587,13 +607,14 @@ def bench_fp8(args, torch, B, W, dev):
         ("fused_ms_per_step" if args.separate else "separate_ms_per_step"): round(other_ms, 4),
         "tokens_per_s_per_layer": round(S * L / (ms_per_step * 1e-3), 1),
         "kv_gbs": round(step_gbs, 2), "hbm_peak_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-        "decode_us_per_layer": round(dec_ms * 1e3, 2),  # the timed launch (see kernel)
+        "decode_us_per_layer": round(launch_ms * 1e3, 2),  # the timed launch (see kernel)
         "roofline": {"bound": "hbm",
                      "kernel": kernel + ("" if args.separate else " (fused store)"),
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(kernel + ("" if args.separate else " (fused store)")),
-                     "algorithmic_bytes_per_launch": launch_bytes, "launch_timing": dec_stats},
+                     "algorithmic_bytes_per_launch": launch_bytes,
+                     "launch_us": round(launch_ms * 1e3, 2), "launch_timing": launch_timing},
     }
 
 
