@@ -3,9 +3,10 @@
 // attention itself -- scaled dot-product attention of one query token per
 // sequence over its paged K/V cache, grouped-query heads sharing a KV head --
 // is in decode_wave.h.
+#include <algorithm>
 #include <mutex>
 
-#include "decode_wave.h"
+#include "decode_fp8_mfma.h"
 
 namespace pkv {
 
@@ -110,15 +111,49 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         nt = make_new_token<D, FP8>(k_new, v_new, slots, k_store, v_store, ks_store, vs_store,
                                     bt_row, num_blocks, num_kv_heads, s, kvh, ctx);
 
+    if constexpr (FP8) {
+        if (ctx > kExactDecodeKeys) {  // uniform: the matrix-core path
+            extern __shared__ float smem[];  // [waves] rings of Fp8Mma<D>::WAVE_BYTES
+            using Mma = Fp8Mma<D>;
+            unsigned char *ring =
+                reinterpret_cast<unsigned char *>(smem) + wave_id_uniform() * Mma::WAVE_BYTES;
+            f32x4_t o[Mma::MT];
+            float mr, lr;
+            wave_attend_fp8_mfma<D, G>(q + (size_t)s * num_q_heads * D,
+                                       static_cast<const uint8_t *>(k_cache),
+                                       static_cast<const uint8_t *>(v_cache), k_scale, v_scale,
+                                       bt_row, num_blocks, num_q_heads, num_kv_heads, scale_log2,
+                                       kvh, t_begin, t_end, nt, ring, o, mr, lr);
+            const int col = lane & 15, grp = lane >> 4;  // head, dimensions 16m + 4grp ..
+            if (col < G) {
+                const size_t hrow = (size_t)s * num_q_heads + h0 + col;
+                if (nparts == 1) {
+                    const float inv = 1.f / lr;
+                    uint16_t *dst = out + hrow * D + 4 * grp;
+#pragma unroll
+                    for (int m = 0; m < Mma::MT; ++m)
+                        *reinterpret_cast<uint2 *>(dst + 16 * m) =
+                            make_uint2(pack_bf16x2(o[m][0] * inv, o[m][1] * inv),
+                                       pack_bf16x2(o[m][2] * inv, o[m][3] * inv));
+                } else {
+                    const size_t r = hrow * max_parts + part;
+#pragma unroll
+                    for (int m = 0; m < Mma::MT; ++m)
+                        *reinterpret_cast<float4 *>(ws_out + r * D + 16 * m + 4 * grp) =
+                            make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
+                    if (grp == 0) {
+                        ws_ml[r * 2 + 0] = mr;
+                        ws_ml[r * 2 + 1] = lr;
+                    }
+                }
+            }
+            return;
+        }
+    }
     float acc[G][8], mg[G], lg[G];
-    if (FP8 && ctx > kExactDecodeKeys)  // uniform: bf16 weights in P V (see wave_attend)
-        wave_attend<D, G, FP8, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
-                                    num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
-                                    nt, rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
-    else
-        wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
-                               num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end, nt,
-                               rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
+    wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks, num_q_heads,
+                           num_kv_heads, scale_log2, s, kvh, t_begin, t_end, nt,
+                           rope_at<D>(rope_table, rope_positions, ctx), acc, mg, lg);
 
     if (nparts == 1) {
 #pragma unroll
@@ -162,13 +197,29 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
     const uint16_t *__restrict__ v_new, const int32_t *__restrict__ slots, void *k_store,
     void *v_store, float *ks_store, float *vs_store, const float *__restrict__ rope_table,
     int32_t rope_positions) {
-    extern __shared__ float smem[];  // [W][G][D] acc, then [W][G] m, then [W][G] l
+    // [W][G][D] acc, then [W][G] m, then [W][G] l; FP8: [W] rings of
+    // Fp8Mma<D>::WAVE_BYTES (the matrix-core path)
+    extern __shared__ float smem[];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
     const int ctx = clamp_context(context_lens[s], max_context_len, max_blocks_per_seq,
                                   kvh == 0 && threadIdx.x == 0, s);
     const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;
     const size_t row = (size_t)s * num_q_heads * D;
+    if constexpr (FP8) {
+        if (ctx > kExactDecodeKeys) {  // uniform over the workgroup: the matrix-core path
+            attend_unit_fp8_mfma<D, G>(
+                q + row, static_cast<const uint8_t *>(k_cache),
+                static_cast<const uint8_t *>(v_cache), k_scale, v_scale, bt_row, ctx, num_blocks,
+                num_q_heads, num_kv_heads, scale_log2, out + row, kvh, blockDim.x >> 6,
+                reinterpret_cast<unsigned char *>(smem), [&]() {
+                    return make_new_token<D, FP8>(k_new, v_new, slots, k_store, v_store,
+                                                  ks_store, vs_store, bt_row, num_blocks,
+                                                  num_kv_heads, s, kvh, ctx);
+                });
+            return;
+        }
+    }
     attend_unit<D, G, FP8>(
         q + row, k_cache, v_cache, k_scale, v_scale, bt_row, ctx, num_blocks, num_q_heads,
         num_kv_heads, scale_log2, out + row, kvh, blockDim.x >> 6, smem,
@@ -219,12 +270,32 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     for (int e = 0; e < E; ++e) o[e] = (uint16_t)f32_to_bf16_rne(a[e] * inv);
 }
 
+// Dynamic LDS of the FP8 kernels: a ring of Fp8Mma<D>::WAVE_BYTES per wave,
+// more than the default 64 KiB a launch may ask for at 8 waves; the kernels
+// are allowed the most they can use once per process.
+template <int D, int G>
+static void allow_fp8_lds() {
+    static const bool done = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_fused_kernel<D, G, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kMaxDecodeWaves * Fp8Mma<D>::WAVE_BYTES);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_split_kernel<D, G, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  4 * Fp8Mma<D>::WAVE_BYTES);
+        (void)hipGetLastError();  // an attribute this runtime ignores is not a launch error
+        return true;
+    }();
+    (void)done;
+}
+
 template <int D, int G, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const float scale_log2 = a.scale * 1.4426950408889634f;
+    if constexpr (FP8) allow_fp8_lds<D, G>();
     if (a.fused_waves > 0) {
         const int W = a.fused_waves;
-        const size_t lds = (size_t)W * G * (D + 2) * sizeof(float);
+        size_t lds = (size_t)W * G * (D + 2) * sizeof(float);
+        if constexpr (FP8) lds = std::max(lds, (size_t)W * Fp8Mma<D>::WAVE_BYTES);
         hipLaunchKernelGGL((decode_fused_kernel<D, G, FP8>), dim3(a.num_kv_heads, a.num_seqs),
                            dim3(64 * W), lds, stream, (const uint16_t *)a.q, a.k_cache, a.v_cache,
                            a.k_scale, a.v_scale, a.block_tables, a.context_lens, a.max_blocks_per_seq,
@@ -237,7 +308,8 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const int waves = a.max_parts >= 4 ? 4 : (a.max_parts >= 2 ? 2 : 1);
     const unsigned groups = (unsigned)((a.max_parts + waves - 1) / waves);
     const dim3 grid(groups * (unsigned)a.num_kv_heads * (unsigned)a.num_seqs);
-    hipLaunchKernelGGL((decode_split_kernel<D, G, FP8>), grid, dim3(64 * waves), 0, stream,
+    const size_t split_lds = FP8 ? (size_t)waves * Fp8Mma<D>::WAVE_BYTES : 0;
+    hipLaunchKernelGGL((decode_split_kernel<D, G, FP8>), grid, dim3(64 * waves), split_lds, stream,
                        (const uint16_t *)a.q, a.k_cache, a.v_cache, a.k_scale, a.v_scale,
                        a.block_tables, a.context_lens,
                        a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.num_seqs,

@@ -69,8 +69,10 @@ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-// Contexts of at most this many keys keep fp32 weights in the FP8 decode's
-// P V (see wave_attend's PVDOT).
+// FP8 decode of a context of at most this many keys runs wave_attend (fp32
+// weights); longer ones run on the matrix cores with bf16 weights
+// (decode_fp8_mfma.h), where a few comparable keys could otherwise leave much
+// of the 1e-2 absolute budget to the weights' rounding.
 constexpr int kExactDecodeKeys = 128;
 
 // a.lo * b.lo + a.hi * b.hi + c on two packed bf16 pairs (v_dot2_f32_bf16)
@@ -295,19 +297,7 @@ __device__ __forceinline__ void patch_fp8_row(uint2 (&kt)[NL], uint2 (&vt)[NL], 
 // bf16 one -- 8 elements per lane per load, 8-byte loads of 512 bytes per
 // instruction -- and the K codes become bf16 pairs for the same dot products;
 // a token's K scale multiplies its scores, its V scale its weights.
-//
-// PVDOT (FP8 only) runs P V as bf16 dot products over pairs of a lane's
-// tokens: each weight times its token's V scale is rounded to bf16 (nearest
-// even), the two tokens' codes become bf16 pairs (a_e, b_e) -- exact, every
-// E4M3 value is a bf16 value -- and one v_dot2 adds both tokens' terms of an
-// element, half the multiply-adds of the fp32 path.  The weight sum is taken
-// from the same rounded weights (rounded weight / V scale), so the output is
-// a convex combination of V rows whose weights are off by at most 2^-9
-// relative, and a row dominated by one key returns that key's V with no
-// weight error.  Callers keep the fp32 path for contexts of at most
-// kExactDecodeKeys keys, where a handful of comparable keys could otherwise
-// leave most of the 1e-2 absolute budget to rounding.
-template <int D, int G, bool FP8 = false, bool PVDOT = false>
+template <int D, int G, bool FP8 = false>
 __device__ __forceinline__ void wave_attend(
     const uint16_t *__restrict__ q, const void *k_cache, const void *v_cache,
     const float *k_scale, const float *v_scale, const int32_t *__restrict__ bt,
@@ -511,30 +501,7 @@ __device__ __forceinline__ void wave_attend(
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
             pr[j] = fast_exp2(sc[j] - m_use);
-            if constexpr (!PVDOT) psum += pr[j];
-        }
-        // PVDOT: the weights as the products use them, two tokens per word,
-        // and their sum from the same rounded values
-        uint32_t wp[NL / 2];
-        if constexpr (PVDOT) {
-#pragma unroll
-            for (int jp = 0; jp < NL / 2; ++jp) {
-                const int j0 = 2 * jp, j1 = 2 * jp + 1;
-                float w0 = pr[j0] * vs[j0], w1 = pr[j1] * vs[j1];
-                float r0 = __builtin_amdgcn_rcpf(vs[j0]), r1 = __builtin_amdgcn_rcpf(vs[j1]);
-                if (partial) {  // rows past the end: NaN scales stay out
-                    const bool live0 = tb + j0 * TPL + row < t_end;
-                    const bool live1 = tb + j1 * TPL + row < t_end;
-                    w0 = live0 ? w0 : 0.f;
-                    w1 = live1 ? w1 : 0.f;
-                    r0 = live0 ? r0 : 0.f;
-                    r1 = live1 ? r1 : 0.f;
-                }
-                wp[jp] = __builtin_bit_cast(uint32_t,
-                                            __builtin_convertvector((float2_t){w0, w1}, bf16x2_t));
-                psum = fmaf(bf16_lo(wp[jp]), r0, psum);
-                psum = fmaf(bf16_hi(wp[jp]), r1, psum);
-            }
+            psum += pr[j];
         }
         l = l * alpha + psum;
         m = m_new;
@@ -547,38 +514,6 @@ __device__ __forceinline__ void wave_attend(
 #pragma unroll
                 for (int x = 0; x < 8; ++x) acc[g][x] *= a;
             });
-        }
-        if constexpr (PVDOT) {
-#pragma unroll
-            for (int jp = 0; jp < NL / 2; ++jp) {
-                const int j0 = 2 * jp, j1 = 2 * jp + 1;
-                uint2 ca = vt[j0], cb = vt[j1];
-                if (partial) {  // rows past the end: their codes (NaN) stay out
-                    const bool live0 = tb + j0 * TPL + row < t_end;
-                    const bool live1 = tb + j1 * TPL + row < t_end;
-                    ca.x = live0 ? ca.x : 0u;
-                    ca.y = live0 ? ca.y : 0u;
-                    cb.x = live1 ? cb.x : 0u;
-                    cb.y = live1 ? cb.y : 0u;
-                }
-                // bytes interleaved by token, then bf16 pairs (a_e, b_e)
-                const uint32_t x0 = __builtin_amdgcn_perm(cb.x, ca.x, 0x05010400u);
-                const uint32_t x1 = __builtin_amdgcn_perm(cb.x, ca.x, 0x07030602u);
-                const uint32_t x2 = __builtin_amdgcn_perm(cb.y, ca.y, 0x05010400u);
-                const uint32_t x3 = __builtin_amdgcn_perm(cb.y, ca.y, 0x07030602u);
-                const uint32_t vp[8] = {fp8x2_to_bf16<false>(x0), fp8x2_to_bf16<true>(x0),
-                                        fp8x2_to_bf16<false>(x1), fp8x2_to_bf16<true>(x1),
-                                        fp8x2_to_bf16<false>(x2), fp8x2_to_bf16<true>(x2),
-                                        fp8x2_to_bf16<false>(x3), fp8x2_to_bf16<true>(x3)};
-                static_for<G>([&](auto gc) {
-                    constexpr int g = decltype(gc)::value;
-                    const uint32_t wg = __float_as_uint(
-                        row_bcast<Geo, g * LPH>(__uint_as_float(wp[jp]), row_base));
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) acc[g][x] = dot2_bf16(wg, vp[x], acc[g][x]);
-                });
-            }
-            return;
         }
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
@@ -806,16 +741,9 @@ __device__ __forceinline__ void attend_unit(
     float *lds_l = lds_m + W * G;
     if (b0 < b1) {
         float acc[G][8], mg[G], lg[G];
-        if (FP8 && ctx > kExactDecodeKeys)  // uniform over the workgroup
-            wave_attend<D, G, FP8, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row,
-                                        num_blocks, num_q_heads, num_kv_heads, scale_log2, 0, kvh,
-                                        b0 * kBlockTokens, min(b1 * kBlockTokens, ctx), nt, rope,
-                                        acc, mg, lg);
-        else
-            wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
-                                   num_q_heads, num_kv_heads, scale_log2, 0, kvh,
-                                   b0 * kBlockTokens, min(b1 * kBlockTokens, ctx), nt, rope, acc,
-                                   mg, lg);
+        wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale, bt_row, num_blocks,
+                               num_q_heads, num_kv_heads, scale_log2, 0, kvh, b0 * kBlockTokens,
+                               min(b1 * kBlockTokens, ctx), nt, rope, acc, mg, lg);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (g % TPL == row) {
