@@ -431,9 +431,9 @@ int pkv_store_fp8(const void *k, const void *v, const int32_t *slot_mapping, int
 
 /*
  * pkv_decode_partition_tokens_fp8 -- the automatic work split of
- * pkv_decode_attn_fp8 (same encoding as pkv_decode_partition_tokens; the
- * single-pass kernel gets up to twice the waves, for FP8's higher arithmetic
- * per byte).  pkv_decode_workspace_bytes(..., 0) bounds its workspace too.
+ * pkv_decode_attn_fp8 (same encoding as pkv_decode_partition_tokens, and at
+ * present the same choice).  pkv_decode_workspace_bytes(..., 0) bounds its
+ * workspace too.
  */
 int32_t pkv_decode_partition_tokens_fp8(int32_t num_seqs, int32_t num_kv_heads,
                                         int32_t max_context_len);

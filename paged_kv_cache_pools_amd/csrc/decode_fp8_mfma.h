@@ -47,6 +47,10 @@
 
 #include "decode_wave.h"
 
+#ifndef PKV_FP8_RING
+#define PKV_FP8_RING 4
+#endif
+
 namespace pkv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -72,13 +76,13 @@ struct Fp8Mma {
     static constexpr int CH = D / 16;                    // 16-byte chunks per token row
     static constexpr int TILE = kBlockTokens * D;        // bytes of a block's K (or V) codes
     static constexpr int SLOT = 2 * TILE + 2 * kBlockTokens * 4;  // K, V, 16 K + 16 V scales
-    static constexpr int RING = 4;                       // slots per wave
+    static constexpr int RING = PKV_FP8_RING;            // slots per wave (even)
     static constexpr int WAVE_BYTES = RING * SLOT;       // LDS per wave
     static constexpr int DMA = TILE / 1024;              // 1 KiB loads per code tile
     static constexpr int OPS = 2 * DMA + 2;              // vector-memory instructions per block
     static constexpr int KS = D / 32;                    // k-steps of the scores
     static constexpr int MT = D / 16;                    // 16-dimension tiles of the output
-    static_assert(2 * OPS < 16, "the landed-block wait is a 4-bit vmcnt");
+    static_assert(RING % 2 == 0 && (RING - 2) * OPS < 64, "ring");
     // LDS offset, within a code tile, of chunk q of token row t
     static __device__ __forceinline__ int chunk(int t, int q) {
         return (t * CH + (q ^ (t & (CH - 1)))) * 16;
@@ -86,7 +90,7 @@ struct Fp8Mma {
 };
 
 // s_waitcnt immediates (expcnt and the counters not named left at their maxima)
-constexpr int waitcnt_vm(int n) { return 0x0F70 | n; }  // vmcnt <= n (n < 16)
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }  // vmcnt <= n < 64
 constexpr int kWaitLgkm0 = 0xC07F;                       // lgkmcnt == 0
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char *lds,
@@ -311,35 +315,42 @@ __device__ __forceinline__ void wave_attend_fp8_mfma(
         }
     };
 
-    // ring: block b_begin + k in slot k % 4; three blocks in flight
-    issue(b_begin, 0);
-    issue(b_begin + 1, 1);
-    issue(b_begin + 2, 2);
+    // ring: block b_begin + k in slot k % RING; RING - 1 blocks in flight
+    constexpr int RING = Geo::RING, AHEAD = (RING - 2) * OPS;
+#pragma unroll
+    for (int k = 0; k < RING - 1; ++k) issue(b_begin + k, k);
     auto pair_step = [&](int i, auto s0c) {
         constexpr int S0 = decltype(s0c)::value;  // slot of the pair's first block
         const int bx = b_begin + i;
         const bool has_y = i + 1 < nblk;  // uniform
         unsigned char *sx = ring + S0 * SLOT;
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * OPS));  // block bx has landed
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(AHEAD));  // block bx has landed
         patch(bx, sx);
         const uint2 wx = scores(bx, sx);
-        issue(bx + 3, (S0 + 3) % 4);  // the previous pair's second slot is free
+        issue(bx + RING - 1, (S0 + RING - 1) % RING);  // the previous pair's second slot
         uint2 wy = make_uint2(0u, 0u);
         if (has_y) {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * OPS));  // block bx + 1 has landed
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(AHEAD));  // block bx + 1 has landed
             patch(bx + 1, sx + SLOT);
             wy = scores(bx + 1, sx + SLOT);
         }
         pv(sx, bx, has_y, wx, wy);
         if (has_y) {
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this pair's reads are done
-            issue(bx + 4, S0);
+            issue(bx + RING, S0);
         }
     };
-    for (int i = 0; i < nblk; i += 4) {
-        pair_step(i, std::integral_constant<int, 0>{});
-        if (i + 2 >= nblk) break;
-        pair_step(i + 2, std::integral_constant<int, 2>{});
+    for (int i = 0; i < nblk; i += RING) {
+        bool done = false;
+        static_for<RING / 2>([&](auto pc) {
+            constexpr int P = decltype(pc)::value;
+            if (done || i + 2 * P >= nblk) {
+                done = true;
+                return;
+            }
+            pair_step(i + 2 * P, std::integral_constant<int, 2 * P>{});
+        });
+        if (done) break;
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no load left in flight into the ring
 

@@ -125,8 +125,9 @@ int32_t partition_for(int64_t units, int32_t max_context_len) {
 // split is the better choice.  Single-pass needs enough (sequence, KV head)
 // units to fill the GPU by itself and contexts short enough that one
 // workgroup per unit is not a straggler; it then gives each unit enough waves
-// for kTargetWaves in all (1024 = four per CU for bf16; the FP8 path, with
-// twice the arithmetic per byte, runs best at 2048 = two per SIMD), at least
+// for kTargetWaves in all (1024 = four per CU; the FP8 kernels too, since
+// their products moved to the matrix cores: 32 x 4096 GQA FP8 ran 49.0 us at
+// 4 waves against 50.1 at 8, 53.0-56.4 at 5-7), at least
 // four (one per SIMD of the compute unit a workgroup lands on) and at least
 // one block per wave.  A wave of the longest context must not walk more than
 // kMaxWaveTokens: with many units of mixed lengths the choice would be one
@@ -357,7 +358,8 @@ namespace {
 int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, bool fp8) {
     if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
     const int64_t units = (int64_t)num_seqs * num_kv_heads;
-    const int32_t w = fused_waves_for(units, max_context_len, fp8 ? 2048 : 1024);
+    (void)fp8;  // the same split for both caches
+    const int32_t w = fused_waves_for(units, max_context_len, 1024);
     if (w > 0) return -w;
     return partition_for(units, max_context_len);
 }

@@ -240,8 +240,11 @@ def test_fp8_validation(lib):
 
 
 def test_fp8_partition_heuristic(lib):
-    # the 32 x 4096 GQA batch: single pass with 8 waves (twice the bf16 choice)
-    assert B.pkv_decode_partition_tokens_fp8(32, 8, 4096) == -8
+    # the 32 x 4096 GQA batch: single pass with 4 waves, as for bf16
+    assert B.pkv_decode_partition_tokens_fp8(32, 8, 4096) == -4
+    for s, h, ctx in ((32, 8, 4096), (64, 8, 2048), (16, 8, 1000), (3, 2, 50000)):
+        assert B.pkv_decode_partition_tokens_fp8(s, h, ctx) == \
+            B.pkv_decode_partition_tokens(s, h, ctx)
     for s, h, ctx in ((1, 1, 1), (2, 2, 37), (256, 8, 32768), (16, 32, 2048), (64, 8, 16)):
         p = B.pkv_decode_partition_tokens_fp8(s, h, ctx)
         assert (p % 16 == 0 and 64 <= p <= 1024) or (-8 <= p <= -1), (s, h, ctx, p)
