@@ -81,9 +81,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     int32_t rope_positions) {
     constexpr int LPR = D / 8, TPL = 64 / LPR;
     const int lane = threadIdx.x & 63;
-    const int kvh = blockIdx.x % num_kv_heads;
-    const int s = (blockIdx.x / num_kv_heads) % num_seqs;
+    int kvh = blockIdx.x % num_kv_heads;
+    int s = (blockIdx.x / num_kv_heads) % num_seqs;
     const int part = (blockIdx.x / (num_kv_heads * num_seqs)) * (blockDim.x >> 6) + wave_id_uniform();
+    if constexpr (FP8)  // within each group of partitions
+        pair_kv_heads(blockIdx.x % (num_kv_heads * num_seqs), num_kv_heads * num_seqs,
+                      num_kv_heads, s, kvh);
     const int row = lane / LPR;
     const int c = lane % LPR;
     const int h0 = kvh * G;
@@ -200,8 +203,11 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
     // [W][G][D] acc, then [W][G] m, then [W][G] l; FP8: [W] rings of
     // Fp8Mma<D>::WAVE_BYTES (the matrix-core path)
     extern __shared__ float smem[];
-    const int kvh = blockIdx.x;
-    const int s = blockIdx.y;
+    int kvh = blockIdx.x;
+    int s = blockIdx.y;
+    if constexpr (FP8)
+        pair_kv_heads(blockIdx.y * num_kv_heads + blockIdx.x, num_kv_heads * (int)gridDim.y,
+                      num_kv_heads, s, kvh);
     const int ctx = clamp_context(context_lens[s], max_context_len, max_blocks_per_seq,
                                   kvh == 0 && threadIdx.x == 0, s);
     const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;

@@ -93,16 +93,32 @@ struct Fp8Mma {
 constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }  // vmcnt <= n < 64
 constexpr int kWaitLgkm0 = 0xC07F;                       // lgkmcnt == 0
 
+template <int AUX = kNontemporal>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char *lds,
                                           uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, kNontemporal);
+        r, (__attribute__((address_space(3))) void *)lds, 16, voff, 0, 0, AUX);
 }
 
 __device__ __forceinline__ uint2 ds_read_tr8(const unsigned char *p) {
     const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
         (__attribute__((address_space(3))) i32x2_t *)(p));
     return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+
+// Two KV heads' scale rows (16 fp32 each) share a 128-byte line.  Units
+// (sequence, KV head) are numbered L = s * H + kvh; this gives the workgroup
+// with linear id L (one of U = S * H in order) the unit that puts heads 2k and
+// 2k + 1 of a sequence on one XCD, back to back: workgroups are dealt to the 8
+// XCDs round-robin by linear id, and ids 16a + 8h + x take pair 8a + x, member
+// h, so the second head reads the line from its XCD's L2 instead of HBM.  Ids
+// past the last whole group of 16, and odd H, keep their unit.
+__device__ __forceinline__ void pair_kv_heads(int L, int U, int H, int &s, int &kvh) {
+    if ((H & 1) == 0 && L < (U & ~15)) {
+        const int pair = 8 * (L >> 4) + (L & 7), h = (L >> 3) & 1;
+        s = pair / (H >> 1);
+        kvh = 2 * (pair % (H >> 1)) + h;
+    }
 }
 
 // The wave's attention over tokens [t_begin, t_end) (t_begin a multiple of 16,
@@ -210,8 +226,9 @@ __device__ __forceinline__ void wave_attend_fp8_mfma(
         const auto ksr = tile_rsrc(k_scale + unit * kBlockTokens, live ? 64u : 0u);
         const auto vsr = tile_rsrc(v_scale + unit * kBlockTokens, live ? 64u : 0u);
         if (lane < 4) {  // 4 lanes x 16 bytes per scale row
-            lds_dma16(ksr, sl + 2 * TILE, lane * 16u);
-            lds_dma16(vsr, sl + 2 * TILE + 64, lane * 16u);
+            // (cached normally: the neighbouring KV head reads the same lines)
+            lds_dma16<0>(ksr, sl + 2 * TILE, lane * 16u);
+            lds_dma16<0>(vsr, sl + 2 * TILE + 64, lane * 16u);
         }
     };
 
