@@ -283,8 +283,8 @@ size_t pkv_mixed_workspace_bytes(int32_t num_seqs, int32_t num_decode_seqs, int3
  * blocks are read once per group instead of once per sequence.  The group's
  * queries attend to the prefix together on the matrix cores (one query tile
  * per group, KV head and key range; P is rounded to bf16 in two parts, as in
- * pkv_prefill_attn), each sequence's remaining tokens run as split-KV
- * partitions, and a second launch merges the partial results exactly.
+ * pkv_prefill_attn), the sequences' remaining tokens are split evenly among
+ * the tail waves, and a second launch merges the partial results exactly.
  *   group_starts     int32 [num_groups + 1], device: group g is sequences
  *                    group_starts[g] .. group_starts[g+1]-1 (nondecreasing,
  *                    within 0 .. num_seqs).  A sequence outside every group
@@ -295,8 +295,11 @@ size_t pkv_mixed_workspace_bytes(int32_t num_seqs, int32_t num_decode_seqs, int3
  *   num_groups       >= 0 (0: every sequence is computed as split-KV decode).
  *   max_group_size   host-side bound of the sizes of groups with a prefix;
  *                    sizes the grid.
- *   partition_tokens length of a tail partition (counted from the prefix
- *                    end): a positive multiple of 16, or 0 for automatic.
+ *   partition_tokens the shortest run of tail tokens one wave takes: a
+ *                    positive multiple of 16, or 0 for automatic.  The tails
+ *                    of all (sequence, KV head) pairs form one list that the
+ *                    tail waves split evenly (runs of at least this length).
+ *   num_seqs         at most 8192 (the tail list is kept in LDS).
  *   workspace        device scratch of at least
  *                    pkv_decode_prefix_workspace_bytes(num_seqs, num_q_heads,
  *                    cache.num_kv_heads, cache.head_dim, max_context_len,

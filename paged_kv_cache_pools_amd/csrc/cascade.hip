@@ -22,19 +22,37 @@
 // prefix_lens[g] tokens (whole blocks); a sequence outside every group, or in
 // a group of prefix 0, is all tail.
 //
-// Workspace row of (sequence s, query head h), slots = max_parts + kMaxSegments:
-// slots 0 .. max_parts - 1 hold the tail partitions (partition_tokens tokens
-// each, counted from the prefix end), slots max_parts .. the prefix segments
-// (the prefix tile splits its keys into up to kMaxSegments ranges of at least
-// 512 keys).  Which slots are written follows from the context length and the
-// group's prefix alone, so the merge recomputes it.
+// Tails, balanced.  The tails of all (sequence, KV head) units, block after
+// block in (sequence, KV head) order, form one list of T blocks, and the NW
+// waves of the tail workgroups each take one contiguous run of it: wave w the
+// blocks [floor(w T / NW), floor((w + 1) T / NW)).  Every wave streams the same
+// number of blocks whatever the lengths of the tails, in long runs (a fixed
+// split into partitions leaves the last round of waves part-filled and makes
+// every short partition pay the start of a stream); where a run crosses from
+// one unit to the next it writes the first unit's partial result and starts
+// afresh.  A run is at least partition_tokens tokens (NW is lowered for short
+// lists), so a unit has at most ceil(tail / partition_tokens) + 1 pieces.
+// Every tail workgroup computes the units' offsets in the list (a scan over
+// the sequences' tail lengths) in LDS; the first also writes them to the
+// workspace for the merge.  The split depends only on the inputs and the
+// grid, so results are reproducible.
 //
-// Dispatch order: all prefix tiles first, then the tail workgroups.  The
-// dispatcher hands an XCD's workgroups to its compute units breadth first, so
-// as long as there are at most 256 tiles no compute unit runs two of them.
-// (Alternating the kinds in short runs instead aliases with the dispatcher's
-// walk over the shader engines and piles the tiles onto half of them --
-// measured.)
+// Workspace row of (sequence s, query head h), slots = max_parts + kMaxSegments:
+// slots 0 .. max_parts - 1 hold the tail pieces of the unit in list order,
+// slots max_parts .. the prefix segments (the prefix tile splits its keys into
+// up to kMaxSegments ranges of at least 512 keys).  After the rows: the list's
+// wave count NW, then the offsets, for the merge.
+//
+// Dispatch order: all prefix tiles first, then the tail workgroups, two per
+// compute unit (as many as can be resident).  The dispatcher hands an XCD's
+// workgroups to its compute units breadth first, so as long as there are at
+// most 256 tiles no compute unit runs two of them, and the tail workgroups
+// that find no slot start as the tiles finish.  (Alternating the kinds in
+// short runs instead aliases with the dispatcher's walk over the shader
+// engines and piles the tiles onto half of them -- measured.  Shorter runs for
+// the workgroups that start late measured slower: 219-250 against 204 us.)
+#include <mutex>
+
 #include "decode_wave.h"
 #include "prefill_tile.h"
 
@@ -78,12 +96,32 @@ __device__ __forceinline__ GroupView group_of(const int32_t *__restrict__ group_
     return v;
 }
 
-// Partitions of a tail of `tail` tokens.
-__device__ __forceinline__ int tail_parts(int tail, int partition_tokens) {
-    return tail > 0 ? (tail + partition_tokens - 1) / partition_tokens : 0;
+// The tail of sequence s: tokens [prefix, ctx) in `blocks` whole or partial
+// blocks (none when the context does not pass the prefix).
+struct TailView {
+    int prefix, ctx, blocks;
+};
+
+__device__ __forceinline__ TailView tail_of(const int32_t *__restrict__ context_lens,
+                                            const int32_t *__restrict__ group_starts,
+                                            const int32_t *__restrict__ prefix_lens,
+                                            int num_groups, int num_seqs, int ctx_cap, int s) {
+    TailView t;
+    t.ctx = min(context_lens[s], ctx_cap);
+    t.prefix = group_of(group_starts, prefix_lens, num_groups, num_seqs, ctx_cap, s).prefix;
+    t.blocks = t.ctx > t.prefix
+                   ? (t.ctx + kBlockTokens - 1) / kBlockTokens - t.prefix / kBlockTokens
+                   : 0;
+    return t;
 }
 
-constexpr int kTailWaves = 4;  // partitions of a tail workgroup (one per wave)
+// The wave of a list of T blocks split among nw waves that holds block x.
+__device__ __forceinline__ int tail_wave_of(int x, int total, int nw) {
+    return (int)(((int64_t)(x + 1) * nw - 1) / total);
+}
+
+constexpr int kTailWaves = 4;  // waves of a tail workgroup
+constexpr int kTailThreads = 64 * kTailWaves;
 
 // Prefix tiles split their keys into segments of at least this many 64-key
 // chunks (512 keys), up to kMaxSegments.
@@ -105,9 +143,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     int32_t num_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     const int32_t *__restrict__ group_starts, const int32_t *__restrict__ prefix_lens,
     int32_t num_groups, int32_t prefix_qblocks, int32_t partition_tokens, int32_t max_parts,
-    float scale_log2, float *__restrict__ ws_out, float *__restrict__ ws_ml) {
+    float scale_log2, float *__restrict__ ws_out, float *__restrict__ ws_ml,
+    int32_t *__restrict__ ws_list) {
     using Geo = PrefillGeom<D, G>;
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Geo::BUF];
+    static_assert(2 * Geo::BUF >= (kMaxPrefixSeqs + 1 + kTailWaves) * (int)sizeof(int32_t),
+                  "a tail workgroup's list fits the tile's LDS");
     const int slots = max_parts + kMaxSegments;
     const int ctx_cap = min(max_context_len, max_blocks_per_seq * kBlockTokens);
     const int pf_units = num_groups * prefix_qblocks * kMaxSegments * num_kv_heads;
@@ -141,45 +182,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         return;
     }
 
-    // a tail workgroup: one wave per partition of partition_tokens tokens of
-    // sequence s's tail, for KV head kvh; the 4 waves take 4 consecutive
-    // partitions.  The KV head is innermost, then the sequence, then the
-    // partition group, so the 8 XCDs (dealt workgroups round-robin) see the
-    // same work, and the late, mostly empty partition groups come last.
-    const int idx = blockIdx.x - pf_units;
-    const int kvh = idx % num_kv_heads;
-    const int s = (idx / num_kv_heads) % num_seqs;
-    const int part = (idx / (num_kv_heads * num_seqs)) * kTailWaves + wave_id_uniform();
-    PKV_DEBUG_CHECK(kvh == 0 && part == 0 && (threadIdx.x & 63) == 0 &&
-                        (context_lens[s] < 0 || context_lens[s] > ctx_cap),
-                    kDbgContext, context_lens[s], s);
-    const int ctx = min(context_lens[s], ctx_cap);
-    if (part * partition_tokens >= ctx) return;  // uniform: empty however long the prefix
-    const GroupView v = group_of(group_starts, prefix_lens, num_groups, num_seqs, ctx_cap, s);
-    const int t_begin = v.prefix + part * partition_tokens;
-    if (t_begin >= ctx) return;
-    const int t_end = min(t_begin + partition_tokens, ctx);
+    // a tail workgroup.  First the list: tail_off[s] = H x the tail blocks of
+    // the sequences before s (each thread counts a run of sequences, then an
+    // exclusive scan of the runs' totals).
+    const int tw = blockIdx.x - pf_units;  // tail workgroup
+    // [num_seqs + 1] list offsets, then the 4 waves' sums (in the tile's LDS)
+    int32_t *tail_off = reinterpret_cast<int32_t *>(lds);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int S = num_seqs, H = num_kv_heads;
+    const int per = (S + kTailThreads - 1) / kTailThreads;
+    const int s_lo = min(S, tid * per), s_hi = min(S, s_lo + per);
+    int run = 0;
+    for (int s = s_lo; s < s_hi; ++s) {
+        PKV_DEBUG_CHECK(tw == 0 && (context_lens[s] < 0 || context_lens[s] > ctx_cap),
+                        kDbgContext, context_lens[s], s);
+        const int b = tail_of(context_lens, group_starts, prefix_lens, num_groups, S, ctx_cap, s)
+                          .blocks;
+        tail_off[s] = b;
+        run += b;
+    }
+    int incl = run;  // inclusive scan within the wave, then across the 4 waves
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    int32_t *wsum = tail_off + S + 1;
+    if (lane == 63) wsum[tid >> 6] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int u = 0; u < (tid >> 6); ++u) before += wsum[u];
+    int at = before + incl - run;
+    for (int s = s_lo; s < s_hi; ++s) {
+        const int b = tail_off[s];
+        tail_off[s] = at * H;
+        at += b;
+    }
+    if (tid == kTailThreads - 1) tail_off[S] = (before + incl) * H;
+    __syncthreads();
+    const int total = tail_off[S];  // T
+    const int nw_all = ((int)gridDim.x - pf_units) * kTailWaves;
+    const int min_run = max(1, partition_tokens / kBlockTokens);
+    const int nw = max(1, min(nw_all, total / min_run));
+    if (tw == 0) {  // the list, for the merge
+        for (int s = tid; s <= S; s += kTailThreads) ws_list[1 + s] = tail_off[s];
+        if (tid == 0) ws_list[0] = nw;
+    }
+
+    const int w = tw * kTailWaves + wave_id_uniform();
+    if (w >= nw || total == 0) return;  // uniform: no run for this wave
+    const int r1 = (int)((int64_t)(w + 1) * total / nw);
+    int x = (int)((int64_t)w * total / nw);
+    // the sequence holding block x: the last s with tail_off[s] <= x
+    int s = 0;
+    for (int lo = 0, hi = S - 1; lo <= hi;) {
+        const int mid = (lo + hi) >> 1;
+        if (tail_off[mid] <= x) {
+            s = mid;
+            lo = mid + 1;
+        } else {
+            hi = mid - 1;
+        }
+    }
     constexpr int LPR = D / 8, TPL = 64 / LPR;
-    const int lane = threadIdx.x & 63;
     const int row = lane / LPR;
     const int c = lane % LPR;
-    float acc[G][8], mg[G], lg[G];
-    wave_attend<D, G, false>(q, k_cache, v_cache, nullptr, nullptr,
-                             block_tables + (size_t)s * max_blocks_per_seq, num_blocks, num_q_heads,
-                             num_kv_heads, scale_log2, s, kvh, t_begin, t_end, NewToken{}, Rope{},
-                             acc, mg, lg);
+    while (x < r1) {
+        while (tail_off[s + 1] <= x) ++s;  // past sequences with no tail
+        const int nb = (tail_off[s + 1] - tail_off[s]) / H;
+        const int rel = x - tail_off[s];
+        const int kvh = rel / nb, j0 = rel - kvh * nb;
+        const int take = min(nb - j0, r1 - x);
+        const TailView tv =
+            tail_of(context_lens, group_starts, prefix_lens, num_groups, S, ctx_cap, s);
+        const int t_begin = tv.prefix + j0 * kBlockTokens;
+        const int t_end = min(tv.prefix + (j0 + take) * kBlockTokens, tv.ctx);
+        float acc[G][8], mg[G], lg[G];
+        wave_attend<D, G, false>(q, k_cache, v_cache, nullptr, nullptr,
+                                 block_tables + (size_t)s * max_blocks_per_seq, num_blocks,
+                                 num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
+                                 NewToken{}, Rope{}, acc, mg, lg);
+        // the unit's piece: waves before this one that hold blocks of it
+        const int ustart = tail_off[s] + kvh * nb;
+        const int piece = w - tail_wave_of(ustart, total, nw);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if (g % TPL == row) {
-            const size_t r = ((size_t)s * num_q_heads + kvh * G + g) * slots + part;
-            float4 *dst = reinterpret_cast<float4 *>(ws_out + r * D + c * 8);
-            dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
-            dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
-            if (c == 0) {
-                ws_ml[r * 2 + 0] = mg[g];
-                ws_ml[r * 2 + 1] = lg[g];
+        for (int g = 0; g < G; ++g) {
+            if (g % TPL == row) {
+                const size_t r = ((size_t)s * num_q_heads + kvh * G + g) * slots + piece;
+                float4 *dst = reinterpret_cast<float4 *>(ws_out + r * D + c * 8);
+                dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+                dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
+                if (c == 0) {
+                    ws_ml[r * 2 + 0] = mg[g];
+                    ws_ml[r * 2 + 1] = lg[g];
+                }
             }
         }
+        x += take;
     }
 }
 
@@ -191,10 +291,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
 template <int D>
 __global__ __launch_bounds__(256) void cascade_reduce_kernel(
     const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
-    int32_t num_seqs, int32_t num_q_heads, const int32_t *__restrict__ group_starts,
-    const int32_t *__restrict__ prefix_lens, int32_t num_groups, int32_t prefix_rows,
-    int32_t partition_tokens, int32_t max_parts, const float *__restrict__ ws_out,
-    const float *__restrict__ ws_ml, uint16_t *__restrict__ out) {
+    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    const int32_t *__restrict__ group_starts, const int32_t *__restrict__ prefix_lens,
+    int32_t num_groups, int32_t prefix_rows, int32_t max_parts, const float *__restrict__ ws_out,
+    const float *__restrict__ ws_ml, const int32_t *__restrict__ ws_list,
+    uint16_t *__restrict__ out) {
     constexpr int E = D / 64;  // elements per lane
     const int lane = threadIdx.x & 63;
     const int row_id = blockIdx.x * (blockDim.x >> 6) + wave_id_uniform();
@@ -216,7 +317,15 @@ __global__ __launch_bounds__(256) void cascade_reduce_kernel(
         for (int e = 0; e < E; ++e) o[e] = 0;
         return;
     }
-    const int nparts = tail_parts(ctx - prefix, partition_tokens);
+    // the unit's tail pieces: the waves of the tail list that hold its blocks
+    const int H = num_kv_heads, kvh = (row_id % num_q_heads) / (num_q_heads / H);
+    const int nw = ws_list[0], total = ws_list[1 + num_seqs];
+    const int off = ws_list[1 + s], nb = (ws_list[2 + s] - off) / H;
+    int nparts = 0;
+    if (nb > 0) {
+        const int ustart = off + kvh * nb;
+        nparts = tail_wave_of(ustart + nb - 1, total, nw) - tail_wave_of(ustart, total, nw) + 1;
+    }
     const int n = nparts + prefix_segments(prefix);
     auto slot_of = [&](int i) { return i < nparts ? i : max_parts + (i - nparts); };
 
@@ -259,13 +368,30 @@ __global__ __launch_bounds__(256) void cascade_reduce_kernel(
     for (int e = 0; e < E; ++e) o[e] = (uint16_t)f32_to_bf16_rne(acc[e] * inv);
 }
 
+int32_t compute_units() {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int32_t cus[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int D, int G>
 static hipError_t launch_cascade_t(const CascadeArgs &a, hipStream_t stream) {
     using Geo = PrefillGeom<D, G>;
     const int prefix_qblocks = cascade_prefix_qblocks(a.max_group_size, G);
+    static_assert(Geo::THREADS == kTailThreads, "tail workgroups are tile-sized");
     const int64_t pf_units = (int64_t)a.num_groups * prefix_qblocks * kMaxSegments * a.num_kv_heads;
-    const int64_t tail_units =
-        (int64_t)(a.max_parts + kTailWaves - 1) / kTailWaves * a.num_seqs * a.num_kv_heads;
+    const int64_t tail_units = a.tail_workgroups;
     const float scale_log2 = a.scale * 1.4426950408889634f;
     hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)(pf_units + tail_units)),
                        dim3(Geo::THREADS), 0, stream, (const uint16_t *)a.q,
@@ -273,15 +399,15 @@ static hipError_t launch_cascade_t(const CascadeArgs &a, hipStream_t stream) {
                        a.context_lens, a.max_blocks_per_seq, a.max_context_len, a.num_blocks,
                        a.num_seqs, a.num_q_heads, a.num_kv_heads, a.group_starts, a.prefix_lens,
                        a.num_groups, prefix_qblocks, a.partition_tokens, a.max_parts, scale_log2,
-                       a.ws_out, a.ws_ml);
+                       a.ws_out, a.ws_ml, a.ws_list);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int rows = a.num_seqs * a.num_q_heads;
     hipLaunchKernelGGL((cascade_reduce_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, stream,
                        a.context_lens, a.max_blocks_per_seq, a.max_context_len, a.num_seqs,
-                       a.num_q_heads, a.group_starts, a.prefix_lens, a.num_groups,
-                       prefix_qblocks * Geo::TWG, a.partition_tokens, a.max_parts, a.ws_out,
-                       a.ws_ml, (uint16_t *)a.out);
+                       a.num_q_heads, a.num_kv_heads, a.group_starts, a.prefix_lens, a.num_groups,
+                       prefix_qblocks * Geo::TWG, a.max_parts, a.ws_out, a.ws_ml, a.ws_list,
+                       (uint16_t *)a.out);
     return hipGetLastError();
 }
 

@@ -661,9 +661,19 @@ int32_t prefix_partition_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max
     return std::min<int32_t>(256, partition_for((int64_t)num_seqs * num_kv_heads, max_context_len));
 }
 
-int32_t prefix_parts(int32_t max_context_len, int32_t p) {
-    return max_context_len > 0 ? ceil_div(max_context_len, p) : 0;
+// Tail slots of a workspace row: a unit's tail of up to max_context_len
+// tokens falls into at most ceil(max_context_len / p) + 1 pieces when every
+// wave's run of the tail list is at least p tokens.
+int32_t prefix_tail_slots(int32_t max_context_len, int32_t p) {
+    return max_context_len > 0 ? ceil_div(max_context_len, p) + 1 : 0;
 }
+
+// The tail list the merge reads: its wave count and num_seqs + 1 offsets,
+// rounded up to 16 bytes.
+size_t prefix_list_bytes(int32_t num_seqs) {
+    return ((size_t)num_seqs + 2) * sizeof(int32_t) + 15 & ~(size_t)15;
+}
+
 
 // Leading block-table entries rows a and b share, among the first `limit`.
 int32_t common_blocks(const int32_t *a, const int32_t *b, int32_t limit) {
@@ -685,9 +695,9 @@ size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
     const int32_t p = partition_tokens
                           ? partition_tokens
                           : prefix_partition_for(num_seqs, num_kv_heads, max_context_len);
-    const int32_t parts = prefix_parts(max_context_len, p);
+    const int32_t parts = prefix_tail_slots(max_context_len, p);
     const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)(parts + pkv::kMaxSegments);
-    return rows * (size_t)(head_dim + 2) * sizeof(float);
+    return rows * (size_t)(head_dim + 2) * sizeof(float) + prefix_list_bytes(num_seqs);
 }
 
 int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_tables,
@@ -715,6 +725,9 @@ int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_
     if (max_group_size > num_seqs)
         return fail(PKV_ERR_SHAPE, "max_group_size %d exceeds num_seqs %d", max_group_size,
                     num_seqs);
+    if (num_seqs > pkv::kMaxPrefixSeqs)
+        return fail(PKV_ERR_SHAPE, "%d sequences exceed the %d of one shared-prefix call",
+                    num_seqs, pkv::kMaxPrefixSeqs);
     if (!q || !out || !context_lens || (max_blocks_per_seq > 0 && !block_tables))
         return fail(PKV_ERR_NULL, "q, out, context_lens or block_tables is null");
     if (num_groups > 0 && (!group_starts || !prefix_lens))
@@ -727,16 +740,19 @@ int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_
     const int32_t p = partition_tokens
                           ? partition_tokens
                           : prefix_partition_for(num_seqs, cache.num_kv_heads, max_context_len);
-    const int32_t parts = prefix_parts(max_context_len, p);
+    const int32_t parts = prefix_tail_slots(max_context_len, p);
     const size_t need = pkv_decode_prefix_workspace_bytes(
         num_seqs, num_q_heads, cache.num_kv_heads, cache.head_dim, max_context_len, p);
     if (!workspace || workspace_bytes < need)
         return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
-    // the grid: tail workgroups (4 partitions each) plus prefix tiles (a tile
-    // holds at least 16 sequences, group size 8); 256 threads per workgroup
+    // the grid: tail workgroups (two per compute unit, as many as can be
+    // resident: 4 tail waves per compute unit stream the list 13% slower on
+    // 256 sequences in 8 shared-prefix groups) plus prefix tiles (a tile holds
+    // at least 16 sequences, group size 8); 256 threads per workgroup
     const int64_t qblocks = ((int64_t)max_group_size + 15) / 16;
-    const int64_t wgs = ((int64_t)parts + 3) / 4 * num_seqs * cache.num_kv_heads +
+    const int32_t tail_wgs = 2 * pkv::compute_units();
+    const int64_t wgs = tail_wgs +
                         (int64_t)num_groups * qblocks * pkv::kMaxSegments * cache.num_kv_heads;
     if (wgs >= (int64_t)1 << 24 || (int64_t)num_seqs * num_q_heads >= (int64_t)1 << 26)
         return fail(PKV_ERR_SHAPE, "%d sequences of up to %d tokens in %d groups exceed one launch's grid",
@@ -760,12 +776,14 @@ int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_
     a.max_group_size = max_group_size;
     a.partition_tokens = p;
     a.max_parts = parts;
+    a.tail_workgroups = tail_wgs;
     a.scale = scale;
     a.out = out;
     float *ws = static_cast<float *>(workspace);
     const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)(parts + pkv::kMaxSegments);
     a.ws_out = ws;
     a.ws_ml = ws + rows * cache.head_dim;
+    a.ws_list = reinterpret_cast<int32_t *>(a.ws_ml + rows * 2);
     return hip_status(pkv::launch_cascade(a, stream), "pkv_decode_attn_prefix launch");
 }
 

@@ -127,12 +127,21 @@ struct CascadeArgs {
     const int32_t *group_starts;  // device [num_groups + 1]
     const int32_t *prefix_lens;   // device [num_groups]
     int32_t num_groups, max_group_size;
-    int32_t partition_tokens, max_parts;
+    int32_t partition_tokens, max_parts;  // max_parts: tail slots per row
+    int32_t tail_workgroups;              // one per compute unit
     float scale;
     void *out;
-    float *ws_out;  // [num_seqs][num_q_heads][max_parts + kMaxSegments][head_dim]
-    float *ws_ml;   // [num_seqs][num_q_heads][max_parts + kMaxSegments][2]
+    float *ws_out;     // [num_seqs][num_q_heads][max_parts + kMaxSegments][head_dim]
+    float *ws_ml;      // [num_seqs][num_q_heads][max_parts + kMaxSegments][2]
+    int32_t *ws_list;  // [1 + num_seqs + 1]: the tail list's wave count and offsets
 };
+// Sequences of one shared-prefix decode call (the tail list's offsets live in
+// the LDS of a tail workgroup).
+constexpr int32_t kMaxPrefixSeqs = 8192;
+// Compute units of the current device (cascade.hip; they size the tail
+// workgroups of a shared-prefix decode), asked once per device; 256 when the
+// runtime cannot tell.
+int32_t compute_units();
 hipError_t launch_cascade(const CascadeArgs &a, hipStream_t stream);
 inline int cascade_prefix_qblocks(int32_t max_group_size, int32_t group) {
     const int twg = kTileWaves * (kTileCols / group);

@@ -18,6 +18,7 @@ hipError_t launch_decode(const DecodeArgs &, hipStream_t) { ++g_launches; return
 hipError_t launch_prefill(const PrefillArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_mixed(const MixedArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_cascade(const CascadeArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
+int32_t compute_units() { return 256; }
 hipError_t launch_copy_blocks(const CopyArgs &) { ++g_launches; return hipSuccess; }
 hipError_t launch_read_probe(const void *, size_t, uint32_t *, hipStream_t) {
     ++g_launches;

@@ -262,6 +262,7 @@ def test_prefix_decode_validation(lib):
     assert pd(s=-1) == 2 and pd(ng=-1) == 2 and pd(mg=-1) == 2
     assert pd(mg=41) == 2                   # a group larger than the batch
     assert pd(mc=80) == 2                   # beyond max_blocks * 16
+    assert pd(s=8193) == 2                  # more sequences than one call's tail list holds
     assert pd(q=0) == 1 and pd(gs=0) == 1 and pd(pl=0) == 1
     assert pd(q=FAKE + 8) == 4
     assert pd(hq=6) == 3 and pd(c=cache(d=96)) == 3 and pd(c=cache(bs=32)) == 3
@@ -272,16 +273,21 @@ def test_prefix_decode_validation(lib):
 
 
 def test_prefix_decode_workspace_sizing(lib):
-    # rows x (tail partitions + 8 prefix segments) x (d + 2) floats
+    # rows x (tail pieces + 8 prefix segments) x (d + 2) floats, then the tail
+    # list (wave count + num_seqs + 1 offsets) rounded up to 16 bytes; a tail
+    # of up to max_context_len tokens falls into ceil(max_context_len / P) + 1
+    # pieces
+    lst = lambda s: ((s + 2) * 4 + 15) // 16 * 16
     assert B.pkv_decode_prefix_workspace_bytes(256, 32, 8, 128, 32768, 512) == \
-        256 * 32 * (64 + 8) * 130 * 4
-    assert B.pkv_decode_prefix_workspace_bytes(3, 4, 2, 64, 0, 16) == 3 * 4 * 8 * 66 * 4
-    assert B.pkv_decode_prefix_workspace_bytes(3, 1, 2, 64, 33, 16) == 3 * 1 * (3 + 8) * 66 * 4
+        256 * 32 * (65 + 8) * 130 * 4 + lst(256)
+    assert B.pkv_decode_prefix_workspace_bytes(3, 4, 2, 64, 0, 16) == 3 * 4 * 8 * 66 * 4 + lst(3)
+    assert B.pkv_decode_prefix_workspace_bytes(3, 1, 2, 64, 33, 16) == \
+        3 * 1 * (4 + 8) * 66 * 4 + lst(3)
     # automatic partitions: the split-KV choice, at most 256 tokens
     assert B.pkv_decode_prefix_workspace_bytes(256, 32, 8, 128, 32768, 0) == \
-        256 * 32 * (128 + 8) * 130 * 4
+        256 * 32 * (129 + 8) * 130 * 4 + lst(256)
     assert B.pkv_decode_prefix_workspace_bytes(1, 32, 8, 128, 32768, 0) == \
-        32 * (32768 // B.pkv_decode_partition_tokens(1, 8, 32768) + 8) * 130 * 4
+        32 * (32768 // B.pkv_decode_partition_tokens(1, 8, 32768) + 1 + 8) * 130 * 4 + lst(1)
     assert B.pkv_decode_prefix_workspace_bytes(0, 32, 8, 128, 100, 0) == 0
     assert B.pkv_decode_prefix_workspace_bytes(4, 32, 8, 128, 100, 24) == 0
 
