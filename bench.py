@@ -797,8 +797,10 @@ def bench_mixed(torch, B, W, dev, name="mixed_step", iters=20):
     tokens), or "mixed_tail", one 64-token chunk after 4032 cached ones.
     Timed against the same work as two launches (pkv_decode_attn on the
     decode sequences, then pkv_prefill_attn on the chunks), and without the
-    key-range split of prefill units.  Two layer pools alternate.  The bound
-    for one launch that overlaps both kinds of work perfectly is
+    key-range split of prefill units.  Two layer pools alternate.  Each form
+    is timed over a region of back-to-back calls, as the decode step is (an
+    event pair around every call is reported beside it).  The bound for one
+    launch that overlaps both kinds of work perfectly is
     max(decode bytes / HBM peak, prefill flops / bf16 MFMA peak)."""
     wl = W.CONFIGS[name]()
     nd = 32
@@ -839,9 +841,20 @@ def bench_mixed(torch, B, W, dev, name="mixed_step", iters=20):
                            wl.scale, out_pf, max_new_len=mnl, max_context_len=mcl)
 
     def timed(fn):
+        """(ms per call over one region of back-to-back calls, the stats of a
+        second pass with an event pair around every call): the region is the
+        figure, as for the decode step; the bracketed pass adds idle GPU time
+        per call and is reported beside it."""
         for l in (0, 1, 0, 1):
             fn(l)
         torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(iters):
+            fn(i & 1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        region_ms = a.elapsed_time(b) / iters
         evs = []
         for i in range(iters):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -850,7 +863,10 @@ def bench_mixed(torch, B, W, dev, name="mixed_step", iters=20):
             b.record(stream)
             evs.append((a, b))
         torch.cuda.synchronize()
-        return launch_stats([a.elapsed_time(b) for a, b in evs])
+        _, stats = launch_stats([a.elapsed_time(b) for a, b in evs])
+        return region_ms, {"source": "timed region / calls",
+                           "timed_region_us_per_call": round(region_ms * 1e3, 2),
+                           "event_bracketed": stats}
 
     for fn in (mixed, mixed_whole, separate):  # every variant warm before any is timed
         timed(fn)

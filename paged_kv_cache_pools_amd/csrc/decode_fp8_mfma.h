@@ -248,9 +248,15 @@ __device__ __forceinline__ void wave_attend_fp8_mfma(
         }
     };
 
-    // scores and weights of block b (slot at sl): returns this lane's 4
-    // weights (tokens 4grp .. 4grp + 3, head col) as bf16 pairs
-    auto scores = [&](int b, const unsigned char *sl) {
+    // scores and weights of block b (slot at sl): this lane's 4 weights
+    // (tokens 4grp .. 4grp + 3, head col) in fp32, times their V scales, and
+    // the reciprocal V scales.  They stay fp32 until the pair's P V: a raised
+    // maximum rescales the accumulators and the weight sum, and `pending`
+    // (the pair's first block's weights, when this is its second) with them.
+    struct Weights {
+        float w[4], rv[4];
+    };
+    auto scores = [&](int b, const unsigned char *sl, Weights *pending) {
         uint4 kf[KS];
 #pragma unroll
         for (int i = 0; i < KS / 2; ++i) {
@@ -283,24 +289,34 @@ __device__ __forceinline__ void wave_attend_fp8_mfma(
             l_run *= alpha;
 #pragma unroll
             for (int m = 0; m < MT; ++m) o[m] *= alpha;
-        }
-        const float mu = (m_run == kNegInf) ? 0.f : m_run;
-        float w[4], rv[4];
+            if (pending != nullptr) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            w[r] = fast_exp2(sc[r] - mu) * vsa[r];
-            rv[r] = __builtin_amdgcn_rcpf(vsa[r]);
-            if (partial) {  // tokens past the end: NaN scales stay out
-                const bool live = t0 + r < t_end;
-                w[r] = live ? w[r] : 0.f;
-                rv[r] = live ? rv[r] : 0.f;
+                for (int r = 0; r < 4; ++r) pending->w[r] *= alpha;
             }
         }
-        const uint2 wb = make_uint2(cvt_pk_bf16_rne(w[0], w[1]), cvt_pk_bf16_rne(w[2], w[3]));
-        l_run = fmaf(bf16_lo(wb.x), rv[0], l_run);
-        l_run = fmaf(bf16_hi(wb.x), rv[1], l_run);
-        l_run = fmaf(bf16_lo(wb.y), rv[2], l_run);
-        l_run = fmaf(bf16_hi(wb.y), rv[3], l_run);
+        const float mu = (m_run == kNegInf) ? 0.f : m_run;
+        Weights out;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            out.w[r] = fast_exp2(sc[r] - mu) * vsa[r];
+            out.rv[r] = __builtin_amdgcn_rcpf(vsa[r]);
+            if (partial) {  // tokens past the end: NaN scales stay out
+                const bool live = t0 + r < t_end;
+                out.w[r] = live ? out.w[r] : 0.f;
+                out.rv[r] = live ? out.rv[r] : 0.f;
+            }
+        }
+        return out;
+    };
+    // a block's weights rounded to bf16 as P V uses them, their sum (the
+    // rounded weights over the V scales) added to the head's
+    auto round_weights = [&](const Weights &x) {
+        const uint2 wb = make_uint2(cvt_pk_bf16_rne(x.w[0], x.w[1]),
+                                    cvt_pk_bf16_rne(x.w[2], x.w[3]));
+        l_run = fmaf(bf16_lo(wb.x), x.rv[0], l_run);
+        l_run = fmaf(bf16_hi(wb.x), x.rv[1], l_run);
+        l_run = fmaf(bf16_lo(wb.y), x.rv[2], l_run);
+        l_run = fmaf(bf16_hi(wb.y), x.rv[3], l_run);
         return wb;
     };
 
@@ -343,14 +359,16 @@ __device__ __forceinline__ void wave_attend_fp8_mfma(
         unsigned char *sx = ring + S0 * SLOT;
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(AHEAD));  // block bx has landed
         patch(bx, sx);
-        const uint2 wx = scores(bx, sx);
+        Weights px = scores(bx, sx, nullptr);
         issue(bx + RING - 1, (S0 + RING - 1) % RING);  // the previous pair's second slot
         uint2 wy = make_uint2(0u, 0u);
         if (has_y) {
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(AHEAD));  // block bx + 1 has landed
             patch(bx + 1, sx + SLOT);
-            wy = scores(bx + 1, sx + SLOT);
+            const Weights py = scores(bx + 1, sx + SLOT, &px);
+            wy = round_weights(py);
         }
+        const uint2 wx = round_weights(px);
         pv(sx, bx, has_y, wx, wy);
         if (has_y) {
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this pair's reads are done

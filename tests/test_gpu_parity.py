@@ -763,6 +763,35 @@ def test_fp8_quantized_normal_data(d, g, part):
     compare(out, ref, f"fp8 quantized d{d} g{g} P{part}")
 
 
+@pytest.mark.parametrize("d,g", [(128, 4), (64, 8)])
+@pytest.mark.parametrize("part", [0, 1024, 2048, -4])
+def test_fp8_quantized_long_contexts(d, g, part):
+    """Contexts past the single-pass range (up to 20,000 tokens) over store-
+    quantized N(0,1) data: the matrix-core path's LDS ring over hundreds of
+    blocks per wave and its lazy maximum over long spans, in the split-KV
+    kernel (automatic, 1024 and 2048 tokens per partition) and in the
+    single-pass kernel forced to 4 waves; plain bound."""
+    lens = [20000, 129, 8200, 4097, 17, 12345]
+    wl = W.make_decode(f"fp8q_long_d{d}_g{g}", lens, 2 * g, 2, d, 820 + d + g, spare_blocks=1)
+    say(f"[gpu] fp8 long contexts d={d} G={g} P={part or 'auto'}")
+    out, ref = fp8_quantized_step(wl, part)
+    compare(out, ref, f"fp8 long contexts d{d} g{g} P{part}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 2.5])
+def test_fp8_quantized_scale_edges(scale):
+    """Zero, negative and sharpened scales on the matrix-core path (contexts
+    above 128 keys): a sharpened softmax raises the reference maximum many
+    times mid-stream.  A near-one-hot row returns one cached V row whose bf16
+    rounding alone can exceed 1e-2, so the per-element allowance of the
+    bf16 scale-edge tests applies."""
+    wl = W.make_decode("fp8q_scale", [4000, 300, 129, 1000, 1], 8, 2, 128, 830, scale=scale,
+                       spare_blocks=1)
+    say(f"[gpu] fp8 quantized data, scale {scale}")
+    out, ref = fp8_quantized_step(wl)
+    compare(out, ref, f"fp8 quantized scale {scale}", plus_floor=True)
+
+
 def test_fp8_quantized_separate_launches():
     """The same over two launches (pkv_store_fp8, then pkv_decode_attn_fp8)."""
     wl = W.make_decode("fp8q_sep", [1, 5, 37, 200, 64, 2048], 8, 2, 128, 811, spare_blocks=1)
