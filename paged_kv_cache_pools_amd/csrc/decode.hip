@@ -276,31 +276,14 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     for (int e = 0; e < E; ++e) o[e] = (uint16_t)f32_to_bf16_rne(a[e] * inv);
 }
 
-// Dynamic LDS of the FP8 kernels: a ring of Fp8Mma<D>::WAVE_BYTES per wave,
-// more than the default 64 KiB a launch may ask for at 8 waves; the kernels
-// are allowed the most they can use once per process.
-template <int D, int G>
-static void allow_fp8_lds() {
-    static const bool done = [] {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_fused_kernel<D, G, true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kMaxDecodeWaves * Fp8Mma<D>::WAVE_BYTES);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_split_kernel<D, G, true>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  4 * Fp8Mma<D>::WAVE_BYTES);
-        (void)hipGetLastError();  // an attribute this runtime ignores is not a launch error
-        return true;
-    }();
-    (void)done;
-}
-
 template <int D, int G, bool FP8>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    if constexpr (FP8) allow_fp8_lds<D, G>();
     if (a.fused_waves > 0) {
         const int W = a.fused_waves;
         size_t lds = (size_t)W * G * (D + 2) * sizeof(float);
+        // (HIP on this GPU launches up to the 160 KiB of LDS a compute unit
+        // has without a per-kernel attribute: 8 FP8 rings take 132 KiB)
         if constexpr (FP8) lds = std::max(lds, (size_t)W * Fp8Mma<D>::WAVE_BYTES);
         hipLaunchKernelGGL((decode_fused_kernel<D, G, FP8>), dim3(a.num_kv_heads, a.num_seqs),
                            dim3(64 * W), lds, stream, (const uint16_t *)a.q, a.k_cache, a.v_cache,

@@ -1,7 +1,7 @@
-"""The decode step, the mixed step and the shared-prefix decode captured in a
-HIP graph (torch.cuda.graph) and replayed: none of their launches records a
-memset, so every replay must reproduce the eager result bit for bit, with
-eager work and synchronisations between the replays."""
+"""The decode step (bf16 and FP8 caches), the mixed step and the shared-prefix
+decode captured in a HIP graph (torch.cuda.graph) and replayed: none of their
+launches records a memset, so every replay must reproduce the eager result bit
+for bit, with eager work and synchronisations between the replays."""
 import numpy as np
 import pytest
 import torch
@@ -65,6 +65,29 @@ def test_graph_decode_layers():
                                     max_context_len=wl.max_context_len, workspace=ws,
                                     partition_tokens=p)
     replay_and_check(step, outs, "decode layers")
+
+
+@pytest.mark.parametrize("part", [0, 256])
+def test_graph_fp8_decode(part):
+    """The FP8 fused store + decode (the matrix-core path above 128 keys, the
+    fp32 path below) over 2 layer pools, single pass and split-KV, as one
+    graph."""
+    wl = W.make_decode("graph_fp8", [100, 2048, 777, 4096, 1, 3000, 129], 32, 8, 128, 312)
+    t = W.make_tensors(wl, device="cuda", nan_fill=True)
+    pools = [W.make_fp8_pools(wl, device="cuda", seed=312 + l) for l in range(2)]
+    outs = [torch.empty_like(t["q"]) for _ in range(2)]
+    p = part or B.pkv_decode_partition_tokens_fp8(wl.num_seqs, wl.num_kv_heads, wl.max_context_len)
+    ws = torch.empty(max(16, B.pkv_decode_workspace_bytes(wl.num_seqs, 32, 128, wl.max_context_len, p)),
+                     dtype=torch.uint8, device="cuda")
+    say(f"[gpu] graph: FP8 store + decode of 2 layers, work split {p}")
+
+    def step():
+        for l in range(2):
+            B.pkv_store_decode_attn_fp8(t["k_new"], t["v_new"], t["slot_mapping"], t["q"],
+                                        *pools[l], t["block_tables"], t["context_lens"], wl.scale,
+                                        outs[l], max_context_len=wl.max_context_len, workspace=ws,
+                                        partition_tokens=p)
+    replay_and_check(step, outs, f"fp8 decode P{p}")
 
 
 def test_graph_split_decode():
