@@ -68,6 +68,9 @@ def _bind(lib):
     lib.pko_fp8_encode.argtypes = [ctypes.c_float]
     lib.pko_store_fp8.restype = ctypes.c_int
     lib.pko_store_fp8.argtypes = [_P, _P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32]
+    lib.pko_prefill_fp8.restype = ctypes.c_int
+    lib.pko_prefill_fp8.argtypes = [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                    _I32, _I32, ctypes.c_float, _P, ctypes.c_int]
     lib.pko_decode_fp8.restype = ctypes.c_int
     lib.pko_decode_fp8.argtypes = [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32,
                                    _I32, ctypes.c_float, _P]
@@ -208,6 +211,35 @@ class Oracle:
                                      hkv, d, bs, float(np.float32(scale)), _ptr(out))
         if rc != OK:
             raise OracleError(rc, "decode_fp8")
+        return out
+
+    def prefill_fp8(self, q, k_codes, v_codes, k_scales, v_scales, block_tables, cu_new_lens,
+                    context_lens, scale, nthreads=0):
+        """q [total_new][Hq][d] uint16 -> out [total_new][Hq][d] float64 over the
+        dequantized FP8 cache (codes uint8 [NB][Hkv][16][d], scales float32
+        [NB][Hkv][16])."""
+        q = _u16(q)
+        k_codes = np.ascontiguousarray(k_codes, np.uint8)
+        v_codes = np.ascontiguousarray(v_codes, np.uint8)
+        k_scales = np.ascontiguousarray(k_scales, np.float32)
+        v_scales = np.ascontiguousarray(v_scales, np.float32)
+        bt = _i32(block_tables)
+        cu = _i32(cu_new_lens)
+        ctx = _i32(context_lens)
+        nb, hkv, bs, d = k_codes.shape
+        total, hq, dq = q.shape
+        s = ctx.shape[0]
+        assert dq == d and v_codes.shape == k_codes.shape
+        assert k_scales.shape == (nb, hkv, bs) and v_scales.shape == (nb, hkv, bs)
+        assert bt.ndim == 2 and bt.shape[0] == s and cu.shape == (s + 1,)
+        assert int(cu[-1]) == total
+        out = np.zeros((total, hq, d), dtype=np.float64)
+        rc = self.lib.pko_prefill_fp8(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales),
+                                      _ptr(v_scales), nb, _ptr(bt), bt.shape[1], _ptr(cu),
+                                      _ptr(ctx), s, hq, hkv, d, bs, float(np.float32(scale)),
+                                      _ptr(out), int(nthreads))
+        if rc != OK:
+            raise OracleError(rc, "prefill_fp8")
         return out
 
     # -- prefill ----------------------------------------------------------------

@@ -183,11 +183,58 @@ static void attend_one(const uint16_t *q_row, const uint16_t *k_cache,
         out_row[x] /= z;
 }
 
+/*
+ * attend_one on a cache whose values are already fp64 (a dequantized FP8
+ * cache, see pko_prefill_fp8): the same definition, the key and value rows
+ * read from kd / vd, which hold [num_blocks][num_kv_heads][block_size]
+ * [head_dim] doubles.
+ */
+static void attend_one_f64(const uint16_t *q_row, const double *kd, const double *vd,
+                           const int32_t *block_table, int32_t n, int32_t kv_head,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           double scale, double *scores, double *out_row)
+{
+    for (int32_t x = 0; x < head_dim; ++x)
+        out_row[x] = 0.0;
+    if (n <= 0)
+        return;
+
+    for (int32_t t = 0; t < n; ++t) {
+        int64_t row = ((int64_t)block_table[t / block_size] * num_kv_heads + kv_head) *
+                          block_size + t % block_size;
+        double dot = 0.0;
+        for (int32_t x = 0; x < head_dim; ++x)
+            dot += bf16_bits_to_double(q_row[x]) * kd[row * head_dim + x];
+        scores[t] = scale * dot;
+    }
+
+    double m = scores[0];
+    for (int32_t t = 1; t < n; ++t)
+        if (scores[t] > m)
+            m = scores[t];
+
+    double z = 0.0;
+    for (int32_t t = 0; t < n; ++t) {
+        scores[t] = exp(scores[t] - m);
+        z += scores[t];
+    }
+
+    for (int32_t t = 0; t < n; ++t) {
+        int64_t row = ((int64_t)block_table[t / block_size] * num_kv_heads + kv_head) *
+                          block_size + t % block_size;
+        for (int32_t x = 0; x < head_dim; ++x)
+            out_row[x] += scores[t] * vd[row * head_dim + x];
+    }
+    for (int32_t x = 0; x < head_dim; ++x)
+        out_row[x] /= z;
+}
+
 /* ---- a minimal static thread split over independent (sequence, kv head) units ---- */
 
 typedef struct {
-    int mode; /* 0 = decode, 1 = prefill */
+    int mode; /* 0 = decode, 1 = prefill, 2 = prefill over fp64 kd / vd */
     const uint16_t *q, *k_cache, *v_cache;
+    const double *kd, *vd;
     const int32_t *block_tables, *context_lens, *cu_new_lens;
     int32_t max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
     double scale;
@@ -223,8 +270,12 @@ static void run_unit(work_t *w, int32_t s, int32_t kvh, double *scores)
                 const uint16_t *q_row =
                     w->q + ((int64_t)(row0 + i) * w->num_q_heads + h) * w->head_dim;
                 double *o = w->out + ((int64_t)(row0 + i) * w->num_q_heads + h) * w->head_dim;
-                attend_one(q_row, w->k_cache, w->v_cache, bt, c + i + 1, kvh,
-                           w->num_kv_heads, w->head_dim, w->block_size, w->scale, scores, o);
+                if (w->mode != 2)
+                    attend_one(q_row, w->k_cache, w->v_cache, bt, c + i + 1, kvh,
+                               w->num_kv_heads, w->head_dim, w->block_size, w->scale, scores, o);
+                else
+                    attend_one_f64(q_row, w->kd, w->vd, bt, c + i + 1, kvh, w->num_kv_heads,
+                                   w->head_dim, w->block_size, w->scale, scores, o);
             }
         }
     }
@@ -624,6 +675,71 @@ int pko_decode_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_c
     return PKO_OK;
 }
 
+
+/*
+ * Chunked causal prefill over an FP8 cache: pko_prefill's definition (new
+ * token i of prompt s at position c + i sees keys 0 .. c + i, [NVE] §3.2,
+ * [LLM4] §22) on the cached values decode(code) * scale of [LLM4] §17.6's
+ * FP8 cache (the reading above pko_fp8_decode), in fp64.  The cache is
+ * dequantized up front into fp64 arrays; the prompts' (sequence, KV head)
+ * units then run on nthreads threads (0 = one per online CPU) as in
+ * pko_prefill.  Arguments as pko_prefill, with pko_decode_fp8's cache.
+ */
+int pko_prefill_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_codes,
+                    const float *k_scales, const float *v_scales, int32_t num_blocks,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *cu_new_lens, const int32_t *context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, float scale, double *out, int nthreads)
+{
+    int32_t max_ctx = 0;
+    if (num_seqs > 0 && (!q || !k_codes || !v_codes || !k_scales || !v_scales ||
+                         !block_tables || !context_lens || !cu_new_lens || !out))
+        return PKO_ERR_ARG;
+    int rc = check_common(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, block_tables, context_lens, num_blocks, &max_ctx);
+    if (rc != PKO_OK || num_seqs == 0)
+        return rc;
+    if (cu_new_lens[0] != 0)
+        return PKO_ERR_ARG;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        int32_t n = cu_new_lens[s + 1] - cu_new_lens[s];
+        if (n < 0 || n > context_lens[s])
+            return PKO_ERR_ARG;
+    }
+    int64_t rows = (int64_t)num_blocks * num_kv_heads * block_size;
+    double *kd = malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * head_dim);
+    double *vd = malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * head_dim);
+    if (!kd || !vd) {
+        free(kd);
+        free(vd);
+        return PKO_ERR_ALLOC;
+    }
+    dequantize(k_codes, k_scales, rows, head_dim, kd);
+    dequantize(v_codes, v_scales, rows, head_dim, vd);
+    work_t w;
+    memset(&w, 0, sizeof w);
+    w.mode = 2;
+    w.q = q;
+    w.kd = kd;
+    w.vd = vd;
+    w.block_tables = block_tables;
+    w.context_lens = context_lens;
+    w.cu_new_lens = cu_new_lens;
+    w.max_blocks_per_seq = max_blocks_per_seq;
+    w.num_seqs = num_seqs;
+    w.num_q_heads = num_q_heads;
+    w.num_kv_heads = num_kv_heads;
+    w.head_dim = head_dim;
+    w.block_size = block_size;
+    w.scale = (double)scale;
+    w.out = out;
+    w.max_context_len = max_ctx;
+    rc = run_threads(&w, nthreads);
+    free(kd);
+    free(vd);
+    return rc;
+}
 
 /* ------------------------------------------------------------------------ */
 /* Rotary position embedding                                                */

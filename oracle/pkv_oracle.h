@@ -67,6 +67,12 @@ int pko_decode_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_c
                    const int32_t *context_lens, int32_t num_seqs, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
                    double *out);
+int pko_prefill_fp8(const uint16_t *q, const uint8_t *k_codes, const uint8_t *v_codes,
+                    const float *k_scales, const float *v_scales, int32_t num_blocks,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *cu_new_lens, const int32_t *context_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, float scale, double *out, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -512,6 +512,78 @@ def pin_decode_fp8_unit_scales_equal_bf16(orc):
     assert np.array_equal(out, ref)
 
 
+def _fp8_prefill_case(cached, new, hq, hkv, dim, seed, spare=2):
+    """A prefill workload whose FP8 pools already hold every context token
+    (the new ones included, as after their store); every other slot holds the
+    NaN code and a NaN scale."""
+    wl = W.make_prefill("pin_fp8_prefill", cached, new, hq, hkv, dim, seed, spare_blocks=spare)
+    t = W.make_tensors(wl, device="cpu", nan_fill=True, layers=1)
+    kc, vc, ks, vs = (x.numpy().copy() for x in W.make_fp8_pools(wl, nan_fill=False))
+    dead = ~W.live_slot_mask(wl, pre_store=False)
+    kc.transpose(0, 2, 1, 3)[dead] = 0x7F
+    vc.transpose(0, 2, 1, 3)[dead] = 0x7F
+    ks.transpose(0, 2, 1)[dead] = np.nan
+    vs.transpose(0, 2, 1)[dead] = np.nan
+    return wl, _bits(t["q"]), kc, vc, ks, vs
+
+
+def pin_prefill_fp8_matches_sdpa(orc):
+    """Chunked causal prefill over an FP8 cache == torch fp64 SDPA on the
+    dequantized values (torch's float8_e4m3fn decode times the scale) with the
+    mask 'key t visible to new query i iff t <= cached + i'; GQA, ragged
+    prompts, NaN codes and scales in dead slots never reach the output."""
+    for cached, new, hq, hkv, dim, seed in (([0, 20, 47], [33, 17, 1], 8, 2, 64, 45),
+                                            ([5, 0], [12, 40], 4, 4, 128, 46)):
+        wl, q, kc, vc, ks, vs = _fp8_prefill_case(cached, new, hq, hkv, dim, seed)
+        out = orc.prefill_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.cu_new_lens,
+                              wl.context_lens, wl.scale)
+        assert np.all(np.isfinite(out))
+        kd = _torch_fp8_decode(kc) * ks[..., None].astype(np.float64)
+        vd = _torch_fp8_decode(vc) * vs[..., None].astype(np.float64)
+        q64 = _f64(q)
+        g = hq // hkv
+        cu = wl.cu_new_lens
+        for p in range(wl.num_seqs):
+            n, ctx = int(wl.new_lens[p]), int(wl.context_lens[p])
+            c = ctx - n
+            k = np.repeat(_gather(kd, wl.block_tables[p], ctx), g, axis=0)
+            v = np.repeat(_gather(vd, wl.block_tables[p], ctx), g, axis=0)
+            qp = q64[cu[p]:cu[p + 1]].transpose(1, 0, 2)  # [Hq][n][d]
+            mask = np.arange(ctx)[None, :] <= (c + np.arange(n))[:, None]
+            ref = _sdpa(qp, k, v, wl.scale, mask=mask)
+            err = np.abs(out[cu[p]:cu[p + 1]] - ref.transpose(1, 0, 2)).max()
+            assert err <= 1e-12, (p, err)
+
+
+def pin_prefill_fp8_one_new_token_is_decode_fp8(orc):
+    """FP8 prefill with one new token per prompt equals FP8 decode over the
+    same cache, bit for bit."""
+    wl, q, kc, vc, ks, vs = _fp8_prefill_case([36, 0, 15], [1, 1, 1], 4, 2, 64, 47)
+    pre = orc.prefill_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.cu_new_lens, wl.context_lens,
+                          wl.scale)
+    dec = orc.decode_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.context_lens, wl.scale)
+    assert np.array_equal(pre, dec)
+
+
+def pin_prefill_fp8_unit_scales_equal_bf16(orc):
+    """With every scale 1 the FP8 cache holds bf16-representable values, so
+    FP8 prefill equals the bf16 prefill over those values, bit for bit."""
+    wl, q, kc, vc, ks, vs = _fp8_prefill_case([9, 30], [23, 3], 4, 2, 64, 48, spare=0)
+    ks[:] = 1.0
+    vs[:] = 1.0
+    out = orc.prefill_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.cu_new_lens, wl.context_lens,
+                          wl.scale)
+    to_bits = lambda c: torch.from_numpy(_torch_fp8_decode(c)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+    kb = np.ascontiguousarray(to_bits(kc))
+    vb = np.ascontiguousarray(to_bits(vc))
+    live = W.live_slot_mask(wl, pre_store=False)
+    kb.transpose(0, 2, 1, 3)[~live] = 0  # dead slots (NaN codes): never read
+    vb.transpose(0, 2, 1, 3)[~live] = 0
+    ref = orc.prefill(q, kb, vb, wl.block_tables, wl.cu_new_lens, wl.context_lens, wl.scale)
+    assert np.array_equal(out, ref)
+
+
 # ---------------------------------------------------------------------------
 # rotary position embedding
 # ---------------------------------------------------------------------------

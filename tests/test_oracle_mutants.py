@@ -50,6 +50,16 @@ MUTANTS = [
     ("fp8_v_stored_from_k", "quantize_row(v + src, head_dim, v_codes", "quantize_row(k + src, head_dim, v_codes"),
     ("fp8_decode_v_from_k", "o[x] += scores[t] * vd[row * head_dim + x];",
      "o[x] += scores[t] * kd[row * head_dim + x];"),
+    ("fp8_prefill_exclusive_diagonal", "attend_one_f64(q_row, w->kd, w->vd, bt, c + i + 1, kvh",
+     "attend_one_f64(q_row, w->kd, w->vd, bt, c + i, kvh"),
+    ("fp8_prefill_v_from_k", "out_row[x] += scores[t] * vd[row * head_dim + x];",
+     "out_row[x] += scores[t] * kd[row * head_dim + x];"),
+    ("fp8_prefill_key_block_untranslated",
+     "int64_t row = ((int64_t)block_table[t / block_size] * num_kv_heads + kv_head) *\n                          block_size + t % block_size;\n        double dot",
+     "int64_t row = ((int64_t)(t / block_size) * num_kv_heads + kv_head) *\n                          block_size + t % block_size;\n        double dot"),
+    ("fp8_prefill_scale_dropped",
+     "dot += bf16_bits_to_double(q_row[x]) * kd[row * head_dim + x];\n        scores[t] = scale * dot;",
+     "dot += bf16_bits_to_double(q_row[x]) * kd[row * head_dim + x];\n        scores[t] = dot;"),
     # rotary position embedding
     ("rope_rotates_backwards", "float y1 = a - b;", "float y1 = a + b;"),
     ("rope_interleaved_pairs", "float x2 = bf16_bits_to_float(xr[i + half]);",
