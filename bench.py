@@ -935,6 +935,36 @@ def bench_prefill(args, torch, B, W, dev):
     fl = prefill_flops(wl)
     tf = fl / (at_ms * 1e-3) / 1e12
     peak = mfma_peak_rocminfo()
+
+    # the same prefill over an FP8 cache (random codes and scales in every
+    # slot; the new tokens quantized into it by pkv_store_fp8)
+    pools = W.make_fp8_pools(wl, device=dev, nan_fill=False)
+
+    def run8():
+        B.pkv_prefill_attn_fp8(t["q"], *pools, t["block_tables"], t["cu_new_lens"],
+                               t["context_lens"], wl.scale, out, max_new_len=wl.max_new_len,
+                               max_context_len=wl.max_context_len)
+
+    def store8():
+        B.pkv_store_fp8(t["k_new"], t["v_new"], t["slot_mapping"], *pools)
+
+    store8()
+    for _ in range(2):
+        run8()
+    torch.cuda.synchronize()
+    evs8 = []
+    for _ in range(args.prefill_iters):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        store8()
+        b.record(stream)
+        run8()
+        c.record(stream)
+        evs8.append((a, b, c))
+    torch.cuda.synchronize()
+    st8 = float(np.median([a.elapsed_time(b) for a, b, _ in evs8]))
+    at8 = float(np.median([b.elapsed_time(c) for _, b, c in evs8]))
+    tf8 = fl / (at8 * 1e-3) / 1e12
     return {
         "workload": "chunked causal prefill: 8 prompts x 2048 new tokens, cached U{0..4096}, "
                     "32q/8kv, d 128",
@@ -945,6 +975,11 @@ def bench_prefill(args, torch, B, W, dev):
         "causal_gflop": round(fl / 1e9, 2),
         "store_ms": round(st_ms, 4),
         "store_gbs": round(store_bytes(wl) / (st_ms * 1e-3) / 1e9, 2),
+        "fp8": {"launch": "pkv_prefill_attn_fp8 (E4M3 cache, bf16 matrix products on the codes)",
+                "attn_ms": round(at8, 4), "attn_tflops": round(tf8, 2),
+                "mfma_peak_frac": round(tf8 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "time_vs_bf16": round(at8 / at_ms, 4),
+                "store_fp8_ms": round(st8, 4)},
     }
 
 

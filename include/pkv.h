@@ -453,6 +453,23 @@ int pkv_decode_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block
                         hipStream_t stream);
 
 /*
+ * pkv_prefill_attn_fp8 -- pkv_prefill_attn over an FP8 cache: the same
+ * chunked causal attention ([NVE] §3.2; [LLM4] §22) on the cached values
+ * code_value * scale ([LLM4] §17.6), bf16 q and out.  Q K^T and P V run on the
+ * matrix cores on the codes (every E4M3 value is exactly a bf16 value); each
+ * key's K scale multiplies its scores, and its V scale its weights before
+ * their rounding to bf16, the weight sum adding each rounded weight over the
+ * V scale.  The new tokens' codes and scales must be stored (pkv_store_fp8)
+ * before the call.  Arguments, preconditions and errors as for
+ * pkv_prefill_attn, with the cache as for pkv_decode_attn_fp8.
+ */
+int pkv_prefill_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t max_new_len,
+                         int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                         hipStream_t stream);
+
+/*
  * pkv_store_decode_attn_fp8 -- pkv_store_decode_attn over an FP8 cache: the
  * store of each sequence's new token, quantized exactly as pkv_store_fp8 does
  * (codes and scale to slot_mapping[s]'s row), followed by pkv_decode_attn_fp8

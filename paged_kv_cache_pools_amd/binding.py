@@ -30,6 +30,7 @@ EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_by
             "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
             "pkv_prefill_attn", "pkv_mixed_attn", "pkv_mixed_workspace_bytes", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_store_decode_attn_fp8",
+            "pkv_prefill_attn_fp8",
             "pkv_kv_bytes", "pkv_read_probe",
             "pkv_status_string", "pkv_last_error",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
@@ -142,6 +143,9 @@ def _open(path: str):
     lib.pkv_prefill_attn.restype = ctypes.c_int
     lib.pkv_prefill_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
                                      ctypes.c_float, _P, _P]
+    lib.pkv_prefill_attn_fp8.restype = ctypes.c_int
+    lib.pkv_prefill_attn_fp8.argtypes = [_P, PkvCacheFp8, _P, _I32, _P, _P, _I32, _I32, _I32, _I32,
+                                         ctypes.c_float, _P, _P]
     lib.pkv_pool_create.restype = ctypes.c_int
     lib.pkv_pool_create.argtypes = [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_void_p)]
     lib.pkv_pool_destroy.restype = None
@@ -637,6 +641,34 @@ def pkv_store_fp8(k, v, slot_mapping, k_codes, v_codes, k_scale, v_scale, stream
         raise ValueError(f"k/v must be {want}, got {tuple(k.shape)} / {tuple(v.shape)}")
     _check(lib.pkv_store_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), t, cache,
                              _stream(k_codes, stream)), "pkv_store_fp8")
+
+
+def pkv_prefill_attn_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, cu_new_lens,
+                         context_lens, scale, out, max_new_len: int, max_context_len: int,
+                         stream=None):
+    """pkv_prefill_attn over an FP8 cache (see pkv_store_fp8 for its layout)."""
+    import torch
+
+    lib = load()
+    cache = _cache_fp8(k_codes, v_codes, k_scale, v_scale)
+    _need(q, "q", torch.bfloat16, 3)
+    _need(out, "out", torch.bfloat16, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(cu_new_lens, "cu_new_lens", torch.int32, 1)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    total, hq, d = q.shape
+    s = context_lens.shape[0]
+    if tuple(out.shape) != (total, hq, d) or d != cache.head_dim:
+        raise ValueError(f"q {tuple(q.shape)}, out {tuple(out.shape)}, head_dim {cache.head_dim}")
+    if cu_new_lens.shape[0] != s + 1 or block_tables.shape[0] != s:
+        raise ValueError("cu_new_lens / block_tables do not match context_lens")
+    _check(lib.pkv_prefill_attn_fp8(q.data_ptr(), cache, block_tables.data_ptr(),
+                                    block_tables.shape[1], cu_new_lens.data_ptr(),
+                                    context_lens.data_ptr(), s, int(max_new_len),
+                                    int(max_context_len), hq, float(scale), out.data_ptr(),
+                                    _stream(q, stream)),
+           "pkv_prefill_attn_fp8")
+    return out
 
 
 def pkv_decode_attn_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens, scale,

@@ -157,6 +157,58 @@ int32_t fused_waves_for(int64_t units, int32_t max_context_len, int64_t kTargetW
     return ceil_div(max_context_len, w) > limit ? 0 : w;
 }
 
+// pkv_prefill_attn over either cache: argument checks, then the launch.
+int prefill_call(const void *q, const CacheDesc &cache, const int32_t *block_tables,
+                 int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                 const int32_t *context_lens, int32_t num_seqs, int32_t max_new_len,
+                 int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                 hipStream_t stream, const char *what) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
+    if (num_seqs < 0 || max_new_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d, max_new_len %d, max_context_len %d", num_seqs,
+                    max_new_len, max_context_len);
+    if (num_seqs == 0 || max_new_len == 0) return ok();
+    if (max_new_len > max_context_len)
+        return fail(PKV_ERR_SHAPE, "max_new_len %d exceeds max_context_len %d", max_new_len,
+                    max_context_len);
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
+        return fail(PKV_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq %d x 16",
+                    max_context_len, max_blocks_per_seq);
+    if (cache.num_blocks == 0)
+        return fail(PKV_ERR_SHAPE, "an empty pool cannot hold a context of %d tokens",
+                    max_context_len);
+    if (!q || !out || !context_lens || !cu_new_lens || !block_tables)
+        return fail(PKV_ERR_NULL, "q, out, cu_new_lens, context_lens or block_tables is null");
+    if (!aligned16(q) || !aligned16(out))
+        return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
+    if (num_seqs > 65535 || cache.num_kv_heads > 65535)
+        return fail(PKV_ERR_SHAPE, "num_seqs %d / num_kv_heads %d exceed one launch's grid",
+                    num_seqs, cache.num_kv_heads);
+    pkv::PrefillArgs a{};
+    a.q = q;
+    a.k_cache = cache.k;
+    a.v_cache = cache.v;
+    a.k_scale = cache.k_scale;
+    a.v_scale = cache.v_scale;
+    a.fp8 = cache.fp8;
+    a.block_tables = block_tables;
+    a.cu_new_lens = cu_new_lens;
+    a.context_lens = context_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_seqs = num_seqs;
+    a.max_new_len = max_new_len;
+    a.max_context_len = max_context_len;
+    a.num_blocks = cache.num_blocks;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache.num_kv_heads;
+    a.head_dim = cache.head_dim;
+    a.scale = scale;
+    a.out = out;
+    return hip_status(pkv::launch_prefill(a, stream), what);
+}
+
 }  // namespace
 
 namespace {
@@ -604,47 +656,19 @@ int pkv_prefill_attn(const void *q, pkv_cache cache, const int32_t *block_tables
                      const int32_t *context_lens, int32_t num_seqs, int32_t max_new_len,
                      int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
                      hipStream_t stream) {
-    int rc = check_cache(cache);
-    if (rc) return rc;
-    if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
-    if (num_seqs < 0 || max_new_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
-        return fail(PKV_ERR_SHAPE, "num_seqs %d, max_new_len %d, max_context_len %d", num_seqs,
-                    max_new_len, max_context_len);
-    if (num_seqs == 0 || max_new_len == 0) return ok();
-    if (max_new_len > max_context_len)
-        return fail(PKV_ERR_SHAPE, "max_new_len %d exceeds max_context_len %d", max_new_len,
-                    max_context_len);
-    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlock)
-        return fail(PKV_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq %d x 16",
-                    max_context_len, max_blocks_per_seq);
-    if (cache.num_blocks == 0)
-        return fail(PKV_ERR_SHAPE, "an empty pool cannot hold a context of %d tokens",
-                    max_context_len);
-    if (!q || !out || !context_lens || !cu_new_lens || !block_tables)
-        return fail(PKV_ERR_NULL, "q, out, cu_new_lens, context_lens or block_tables is null");
-    if (!aligned16(q) || !aligned16(out))
-        return fail(PKV_ERR_ALIGN, "q / out must be 16-byte aligned");
-    if (num_seqs > 65535 || cache.num_kv_heads > 65535)
-        return fail(PKV_ERR_SHAPE, "num_seqs %d / num_kv_heads %d exceed one launch's grid",
-                    num_seqs, cache.num_kv_heads);
-    pkv::PrefillArgs a{};
-    a.q = q;
-    a.k_cache = cache.k;
-    a.v_cache = cache.v;
-    a.block_tables = block_tables;
-    a.cu_new_lens = cu_new_lens;
-    a.context_lens = context_lens;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.num_seqs = num_seqs;
-    a.max_new_len = max_new_len;
-    a.max_context_len = max_context_len;
-    a.num_blocks = cache.num_blocks;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = cache.num_kv_heads;
-    a.head_dim = cache.head_dim;
-    a.scale = scale;
-    a.out = out;
-    return hip_status(pkv::launch_prefill(a, stream), "pkv_prefill_attn launch");
+    return prefill_call(q, desc_of(cache), block_tables, max_blocks_per_seq, cu_new_lens,
+                        context_lens, num_seqs, max_new_len, max_context_len, num_q_heads, scale,
+                        out, stream, "pkv_prefill_attn launch");
+}
+
+int pkv_prefill_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                         const int32_t *context_lens, int32_t num_seqs, int32_t max_new_len,
+                         int32_t max_context_len, int32_t num_q_heads, float scale, void *out,
+                         hipStream_t stream) {
+    return prefill_call(q, desc_of(cache), block_tables, max_blocks_per_seq, cu_new_lens,
+                        context_lens, num_seqs, max_new_len, max_context_len, num_q_heads, scale,
+                        out, stream, "pkv_prefill_attn_fp8 launch");
 }
 
 }  // extern "C"

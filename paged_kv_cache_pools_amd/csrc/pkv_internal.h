@@ -73,6 +73,8 @@ hipError_t noalloc_scratch(void **ptr);
 struct PrefillArgs {
     const void *q;
     const void *k_cache, *v_cache;
+    const float *k_scale = nullptr, *v_scale = nullptr;  // FP8 cache (prefill only)
+    bool fp8 = false;
     const int32_t *block_tables;
     const int32_t *cu_new_lens;
     const int32_t *context_lens;

@@ -51,6 +51,19 @@
 //
 // Keys at or past the context end are zero in LDS (V) or masked by select (S),
 // so NaN bits in unused slots never reach the output.
+//
+// FP8 cache (the standalone prefill only): K and V arrive as OCP E4M3 codes
+// with one fp32 scale per (token, KV head).  Every E4M3 value is exactly a
+// bf16 value, so the codes are converted once per workgroup while staged
+// (global -> registers -> LDS, K like V) and the matrix products run on them
+// unchanged; the scales enter the scalar work instead.  A key's K scale
+// multiplies its scores before the mask and the maximum; its V scale
+// multiplies its weights before their rounding to bf16, so P V sums weight
+// times code times scale, and the weight sum adds each rounded weight times
+// the reciprocal of the V scale, so the normalisation again matches what
+// multiplied V (the FP8 decode path's rule).  The per-lane weight sums are
+// reduced across the column's lanes at the end.  Keys past the context end
+// get scales 0 in LDS, so their NaN scales never reach the output.
 #pragma once
 
 #include <math.h>
@@ -107,6 +120,25 @@ __device__ __forceinline__ float max_xor32(float x) {
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
+__device__ __forceinline__ float add_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Eight OCP E4M3 codes (bytes of u, in order) to eight bf16 values, packed in
+// pairs: the gfx950 conversion at scale 1 is exact (E4M3 is a subset of bf16).
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+    return make_uint4(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true)));
+}
+
 // The running maximum is raised only when it grows by more than this (log2
 // units), which bounds every softmax weight by 2^8.
 constexpr float kRescaleLog2 = 8.0f;
@@ -115,7 +147,7 @@ constexpr float kRescaleLog2 = 8.0f;
 // their maxima (no wait on them).
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <int D, int G, int NW = 4>
+template <int D, int G, int NW = 4, bool FP8 = false>
 struct PrefillGeom {
     static constexpr int WAVES = NW;
     static constexpr int THREADS = 64 * WAVES;
@@ -132,10 +164,13 @@ struct PrefillGeom {
     static constexpr int VROW = KC * 2 + 8;      // bytes per V^T row in LDS (34 dwords)
     static constexpr int KBYTES = KC * KROW;
     static constexpr int VBYTES = D * VROW;
-    static constexpr int BUF = KBYTES + VBYTES;  // one LDS buffer
+    // FP8: per key of the chunk its K scale, V scale and reciprocal V scale
+    static constexpr int SBYTES = FP8 ? 3 * KC * 4 : 0;
+    static constexpr int BUF = KBYTES + VBYTES + SBYTES;  // one LDS buffer
     static constexpr int CPB = kBlockTokens * D / 8;   // 16-byte chunks per block tile
     static constexpr int KLOADS = KC * D / 8 / THREADS;  // K direct loads per thread
     static constexpr int VITEMS = (KC / 2) * (D / 8) / THREADS;  // V key-pair items per thread
+    static constexpr int KITEMS = KC * (D / 16) / THREADS;       // FP8: 16-code K items per thread
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
     static_assert(CPB % 64 == 0 && D % 64 == 0, "a wave's staging stays inside one block");
@@ -205,19 +240,27 @@ __device__ __forceinline__ int prefill_segments(int nchunks, int slots,
 //
 // CROSS: the unit's queries and keys come from `cross` instead of prompt p
 // (p, cu_new_lens and context_lens are not read).
-template <int D, int G, bool SPLIT = false, bool CROSS = false, int NW = 4>
+//
+// FP8: k_cache / v_cache hold E4M3 codes (one byte per element, the same
+// [block][KV head][16][D] layout) and k_scale / v_scale their fp32 scales
+// [block][KV head][16]; `lds` holds 2 * PrefillGeom<D, G, NW, true>::BUF bytes.
+template <int D, int G, bool SPLIT = false, bool CROSS = false, int NW = 4, bool FP8 = false>
 __device__ __forceinline__ void prefill_unit(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ cu_new_lens, const int32_t *__restrict__ context_lens,
     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks, int32_t num_q_heads,
     int32_t num_kv_heads, float scale_log2, uint16_t *__restrict__ out, int p, int qb, int kvh,
-    unsigned char *lds, const SplitSlot &split = SplitSlot{}, const CrossGeom &cross = CrossGeom{}) {
-    using Geo = PrefillGeom<D, G, NW>;
+    unsigned char *lds, const SplitSlot &split = SplitSlot{}, const CrossGeom &cross = CrossGeom{},
+    const float *__restrict__ k_scale = nullptr, const float *__restrict__ v_scale = nullptr) {
+    using Geo = PrefillGeom<D, G, NW, FP8>;
     static_assert(!SPLIT || NW == 4, "split units use the 4-wave partial layout");
+    static_assert(!FP8 || (!SPLIT && !CROSS), "the FP8 cache is read by the plain prefill only");
     constexpr int TW = Geo::TW, TWG = Geo::TWG, KC = Geo::KC, KSTEPS = Geo::KSTEPS, NT = Geo::NT;
     constexpr int MT = Geo::MT, KROW = Geo::KROW, VROW = Geo::VROW, CPR = Geo::CPR;
-    constexpr int KLOADS = Geo::KLOADS, VITEMS = Geo::VITEMS;
+    constexpr int KLOADS = Geo::KLOADS, VITEMS = Geo::VITEMS, KITEMS = Geo::KITEMS;
+    const uint8_t *const k_codes = reinterpret_cast<const uint8_t *>(k_cache);
+    const uint8_t *const v_codes = reinterpret_cast<const uint8_t *>(v_cache);
     const float kNegInf = -INFINITY;
 
     const int tid = threadIdx.x;
@@ -293,11 +336,13 @@ __device__ __forceinline__ void prefill_unit(
     // weight sum, which arrives in all 4 rows of ol[nt] (every lane holds it)
     float m[NT];
     f32x4_t ol[NT];
+    float lf[NT];  // FP8: this lane's share of the column's weight sum
     const uint4 ones = make_uint4(kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         m[nt] = kNegInf;
         ol[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lf[nt] = 0.f;
     }
     // positions of this wave's first and last live token: chunks wholly below
     // the first need no causal mask, chunks wholly above the last are skipped
@@ -326,6 +371,7 @@ __device__ __forceinline__ void prefill_unit(
         return pb;
     };
     auto stage_k = [&](unsigned char *buf, int k0) {
+        if constexpr (FP8) return;  // FP8 K is staged through registers (stage_load)
 #pragma unroll
         for (int it = 0; it < KLOADS; ++it) {
             const int g = it * Geo::WAVES + w;            // 1 KiB segment of the K buffer
@@ -341,7 +387,52 @@ __device__ __forceinline__ void prefill_unit(
     };
     uint4 vreg[VITEMS][2];
     int keys[VITEMS];  // first key of each V item being staged
+    // FP8: the chunk's K codes (16 per item: key row id / (D / 16), codes
+    // 16 (id % (D / 16)) ..), V codes (8 per key of each V item), and the K and
+    // V scales of key `lane` (wave 0), between their load and their LDS write
+    uint4 kcode[FP8 ? KITEMS : 1];
+    uint2 vcode[FP8 ? VITEMS : 1][2];
+    float ksc = 0.f, vsc = 0.f;
+    int staged_k0 = 0;
+    auto stage_load_fp8 = [&](int k0) {
+        staged_k0 = k0;
+#pragma unroll
+        for (int it = 0; it < KITEMS; ++it) {
+            const int id = it * Geo::THREADS + tid;
+            const int r = id / (D / 16), jj = id % (D / 16);
+            // a wave's items lie in one cache block (8 or 16 rows)
+            const int lb = __builtin_amdgcn_readfirstlane(k0 / kBlockTokens + r / kBlockTokens);
+            const uint8_t *src = k_codes +
+                                 (((size_t)block_id(lb) * num_kv_heads + kvh) * kBlockTokens + r % kBlockTokens) * D +
+                                 jj * 16;
+            kcode[it] = *reinterpret_cast<const uint4 *>(src);
+        }
+#pragma unroll
+        for (int it = 0; it < VITEMS; ++it) {
+            const int id = it * Geo::THREADS + tid;
+            const int blk = __builtin_amdgcn_readfirstlane(id / D);  // D items per block
+            const int within = id % D;
+            const int pair = within % 8, dc = within / 8;
+            const int lb = k0 / kBlockTokens + blk;
+            const uint2 *base = reinterpret_cast<const uint2 *>(
+                v_codes + ((size_t)block_id(lb) * num_kv_heads + kvh) * kBlockTokens * D);
+            vcode[it][0] = base[(2 * pair) * (D / 8) + dc];
+            vcode[it][1] = base[(2 * pair + 1) * (D / 8) + dc];
+            keys[it] = lb * kBlockTokens + 2 * pair;
+        }
+        if (w == 0) {  // uniform: one scale pair per key of the chunk
+            const int key = k0 + lane;
+            const size_t row = ((size_t)block_id(key / kBlockTokens) * num_kv_heads + kvh) * kBlockTokens +
+                               key % kBlockTokens;
+            ksc = key < ctx ? k_scale[row] : 0.f;
+            vsc = key < ctx ? v_scale[row] : 0.f;
+        }
+    };
     auto stage_load = [&](int k0) {
+        if constexpr (FP8) {
+            stage_load_fp8(k0);
+            return;
+        }
 #pragma unroll
         for (int it = 0; it < VITEMS; ++it) {
             const int id = it * Geo::THREADS + tid;
@@ -372,6 +463,41 @@ __device__ __forceinline__ void prefill_unit(
     };
     auto stage_store = [&](unsigned char *buf) {
         unsigned char *lv = buf + Geo::KBYTES;
+        if constexpr (FP8) {
+            // K: each item's 16 codes as two swizzled 16-byte slots of bf16
+#pragma unroll
+            for (int it = 0; it < KITEMS; ++it) {
+                const int id = it * Geo::THREADS + tid;
+                const int r = id / (D / 16), jj = id % (D / 16);
+                unsigned char *row = buf + r * KROW;
+                *reinterpret_cast<uint4 *>(row + Geo::kslot(r, 2 * jj) * 16) =
+                    e4m3x8_to_bf16(kcode[it].x, kcode[it].y);
+                *reinterpret_cast<uint4 *>(row + Geo::kslot(r, 2 * jj + 1) * 16) =
+                    e4m3x8_to_bf16(kcode[it].z, kcode[it].w);
+            }
+            if (w == 0) {
+                float *sb = reinterpret_cast<float *>(buf + Geo::KBYTES + Geo::VBYTES);
+                sb[lane] = ksc;
+                sb[KC + lane] = vsc;
+                sb[2 * KC + lane] = vsc != 0.f ? __builtin_amdgcn_rcpf(vsc) : 0.f;
+            }
+            // V: the codes as bf16, zero past the context end (as below)
+#pragma unroll
+            for (int it = 0; it < VITEMS; ++it) {
+                vreg[it][0] = e4m3x8_to_bf16(vcode[it][0].x, vcode[it][0].y);
+                vreg[it][1] = e4m3x8_to_bf16(vcode[it][1].x, vcode[it][1].y);
+            }
+            if (staged_k0 + KC > ctx) {
+#pragma unroll
+                for (int it = 0; it < VITEMS; ++it) {
+                    const uint32_t k0m = keys[it] < ctx ? 0xffffffffu : 0u;
+                    const uint32_t k1m = keys[it] + 1 < ctx ? 0xffffffffu : 0u;
+                    uint4 &x0 = vreg[it][0], &x1 = vreg[it][1];
+                    x0 = make_uint4(x0.x & k0m, x0.y & k0m, x0.z & k0m, x0.w & k0m);
+                    x1 = make_uint4(x1.x & k1m, x1.y & k1m, x1.z & k1m, x1.w & k1m);
+                }
+            }
+        }
 #pragma unroll
         for (int it = 0; it < VITEMS; ++it) {
             const int id = it * Geo::THREADS + tid;
@@ -422,6 +548,27 @@ __device__ __forceinline__ void prefill_unit(
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) s[t][nt] = mfma16x16x32(kfr[ks][t], qf[nt][ks], s[t][nt]);
                 }
+            }
+            // FP8: this lane's keys' scales (s[t][nt][r] is key 32 hf + 16 t + 4 a + r)
+            float4 fks[2], fvs[2], frv[2];
+            if constexpr (FP8) {
+                const float *sb = reinterpret_cast<const float *>(buf + Geo::KBYTES + Geo::VBYTES);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int k = hf * 32 + t * 16 + a * 4;
+                    fks[t] = *reinterpret_cast<const float4 *>(sb + k);
+                    fvs[t] = *reinterpret_cast<const float4 *>(sb + KC + k);
+                    frv[t] = *reinterpret_cast<const float4 *>(sb + 2 * KC + k);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        s[t][nt][0] *= fks[t].x;
+                        s[t][nt][1] *= fks[t].y;
+                        s[t][nt][2] *= fks[t].z;
+                        s[t][nt][3] *= fks[t].w;
+                    }
             }
 
             // V^T fragments of the half, read now so the softmax hides their latency
@@ -477,7 +624,10 @@ __device__ __forceinline__ void prefill_unit(
                     const float mc = fmaxf(m[nt], bms);
                     const float alpha = (mc == kNegInf) ? 1.f : exp2f(m[nt] - mc);
                     m[nt] = mc;
-                    ol[nt] *= alpha;
+                    if constexpr (FP8)
+                        lf[nt] *= alpha;
+                    else
+                        ol[nt] *= alpha;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
                 }
@@ -506,6 +656,17 @@ __device__ __forceinline__ void prefill_unit(
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
                             s[t][nt][r] = (dead >> ((t * NT + nt) * 4 + r)) & 1u ? 0.f : s[t][nt][r];
+            }
+            if constexpr (FP8) {  // weight times V scale (0 past the context end)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        s[t][nt][0] *= fvs[t].x;
+                        s[t][nt][1] *= fvs[t].y;
+                        s[t][nt][2] *= fvs[t].z;
+                        s[t][nt][3] *= fvs[t].w;
+                    }
             }
             if (precise) {
 #pragma unroll
@@ -537,9 +698,29 @@ __device__ __forceinline__ void prefill_unit(
                     for (int nt = 0; nt < NT; ++nt)
                         o[mt + u][nt] = mfma16x16x32(vf[u], ph[nt], o[mt + u][nt]);
             }
-            // the weight sums of the half, from the same bf16 weights
+            // the weight sums of the half, from the same bf16 weights (FP8:
+            // each over its key's V scale, in this lane's share)
+            auto fp8_sum = [&](const uint4 (&p)[NT]) {
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) ol[nt] = mfma16x16x32(ones, ph[nt], ol[nt]);
+                for (int nt = 0; nt < NT; ++nt) {
+                    float acc = lf[nt];
+                    acc = fmaf(__uint_as_float(p[nt].x << 16), frv[0].x, acc);
+                    acc = fmaf(__uint_as_float(p[nt].x & 0xffff0000u), frv[0].y, acc);
+                    acc = fmaf(__uint_as_float(p[nt].y << 16), frv[0].z, acc);
+                    acc = fmaf(__uint_as_float(p[nt].y & 0xffff0000u), frv[0].w, acc);
+                    acc = fmaf(__uint_as_float(p[nt].z << 16), frv[1].x, acc);
+                    acc = fmaf(__uint_as_float(p[nt].z & 0xffff0000u), frv[1].y, acc);
+                    acc = fmaf(__uint_as_float(p[nt].w << 16), frv[1].z, acc);
+                    acc = fmaf(__uint_as_float(p[nt].w & 0xffff0000u), frv[1].w, acc);
+                    lf[nt] = acc;
+                }
+            };
+            if constexpr (FP8) {
+                fp8_sum(ph);
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) ol[nt] = mfma16x16x32(ones, ph[nt], ol[nt]);
+            }
             if (precise) {  // the lo parts, into O and the sums alike
 #pragma unroll
                 for (int mt = 0; mt < MT; mt += 2) {
@@ -550,8 +731,12 @@ __device__ __forceinline__ void prefill_unit(
                         for (int nt = 0; nt < NT; ++nt)
                             o[mt + u][nt] = mfma16x16x32(vf[u], pl[nt], o[mt + u][nt]);
                 }
+                if constexpr (FP8) {
+                    fp8_sum(pl);
+                } else {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) ol[nt] = mfma16x16x32(ones, pl[nt], ol[nt]);
+                    for (int nt = 0; nt < NT; ++nt) ol[nt] = mfma16x16x32(ones, pl[nt], ol[nt]);
+                }
             }
         }
     };
@@ -583,7 +768,7 @@ __device__ __forceinline__ void prefill_unit(
     // ---- the column sums of the weights (each lane holds its column's)
     float lt[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) lt[nt] = ol[nt][0];
+    for (int nt = 0; nt < NT; ++nt) lt[nt] = FP8 ? add_xor32(add_xor16(lf[nt])) : ol[nt][0];
 
     if constexpr (SPLIT) {
         if (split.ws_out != nullptr) {  // uniform: rows of a split-KV workspace

@@ -237,6 +237,13 @@ def test_fp8_validation(lib):
     assert sd(c=c8(ks=0)) == 1 and sd(c=c8(d=96)) == 3
     assert sd(q=0) == 1                     # the decode checks still apply
     assert B.pkv_last_error() != ""
+    pf = lambda c=None, q=FAKE, s=2, mn=16, mc=40, hq=4: lib.pkv_prefill_attn_fp8(
+        q, c or c8(), FAKE, 4, FAKE, FAKE, s, mn, mc, hq, ctypes.c_float(0.125), FAKE, None)
+    assert pf(s=0) == 0 and pf(mn=0) == 0   # nothing to attend: nothing launched
+    assert pf(c=c8(ks=0)) == 1 and pf(c=c8(vs=FAKE + 4)) == 4 and pf(c=c8(d=96)) == 3
+    assert pf(mn=50) == 2 and pf(mc=80) == 2 and pf(hq=5) == 2
+    assert pf(q=0) == 1
+    assert "null" in B.pkv_last_error()
 
 
 def test_fp8_partition_heuristic(lib):
