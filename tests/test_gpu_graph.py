@@ -1,5 +1,5 @@
-"""The decode step (bf16 and FP8 caches), the mixed step and the shared-prefix
-decode captured in a HIP graph (torch.cuda.graph) and replayed: none of their
+"""The decode step (bf16 and FP8 caches), the FP8 chunked prefill, the mixed
+step and the shared-prefix decode captured in a HIP graph (torch.cuda.graph) and replayed: none of their
 launches records a memset, so every replay must reproduce the eager result bit
 for bit, with eager work and synchronisations between the replays."""
 import numpy as np
@@ -88,6 +88,24 @@ def test_graph_fp8_decode(part):
                                         outs[l], max_context_len=wl.max_context_len, workspace=ws,
                                         partition_tokens=p)
     replay_and_check(step, outs, f"fp8 decode P{p}")
+
+
+def test_graph_fp8_prefill():
+    """The FP8 quantizing store of a chunked-prefill batch and the prefill over
+    the FP8 cache, as one graph."""
+    wl = W.make_prefill("graph_pf8", [0, 37, 300, 1500], [70, 16, 129, 64], 32, 8, 128, 314,
+                        spare_blocks=1)
+    t = W.make_tensors(wl, device="cuda", nan_fill=True)
+    pools = W.make_fp8_pools(wl, device="cuda", seed=314)
+    out = torch.empty_like(t["q"])
+    say("[gpu] graph: FP8 store + chunked prefill")
+
+    def step():
+        B.pkv_store_fp8(t["k_new"], t["v_new"], t["slot_mapping"], *pools)
+        B.pkv_prefill_attn_fp8(t["q"], *pools, t["block_tables"], t["cu_new_lens"],
+                               t["context_lens"], wl.scale, out, max_new_len=wl.max_new_len,
+                               max_context_len=wl.max_context_len)
+    replay_and_check(step, [out], "fp8 prefill")
 
 
 def test_graph_split_decode():
