@@ -84,7 +84,11 @@ typedef enum {
 } pkv_status;
 
 /* One layer's K and V pools.  k and v are device pointers to bf16 arrays of
- * [num_blocks][num_kv_heads][block_size][head_dim]. */
+ * [num_blocks][num_kv_heads][block_size][head_dim].  Placement is the
+ * caller's; it matters for decode speed through the HBM channels the two
+ * pools' blocks map to: on MI355X a layer's V pool right after its K pool in
+ * one allocation measured up to 3% faster than V a further 2 MiB on, or than
+ * all layers' K pools allocated before all their V pools. */
 typedef struct {
     void *k;
     void *v;
