@@ -37,6 +37,16 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(raw, n), n
 
 
+def test_debug_build_exports_every_declared_symbol(lib):
+    """The debug-bounds build is the same library: a build of older sources
+    (one missing a declared entry point) fails here, before any GPU test."""
+    if not os.path.exists(B.LIB_DEBUG_PATH):
+        pytest.skip("libpkv_debug.so not built")
+    raw = ctypes.CDLL(B.LIB_DEBUG_PATH)
+    for n in header_functions():
+        assert hasattr(raw, n), n
+
+
 def test_kv_bytes_matches_pages(lib):
     # LLM primer part 4, §17.3 and §23.2 lab 2 (tests/golden/kv_sizing.json)
     import json
