@@ -61,9 +61,11 @@
 // multiplies its weights before their rounding to bf16, so P V sums weight
 // times code times scale, and the weight sum adds each rounded weight times
 // the reciprocal of the V scale, so the normalisation again matches what
-// multiplied V (the FP8 decode path's rule).  The per-lane weight sums are
-// reduced across the column's lanes at the end.  Keys past the context end
-// get scales 0 in LDS, so their NaN scales never reach the output.
+// multiplied V (the FP8 decode path's rule).  That sum is the bf16 path's
+// weight-sum MFMA with the reciprocal V scales, split into bf16 hi and lo
+// parts (p = hi + lo to about 2^-16), in place of the all-ones A operand.
+// Keys past the context end get scales 0 in LDS, so their NaN scales never
+// reach the output.
 #pragma once
 
 #include <math.h>
@@ -120,15 +122,6 @@ __device__ __forceinline__ float max_xor32(float x) {
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 
-__device__ __forceinline__ float add_xor16(float x) {
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ __forceinline__ float add_xor32(float x) {
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
 // Eight OCP E4M3 codes (bytes of u, in order) to eight bf16 values, packed in
 // pairs: the gfx950 conversion at scale 1 is exact (E4M3 is a subset of bf16).
 __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -164,8 +157,9 @@ struct PrefillGeom {
     static constexpr int VROW = KC * 2 + 8;      // bytes per V^T row in LDS (34 dwords)
     static constexpr int KBYTES = KC * KROW;
     static constexpr int VBYTES = D * VROW;
-    // FP8: per key of the chunk its K scale, V scale and reciprocal V scale
-    static constexpr int SBYTES = FP8 ? 3 * KC * 4 : 0;
+    // FP8: per key of the chunk its K scale and V scale (fp32), and its
+    // reciprocal V scale as bf16 hi and lo parts
+    static constexpr int SBYTES = FP8 ? 2 * KC * 4 + 2 * KC * 2 : 0;
     static constexpr int BUF = KBYTES + VBYTES + SBYTES;  // one LDS buffer
     static constexpr int CPB = kBlockTokens * D / 8;   // 16-byte chunks per block tile
     static constexpr int KLOADS = KC * D / 8 / THREADS;  // K direct loads per thread
@@ -336,13 +330,11 @@ __device__ __forceinline__ void prefill_unit(
     // weight sum, which arrives in all 4 rows of ol[nt] (every lane holds it)
     float m[NT];
     f32x4_t ol[NT];
-    float lf[NT];  // FP8: this lane's share of the column's weight sum
     const uint4 ones = make_uint4(kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         m[nt] = kNegInf;
         ol[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        lf[nt] = 0.f;
     }
     // positions of this wave's first and last live token: chunks wholly below
     // the first need no causal mask, chunks wholly above the last are skipped
@@ -479,7 +471,12 @@ __device__ __forceinline__ void prefill_unit(
                 float *sb = reinterpret_cast<float *>(buf + Geo::KBYTES + Geo::VBYTES);
                 sb[lane] = ksc;
                 sb[KC + lane] = vsc;
-                sb[2 * KC + lane] = vsc != 0.f ? __builtin_amdgcn_rcpf(vsc) : 0.f;
+                // 1 / V scale as bf16 hi (truncated) + lo (the rest, rounded)
+                const float rv = vsc != 0.f ? __builtin_amdgcn_rcpf(vsc) : 0.f;
+                const uint32_t rb = __float_as_uint(rv);
+                uint16_t *rh = reinterpret_cast<uint16_t *>(sb + 2 * KC);
+                rh[lane] = (uint16_t)(rb >> 16);
+                rh[KC + lane] = (uint16_t)(cvt_pk_bf16(rv - __uint_as_float(rb & 0xffff0000u), 0.f) & 0xffffu);
             }
             // V: the codes as bf16, zero past the context end (as below)
 #pragma unroll
@@ -550,7 +547,8 @@ __device__ __forceinline__ void prefill_unit(
                 }
             }
             // FP8: this lane's keys' scales (s[t][nt][r] is key 32 hf + 16 t + 4 a + r)
-            float4 fks[2], fvs[2], frv[2];
+            float4 fks[2], fvs[2];
+            uint4 rvh, rvl;  // A operands of the weight sum: 1 / V scale of the k-slot's key
             if constexpr (FP8) {
                 const float *sb = reinterpret_cast<const float *>(buf + Geo::KBYTES + Geo::VBYTES);
 #pragma unroll
@@ -558,8 +556,15 @@ __device__ __forceinline__ void prefill_unit(
                     const int k = hf * 32 + t * 16 + a * 4;
                     fks[t] = *reinterpret_cast<const float4 *>(sb + k);
                     fvs[t] = *reinterpret_cast<const float4 *>(sb + KC + k);
-                    frv[t] = *reinterpret_cast<const float4 *>(sb + 2 * KC + k);
                 }
+                // k-slots (a, 0..3) and (a, 4..7) hold keys 4a .. and 16 + 4a .. of the half
+                const uint16_t *rh = reinterpret_cast<const uint16_t *>(sb + 2 * KC);
+                const uint2 h0 = *reinterpret_cast<const uint2 *>(rh + hf * 32 + a * 4);
+                const uint2 h1 = *reinterpret_cast<const uint2 *>(rh + hf * 32 + 16 + a * 4);
+                const uint2 l0 = *reinterpret_cast<const uint2 *>(rh + KC + hf * 32 + a * 4);
+                const uint2 l1 = *reinterpret_cast<const uint2 *>(rh + KC + hf * 32 + 16 + a * 4);
+                rvh = make_uint4(h0.x, h0.y, h1.x, h1.y);
+                rvl = make_uint4(l0.x, l0.y, l1.x, l1.y);
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -624,10 +629,7 @@ __device__ __forceinline__ void prefill_unit(
                     const float mc = fmaxf(m[nt], bms);
                     const float alpha = (mc == kNegInf) ? 1.f : exp2f(m[nt] - mc);
                     m[nt] = mc;
-                    if constexpr (FP8)
-                        lf[nt] *= alpha;
-                    else
-                        ol[nt] *= alpha;
+                    ol[nt] *= alpha;
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) o[mt][nt] *= alpha;
                 }
@@ -699,20 +701,12 @@ __device__ __forceinline__ void prefill_unit(
                         o[mt + u][nt] = mfma16x16x32(vf[u], ph[nt], o[mt + u][nt]);
             }
             // the weight sums of the half, from the same bf16 weights (FP8:
-            // each over its key's V scale, in this lane's share)
+            // each over its key's V scale)
             auto fp8_sum = [&](const uint4 (&p)[NT]) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    float acc = lf[nt];
-                    acc = fmaf(__uint_as_float(p[nt].x << 16), frv[0].x, acc);
-                    acc = fmaf(__uint_as_float(p[nt].x & 0xffff0000u), frv[0].y, acc);
-                    acc = fmaf(__uint_as_float(p[nt].y << 16), frv[0].z, acc);
-                    acc = fmaf(__uint_as_float(p[nt].y & 0xffff0000u), frv[0].w, acc);
-                    acc = fmaf(__uint_as_float(p[nt].z << 16), frv[1].x, acc);
-                    acc = fmaf(__uint_as_float(p[nt].z & 0xffff0000u), frv[1].y, acc);
-                    acc = fmaf(__uint_as_float(p[nt].w << 16), frv[1].z, acc);
-                    acc = fmaf(__uint_as_float(p[nt].w & 0xffff0000u), frv[1].w, acc);
-                    lf[nt] = acc;
+                    ol[nt] = mfma16x16x32(rvh, p[nt], ol[nt]);
+                    ol[nt] = mfma16x16x32(rvl, p[nt], ol[nt]);
                 }
             };
             if constexpr (FP8) {
@@ -768,7 +762,7 @@ __device__ __forceinline__ void prefill_unit(
     // ---- the column sums of the weights (each lane holds its column's)
     float lt[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) lt[nt] = FP8 ? add_xor32(add_xor16(lf[nt])) : ol[nt][0];
+    for (int nt = 0; nt < NT; ++nt) lt[nt] = ol[nt][0];
 
     if constexpr (SPLIT) {
         if (split.ws_out != nullptr) {  // uniform: rows of a split-KV workspace
