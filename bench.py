@@ -880,6 +880,30 @@ def bench_mixed(torch, B, W, dev, name="mixed_step", iters=20):
     mixed_ms, mixed_stats = timed(mixed)
     whole_ms, _ = timed(mixed_whole)
     sep_ms, sep_stats = timed(separate)
+
+    # the same iteration over FP8 caches (random codes and scales, the new
+    # tokens quantized into them by pkv_store_fp8)
+    pools8 = [W.make_fp8_pools(wl, device=dev, seed=wl.seed + l, nan_fill=False) for l in range(2)]
+    for l in range(2):
+        B.pkv_store_fp8(t["k_new"], t["v_new"], t["slot_mapping"], *pools8[l])
+    P8 = B.pkv_decode_partition_tokens_fp8(nd, wl.num_kv_heads, 4096)
+
+    def mixed8(l):
+        B.pkv_mixed_attn_fp8(t["q"], *pools8[l], t["block_tables"], t["cu_new_lens"],
+                             t["context_lens"], nd, wl.scale, out, max_new_len=mnl,
+                             max_context_len=mcl, workspace=ws_mixed)
+
+    def separate8(l):
+        B.pkv_decode_attn_fp8(q_dec, *pools8[l], bt_dec, ctx_dec, wl.scale, out_dec,
+                              max_context_len=4096, workspace=ws, partition_tokens=P8)
+        B.pkv_prefill_attn_fp8(q_pf, *pools8[l], bt_pf, cu_pf, ctx_pf, wl.scale, out_pf,
+                               max_new_len=mnl, max_context_len=mcl)
+
+    for fn in (mixed8, separate8):
+        timed(fn)
+    mixed8_ms, _ = timed(mixed8)
+    sep8_ms, _ = timed(separate8)
+    del pools8
     S, Hq, Hkv, D = wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim
     dec_bytes = (int(wl.context_lens[:nd].sum()) * 2 * Hkv * D * 2 + 2 * nd * Hq * D * 2
                  + 4 * int((-(-wl.context_lens[:nd] // 16)).sum()) + 4 * nd)
@@ -898,6 +922,9 @@ def bench_mixed(torch, B, W, dev, name="mixed_step", iters=20):
             "mixed_us": round(mixed_ms * 1e3, 2), "separate_us": round(sep_ms * 1e3, 2),
             "mixed_unsplit_us": round(whole_ms * 1e3, 2), "split_workspace_bytes": ws_bytes,
             "speedup_vs_separate": round(sep_ms / mixed_ms, 4),
+            "fp8": {"launch": "pkv_mixed_attn_fp8", "mixed_us": round(mixed8_ms * 1e3, 2),
+                    "separate_us": round(sep8_ms * 1e3, 2),
+                    "speedup_vs_separate": round(sep8_ms / mixed8_ms, 4)},
             "decode_bytes": dec_bytes, "prefill_gflop": round(pf_flops / 1e9, 3),
             "roofline": {"bound": "hbm+mfma overlap", "kernel": "mixed_kernel<128,4>",
                          "bound_us": round(bound_ms * 1e3, 2),

@@ -474,6 +474,23 @@ int pkv_prefill_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *bloc
                          hipStream_t stream);
 
 /*
+ * pkv_mixed_attn_fp8 -- pkv_mixed_attn over an FP8 cache ([NVE] §5.1-5.2;
+ * [LLM4] §17.5-17.6): the decode sequences run as pkv_decode_attn_fp8's
+ * single pass with 4 waves, the prefill chunks as pkv_prefill_attn_fp8's
+ * query tiles (split by key range when a workspace is given, as for
+ * pkv_mixed_attn; pkv_mixed_workspace_bytes sizes it).  The new tokens'
+ * codes and scales must be stored (pkv_store_fp8) before the call.
+ * Arguments, preconditions and errors as for pkv_mixed_attn, with the cache
+ * as for pkv_decode_attn_fp8.
+ */
+int pkv_mixed_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                       int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                       const int32_t *context_lens, int32_t num_decode_seqs, int32_t num_seqs,
+                       int32_t max_new_len, int32_t max_context_len, int32_t num_q_heads,
+                       float scale, void *out, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
  * pkv_store_decode_attn_fp8 -- pkv_store_decode_attn over an FP8 cache: the
  * store of each sequence's new token, quantized exactly as pkv_store_fp8 does
  * (codes and scale to slot_mapping[s]'s row), followed by pkv_decode_attn_fp8

@@ -30,7 +30,7 @@ EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_by
             "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
             "pkv_prefill_attn", "pkv_mixed_attn", "pkv_mixed_workspace_bytes", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_store_decode_attn_fp8",
-            "pkv_prefill_attn_fp8",
+            "pkv_prefill_attn_fp8", "pkv_mixed_attn_fp8",
             "pkv_kv_bytes", "pkv_read_probe",
             "pkv_status_string", "pkv_last_error",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
@@ -172,6 +172,9 @@ def _open(path: str):
     lib.pkv_read_probe.argtypes = [_P, _SZ, _P, _P]
     lib.pkv_mixed_attn.restype = ctypes.c_int
     lib.pkv_mixed_attn.argtypes = [_P, PkvCache, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                   ctypes.c_float, _P, _P, _SZ, _P]
+    lib.pkv_mixed_attn_fp8.restype = ctypes.c_int
+    lib.pkv_mixed_attn_fp8.argtypes = [_P, PkvCacheFp8, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
                                    ctypes.c_float, _P, _P, _SZ, _P]
     lib.pkv_mixed_workspace_bytes.restype = _SZ
     lib.pkv_mixed_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32, _I32]
@@ -492,10 +495,25 @@ def pkv_mixed_attn(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens,
     pkv_prefill_attn.  ``workspace``: a uint8 device tensor of at least
     pkv_mixed_workspace_bytes (any contents); None allocates one when
     ``split`` and the sizes call for it, ``split=False`` passes none."""
+    return _mixed("pkv_mixed_attn", _cache(k_cache, v_cache), q, block_tables, cu_new_lens,
+                  context_lens, num_decode, scale, out, max_new_len, max_context_len, workspace,
+                  split, stream)
+
+
+def pkv_mixed_attn_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, cu_new_lens,
+                       context_lens, num_decode: int, scale, out, max_new_len: int,
+                       max_context_len: int, workspace=None, split: bool = True, stream=None):
+    """pkv_mixed_attn over an FP8 cache (see pkv_store_fp8 for its layout)."""
+    return _mixed("pkv_mixed_attn_fp8", _cache_fp8(k_codes, v_codes, k_scale, v_scale), q,
+                  block_tables, cu_new_lens, context_lens, num_decode, scale, out, max_new_len,
+                  max_context_len, workspace, split, stream)
+
+
+def _mixed(name, cache, q, block_tables, cu_new_lens, context_lens, num_decode, scale, out,
+           max_new_len, max_context_len, workspace, split, stream):
     import torch
 
     lib = load()
-    cache = _cache(k_cache, v_cache)
     _need(q, "q", torch.bfloat16, 3)
     _need(out, "out", torch.bfloat16, 3)
     _need(block_tables, "block_tables", torch.int32, 2)
@@ -517,11 +535,11 @@ def pkv_mixed_attn(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens,
         if workspace is not None:
             _need(workspace, "workspace", torch.uint8, 1)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    _check(lib.pkv_mixed_attn(q.data_ptr(), cache, block_tables.data_ptr(), block_tables.shape[1],
+    _check(getattr(lib, name)(q.data_ptr(), cache, block_tables.data_ptr(), block_tables.shape[1],
                               cu_new_lens.data_ptr(), context_lens.data_ptr(), int(num_decode), s,
                               int(max_new_len), int(max_context_len), hq, float(scale),
                               out.data_ptr(), ws_ptr, ws_bytes, _stream(q, stream)),
-           "pkv_mixed_attn")
+           name)
     return out
 
 

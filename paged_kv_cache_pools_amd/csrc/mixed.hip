@@ -50,6 +50,12 @@
 // Sequences 0 .. num_decode-1 are the decode sequences: one new token each.
 // One with more new tokens is still computed in full (its workgroup for a KV
 // head runs every query block of it in turn); one with none writes nothing.
+//
+// Over an FP8 cache (codes + per-(token, KV head) scales) each kind runs the
+// FP8 form of its own launch: the decode units the FP8 decode's (matrix cores
+// above 128 keys, its LDS rings inside this kernel's LDS), the prefill units
+// the FP8 query tile.
+#include "decode_fp8_mfma.h"
 #include "decode_wave.h"
 #include "prefill_tile.h"
 
@@ -73,16 +79,19 @@ __device__ __forceinline__ int prompt_of_rank(const int32_t *__restrict__ contex
     return __ffsll((long long)hit) - 1;
 }
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void mixed_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ v_cache, const float *__restrict__ k_scale,
+    const float *__restrict__ v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ cu_new_lens, const int32_t *__restrict__ context_lens,
     int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_blocks, int32_t num_decode,
     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t num_qblocks,
     float scale_log2, uint16_t *__restrict__ out, float *partials, int32_t seg_slots) {
-    using Geo = PrefillGeom<D, G>;
+    using Geo = PrefillGeom<D, G, 4, FP8>;
     static_assert(kMixedWaves * G * (D + 2) * sizeof(float) <= 2 * Geo::BUF, "decode merge fits the LDS");
+    static_assert(!FP8 || kMixedWaves * Fp8Mma<D>::WAVE_BYTES <= 2 * Geo::BUF,
+                  "the FP8 decode rings fit the LDS");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Geo::BUF];
 
     const int num_prefill = num_seqs - num_decode;
@@ -123,9 +132,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
         if (seg_slots > 1)
             split.partials = partials + (size_t)unit * seg_slots * prefill_partial_floats<D, G>();
         const int p = prompt_of_rank(context_lens, num_decode, num_prefill, rank);
-        prefill_unit<D, G, true>(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens,
-                                 max_blocks_per_seq, max_context_len, num_blocks, num_q_heads,
-                                 num_kv_heads, scale_log2, out, num_decode + p, qb, kvh, lds, split);
+        prefill_unit<D, G, true, false, 4, FP8>(
+            q, k_cache, v_cache, block_tables, cu_new_lens, context_lens, max_blocks_per_seq,
+            max_context_len, num_blocks, num_q_heads, num_kv_heads, scale_log2, out,
+            num_decode + p, qb, kvh, lds, split, CrossGeom{}, k_scale, v_scale);
         return;
     }
 
@@ -137,20 +147,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void m
                                   kvh == 0 && threadIdx.x == 0, s);
     if (n == 1 && ctx >= 1) {
         const size_t row = (size_t)row0 * num_q_heads * D;
-        attend_unit<D, G, false>(q + row, k_cache, v_cache, nullptr, nullptr,
-                                 block_tables + (size_t)s * max_blocks_per_seq, ctx, num_blocks,
-                                 num_q_heads, num_kv_heads, scale_log2, out + row, kvh, kMixedWaves,
-                                 reinterpret_cast<float *>(lds), []() { return NewToken{}; },
-                                 Rope{});
+        const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;
+        if constexpr (FP8) {
+            if (ctx > kExactDecodeKeys) {  // uniform: the FP8 decode's matrix-core path
+                attend_unit_fp8_mfma<D, G>(q + row, reinterpret_cast<const uint8_t *>(k_cache),
+                                           reinterpret_cast<const uint8_t *>(v_cache), k_scale,
+                                           v_scale, bt_row, ctx, num_blocks, num_q_heads,
+                                           num_kv_heads, scale_log2, out + row, kvh, kMixedWaves,
+                                           lds, []() { return NewToken{}; });
+                return;
+            }
+        }
+        attend_unit<D, G, FP8>(q + row, k_cache, v_cache, k_scale, v_scale, bt_row, ctx,
+                               num_blocks, num_q_heads, num_kv_heads, scale_log2, out + row, kvh,
+                               kMixedWaves, reinterpret_cast<float *>(lds),
+                               []() { return NewToken{}; }, Rope{});
         return;
     }
     // not a single token: the prefill tiles of the whole sequence, in turn
     const int nq = (min(n, ctx) + Geo::TWG - 1) / Geo::TWG;
     for (int qb = nq - 1; qb >= 0; --qb) {
         __syncthreads();  // the previous tile's last LDS reads are done
-        prefill_unit<D, G>(q, k_cache, v_cache, block_tables, cu_new_lens, context_lens,
-                           max_blocks_per_seq, max_context_len, num_blocks, num_q_heads,
-                           num_kv_heads, scale_log2, out, s, qb, kvh, lds);
+        prefill_unit<D, G, false, false, 4, FP8>(
+            q, k_cache, v_cache, block_tables, cu_new_lens, context_lens, max_blocks_per_seq,
+            max_context_len, num_blocks, num_q_heads, num_kv_heads, scale_log2, out, s, qb, kvh,
+            lds, SplitSlot{}, CrossGeom{}, k_scale, v_scale);
     }
 }
 
@@ -177,17 +198,18 @@ __global__ __launch_bounds__(256) void mixed_merge_kernel(
                         seg_slots, blockIdx.x % PARTS);
 }
 
-template <int D, int G>
-static hipError_t launch_mixed_t(const MixedArgs &a, hipStream_t stream) {
-    using Geo = PrefillGeom<D, G>;
+template <int D, int G, bool FP8>
+static hipError_t launch_mixed_f(const MixedArgs &a, hipStream_t stream) {
+    using Geo = PrefillGeom<D, G, 4, FP8>;
     const int nqb = a.num_seqs > a.num_decode ? (a.max_new_len + Geo::TWG - 1) / Geo::TWG : 0;
     const int64_t units = (int64_t)a.num_decode * a.num_kv_heads +
                           (int64_t)(a.num_seqs - a.num_decode) * a.num_kv_heads * nqb * a.seg_slots;
     if (units == 0) return hipSuccess;
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((mixed_kernel<D, G>), dim3((unsigned)units), dim3(Geo::THREADS), 0, stream,
-                       (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
-                       (const uint16_t *)a.v_cache, a.block_tables, a.cu_new_lens, a.context_lens,
+    hipLaunchKernelGGL((mixed_kernel<D, G, FP8>), dim3((unsigned)units), dim3(Geo::THREADS), 0,
+                       stream, (const uint16_t *)a.q, (const uint16_t *)a.k_cache,
+                       (const uint16_t *)a.v_cache, a.k_scale, a.v_scale, a.block_tables,
+                       a.cu_new_lens, a.context_lens,
                        a.max_blocks_per_seq, a.max_context_len, a.num_blocks, a.num_decode,
                        a.num_seqs, a.num_q_heads, a.num_kv_heads, nqb, scale_log2,
                        (uint16_t *)a.out, a.partials, a.seg_slots);
@@ -200,6 +222,11 @@ static hipError_t launch_mixed_t(const MixedArgs &a, hipStream_t stream) {
                        a.max_context_len, a.num_decode, a.num_seqs, a.num_q_heads, a.num_kv_heads,
                        nqb, (uint16_t *)a.out, a.partials, a.seg_slots);
     return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_mixed_t(const MixedArgs &a, hipStream_t stream) {
+    return a.fp8 ? launch_mixed_f<D, G, true>(a, stream) : launch_mixed_f<D, G, false>(a, stream);
 }
 
 PKV_DEBUG_WORD_ACCESS(mixed)

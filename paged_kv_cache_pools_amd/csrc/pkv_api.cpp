@@ -244,26 +244,13 @@ MixedSplit mixed_split(int32_t num_seqs, int32_t num_decode_seqs, int32_t max_ne
     return m;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t pkv_mixed_workspace_bytes(int32_t num_seqs, int32_t num_decode_seqs, int32_t max_new_len,
-                                 int32_t max_context_len, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t head_dim) {
-    if (num_seqs < 0 || num_decode_seqs < 0 || num_decode_seqs > num_seqs || max_new_len < 0 ||
-        max_context_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-        num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
-        return 0;
-    return mixed_split(num_seqs, num_decode_seqs, max_new_len, max_context_len, num_q_heads,
-                       num_kv_heads, head_dim).bytes;
-}
-
-int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
-                   int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
-                   const int32_t *context_lens, int32_t num_decode_seqs, int32_t num_seqs,
-                   int32_t max_new_len, int32_t max_context_len, int32_t num_q_heads, float scale,
-                   void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+// pkv_mixed_attn over either cache: argument checks, the split, the launch.
+int mixed_call(const void *q, const CacheDesc &cache, const int32_t *block_tables,
+               int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+               const int32_t *context_lens, int32_t num_decode_seqs, int32_t num_seqs,
+               int32_t max_new_len, int32_t max_context_len, int32_t num_q_heads, float scale,
+               void *out, void *workspace, size_t workspace_bytes, hipStream_t stream,
+               const char *what) {
     int rc = check_cache(cache);
     if (rc) return rc;
     if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
@@ -298,6 +285,9 @@ int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
     a.q = q;
     a.k_cache = cache.k;
     a.v_cache = cache.v;
+    a.k_scale = cache.k_scale;
+    a.v_scale = cache.v_scale;
+    a.fp8 = cache.fp8;
     a.block_tables = block_tables;
     a.cu_new_lens = cu_new_lens;
     a.context_lens = context_lens;
@@ -325,7 +315,46 @@ int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
             a.partials = static_cast<float *>(workspace);
         }
     }
-    return hip_status(pkv::launch_mixed(a, stream), "pkv_mixed_attn launch");
+    return hip_status(pkv::launch_mixed(a, stream), what);
+}
+
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_mixed_workspace_bytes(int32_t num_seqs, int32_t num_decode_seqs, int32_t max_new_len,
+                                 int32_t max_context_len, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim) {
+    if (num_seqs < 0 || num_decode_seqs < 0 || num_decode_seqs > num_seqs || max_new_len < 0 ||
+        max_context_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
+        return 0;
+    return mixed_split(num_seqs, num_decode_seqs, max_new_len, max_context_len, num_q_heads,
+                       num_kv_heads, head_dim).bytes;
+}
+
+int pkv_mixed_attn(const void *q, pkv_cache cache, const int32_t *block_tables,
+                   int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                   const int32_t *context_lens, int32_t num_decode_seqs, int32_t num_seqs,
+                   int32_t max_new_len, int32_t max_context_len, int32_t num_q_heads, float scale,
+                   void *out, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return mixed_call(q, desc_of(cache), block_tables, max_blocks_per_seq, cu_new_lens,
+                      context_lens, num_decode_seqs, num_seqs, max_new_len, max_context_len,
+                      num_q_heads, scale, out, workspace, workspace_bytes, stream,
+                      "pkv_mixed_attn launch");
+}
+
+int pkv_mixed_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                       int32_t max_blocks_per_seq, const int32_t *cu_new_lens,
+                       const int32_t *context_lens, int32_t num_decode_seqs, int32_t num_seqs,
+                       int32_t max_new_len, int32_t max_context_len, int32_t num_q_heads,
+                       float scale, void *out, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    return mixed_call(q, desc_of(cache), block_tables, max_blocks_per_seq, cu_new_lens,
+                      context_lens, num_decode_seqs, num_seqs, max_new_len, max_context_len,
+                      num_q_heads, scale, out, workspace, workspace_bytes, stream,
+                      "pkv_mixed_attn_fp8 launch");
 }
 
 int pkv_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {

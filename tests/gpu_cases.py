@@ -216,3 +216,16 @@ def fp8_quantized_pools(wl, k_cache, v_cache):
             assert np.array_equal(g.cpu().numpy().view(np.uint8), h.view(np.uint8)), \
                 f"FP8 fill differs ({what})"
     return host, dev
+
+
+def random_code_pools(wl):
+    """Uniformly random codes and scales in every slot the sequences' contexts
+    cover (their new tokens included, as after their store); the NaN code and
+    a NaN scale everywhere else.  Returns (host pools, GPU pools)."""
+    host = [x.numpy().copy() for x in W.make_fp8_pools(wl, device="cpu", nan_fill=False)]
+    dead = ~W.live_slot_mask(wl, pre_store=False)
+    nan = fp8_nan_pools(wl)
+    for x, n in zip(host, nan):
+        x.swapaxes(1, 2)[dead] = n.swapaxes(1, 2)[dead]
+    return host, [torch.from_numpy(x).cuda() for x in host]
+

@@ -254,6 +254,13 @@ def test_fp8_validation(lib):
     assert pf(mn=50) == 2 and pf(mc=80) == 2 and pf(hq=5) == 2
     assert pf(q=0) == 1
     assert "null" in B.pkv_last_error()
+    mx = lambda c=None, nd=1, s=3, mn=16, mc=40, q=FAKE: lib.pkv_mixed_attn_fp8(
+        q, c or c8(), FAKE, 4, FAKE, FAKE, nd, s, mn, mc, 4, ctypes.c_float(0.125), FAKE, None, 0,
+        None)
+    assert mx(s=0, nd=0) == 0               # empty batch: nothing launched
+    assert mx(c=c8(ks=0)) == 1 and mx(c=c8(vs=FAKE + 4)) == 4 and mx(c=c8(d=96)) == 3
+    assert mx(nd=4) == 2 and mx(mn=50) == 2 and mx(mc=80) == 2
+    assert mx(q=0) == 1
 
 
 def test_fp8_partition_heuristic(lib):

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_cases import Case, compare, fp8_nan_pools, fp8_quantized_pools, orc, say
+from gpu_cases import Case, compare, fp8_quantized_pools, orc, random_code_pools, say
 from paged_kv_cache_pools_amd import binding as B
 from paged_kv_cache_pools_amd import workloads as W
 
@@ -92,18 +92,6 @@ def test_prefill_fp8_scale_edges(scale):
     say(f"[gpu] prefill fp8 scale {scale}")
     out, ref = quantized_prefill(wl)
     compare(out, ref, f"prefill fp8 scale {scale}", plus_floor=True)
-
-
-def random_code_pools(wl):
-    """Uniformly random codes and scales in every slot the prompts' contexts
-    cover (their new tokens included, as after their store); the NaN code and
-    a NaN scale everywhere else.  Returns (host pools, GPU pools)."""
-    host = [x.numpy().copy() for x in W.make_fp8_pools(wl, device="cpu", nan_fill=False)]
-    dead = ~W.live_slot_mask(wl, pre_store=False)
-    nan = fp8_nan_pools(wl)
-    for x, n in zip(host, nan):
-        x.swapaxes(1, 2)[dead] = n.swapaxes(1, 2)[dead]
-    return host, [torch.from_numpy(x).cuda() for x in host]
 
 
 @pytest.mark.parametrize("d,g", [(64, 1), (128, 4), (128, 8)])
