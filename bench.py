@@ -677,6 +677,8 @@ def bench_other(torch, B, W, dev, name, iters=20):
 def bench_prefix(torch, B, wl, t, out, stream, iters, logical, uniq):
     """The same step as store + pkv_decode_attn_prefix: groups found by
     pkv_prefix_groups on the host tables, each group's prefix read once."""
+    from paged_kv_cache_pools_amd import workloads as W
+
     dev = t["q"].device
     starts, plens, mg = B.pkv_prefix_groups(wl.block_tables, wl.context_lens)
     gs, pl = torch.from_numpy(starts).to(dev), torch.from_numpy(plens).to(dev)
@@ -706,11 +708,48 @@ def bench_prefix(torch, B, wl, t, out, stream, iters, logical, uniq):
         torch.cuda.synchronize()
         sweep["auto" if p == 0 else str(p)] = round(a.elapsed_time(b) * 1e3 / iters, 2)
     us = sweep["auto"]
+
+    # the same step over FP8 caches (random codes and scales; the new tokens
+    # quantized by pkv_store_fp8), against the FP8 fused store + split decode
+    pools8 = [W.make_fp8_pools(wl, device=dev, seed=wl.seed + l, nan_fill=False) for l in range(2)]
+    P8 = B.pkv_decode_partition_tokens_fp8(wl.num_seqs, wl.num_kv_heads, wl.max_context_len)
+    ws8 = torch.empty(max(16, B.pkv_decode_workspace_bytes(wl.num_seqs, wl.num_q_heads,
+                                                           wl.head_dim, wl.max_context_len, P8)),
+                      dtype=torch.uint8, device=dev)
+
+    def run8(l):
+        B.pkv_store_fp8(t["k_new"], t["v_new"], t["slot_mapping"], *pools8[l])
+        B.pkv_decode_attn_prefix_fp8(t["q"], *pools8[l], t["block_tables"], t["context_lens"],
+                                     wl.scale, out, gs, pl, mg, max_context_len=wl.max_context_len,
+                                     workspace=ws)
+
+    def plain8(l):
+        B.pkv_store_decode_attn_fp8(t["k_new"], t["v_new"], t["slot_mapping"], t["q"], *pools8[l],
+                                    t["block_tables"], t["context_lens"], wl.scale, out,
+                                    max_context_len=wl.max_context_len, workspace=ws8,
+                                    partition_tokens=P8)
+
+    fp8 = {}
+    for key, fn in (("us_per_step", run8), ("plain_decode_us", plain8)):
+        for l in (0, 1, 0, 1):
+            fn(l)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(iters):
+            fn(i & 1)
+        b.record(stream)
+        torch.cuda.synchronize()
+        fp8[key] = round(a.elapsed_time(b) * 1e3 / iters, 2)
+    del pools8
+    fp8 = {"launch": "pkv_store_fp8 + pkv_decode_attn_prefix_fp8", **fp8,
+           "plain_decode": "pkv_store_decode_attn_fp8, its own work split",
+           "speedup_vs_plain": round(fp8["plain_decode_us"] / fp8["us_per_step"], 4)}
     return {"groups": len(plens), "prefix_lens": sorted(set(int(x) for x in plens)),
             "max_group_size": int(mg), "us_per_step": us,
             "us_by_partition_tokens": sweep, "logical_kv_gbs": round(logical / us / 1e3, 1),
             "unique_kv_gbs": round(uniq / us / 1e3, 1),
-            "tokens_per_s": round(wl.num_seqs / (us * 1e-6), 1)}
+            "tokens_per_s": round(wl.num_seqs / (us * 1e-6), 1), "fp8": fp8}
 
 
 def bench_pool(torch, B, W, dev, steps=64):

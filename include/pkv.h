@@ -491,6 +491,23 @@ int pkv_mixed_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_
                        hipStream_t stream);
 
 /*
+ * pkv_decode_attn_prefix_fp8 -- pkv_decode_attn_prefix over an FP8 cache
+ * ([LLM4] §17.6-17.7; [NVE] §2.2): each group's shared prefix read once by the
+ * FP8 query tile (MFMA on the codes, scales on the scores and weights), each
+ * sequence's tail by the FP8 decode's VALU path.  Arguments, groups,
+ * workspace (pkv_decode_prefix_workspace_bytes), preconditions and errors as
+ * for pkv_decode_attn_prefix, with the cache as for pkv_decode_attn_fp8.
+ */
+int pkv_decode_attn_prefix_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                               float scale, const int32_t *group_starts,
+                               const int32_t *prefix_lens, int32_t num_groups,
+                               int32_t max_group_size, void *out, void *workspace,
+                               size_t workspace_bytes, int32_t partition_tokens,
+                               hipStream_t stream);
+
+/*
  * pkv_store_decode_attn_fp8 -- pkv_store_decode_attn over an FP8 cache: the
  * store of each sequence's new token, quantized exactly as pkv_store_fp8 does
  * (codes and scale to slot_mapping[s]'s row), followed by pkv_decode_attn_fp8

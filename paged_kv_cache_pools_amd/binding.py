@@ -30,7 +30,7 @@ EXPORTED = ["pkv_store", "pkv_decode_partition_tokens", "pkv_decode_workspace_by
             "pkv_store_decode_attn", "pkv_store_decode_attn_rope",
             "pkv_prefill_attn", "pkv_mixed_attn", "pkv_mixed_workspace_bytes", "pkv_store_fp8",
             "pkv_decode_partition_tokens_fp8", "pkv_decode_attn_fp8", "pkv_store_decode_attn_fp8",
-            "pkv_prefill_attn_fp8", "pkv_mixed_attn_fp8",
+            "pkv_prefill_attn_fp8", "pkv_mixed_attn_fp8", "pkv_decode_attn_prefix_fp8",
             "pkv_kv_bytes", "pkv_read_probe",
             "pkv_status_string", "pkv_last_error",
             "pkv_pool_create", "pkv_pool_destroy", "pkv_pool_add_seq", "pkv_pool_append",
@@ -182,6 +182,10 @@ def _open(path: str):
     lib.pkv_decode_attn_prefix.argtypes = [_P, PkvCache, _P, _I32, _P, _I32, _I32, _I32,
                                            ctypes.c_float, _P, _P, _I32, _I32, _P, _P, _SZ, _I32,
                                            _P]
+    lib.pkv_decode_attn_prefix_fp8.restype = ctypes.c_int
+    lib.pkv_decode_attn_prefix_fp8.argtypes = [_P, PkvCacheFp8, _P, _I32, _P, _I32, _I32, _I32,
+                                               ctypes.c_float, _P, _P, _I32, _I32, _P, _P, _SZ,
+                                               _I32, _P]
     lib.pkv_decode_prefix_workspace_bytes.restype = _SZ
     lib.pkv_decode_prefix_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32]
     lib.pkv_prefix_groups.restype = ctypes.c_int
@@ -607,10 +611,26 @@ def pkv_decode_attn_prefix(q, k_cache, v_cache, block_tables, context_lens, scal
     tensors (see pkv_prefix_groups), ``max_group_size`` a host int bounding
     the sizes of groups with a prefix; other tensors as for pkv_decode_attn.
     ``workspace``: uint8 device tensor, allocated here when None."""
+    return _prefix("pkv_decode_attn_prefix", _cache(k_cache, v_cache), q, block_tables,
+                   context_lens, scale, out, group_starts, prefix_lens, max_group_size,
+                   max_context_len, workspace, partition_tokens, stream)
+
+
+def pkv_decode_attn_prefix_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables,
+                               context_lens, scale, out, group_starts, prefix_lens,
+                               max_group_size: int, max_context_len: Optional[int] = None,
+                               workspace=None, partition_tokens: int = 0, stream=None):
+    """pkv_decode_attn_prefix over an FP8 cache (see pkv_store_fp8 for its layout)."""
+    return _prefix("pkv_decode_attn_prefix_fp8", _cache_fp8(k_codes, v_codes, k_scale, v_scale),
+                   q, block_tables, context_lens, scale, out, group_starts, prefix_lens,
+                   max_group_size, max_context_len, workspace, partition_tokens, stream)
+
+
+def _prefix(name, cache, q, block_tables, context_lens, scale, out, group_starts, prefix_lens,
+            max_group_size, max_context_len, workspace, partition_tokens, stream):
     import torch
 
     lib = load()
-    cache = _cache(k_cache, v_cache)
     _need(q, "q", torch.bfloat16, 3)
     _need(out, "out", torch.bfloat16, 3)
     _need(block_tables, "block_tables", torch.int32, 2)
@@ -633,13 +653,12 @@ def pkv_decode_attn_prefix(q, k_cache, v_cache, block_tables, context_lens, scal
                                                  int(max_context_len), int(partition_tokens))
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace", torch.uint8, 1)
-    _check(lib.pkv_decode_attn_prefix(q.data_ptr(), cache, block_tables.data_ptr(), max_blocks,
-                                      context_lens.data_ptr(), s, int(max_context_len), hq,
-                                      float(scale), group_starts.data_ptr(),
-                                      prefix_lens.data_ptr(), ng, int(max_group_size),
-                                      out.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                      int(partition_tokens), _stream(q, stream)),
-           "pkv_decode_attn_prefix")
+    _check(getattr(lib, name)(q.data_ptr(), cache, block_tables.data_ptr(), max_blocks,
+                              context_lens.data_ptr(), s, int(max_context_len), hq, float(scale),
+                              group_starts.data_ptr(), prefix_lens.data_ptr(), ng,
+                              int(max_group_size), out.data_ptr(), workspace.data_ptr(),
+                              workspace.numel(), int(partition_tokens), _stream(q, stream)),
+           name)
     return out
 
 

@@ -51,6 +51,9 @@
 // short runs instead aliases with the dispatcher's walk over the shader
 // engines and piles the tiles onto half of them -- measured.  Shorter runs for
 // the workgroups that start late measured slower: 219-250 against 204 us.)
+// Over an FP8 cache (codes + per-(token, KV head) scales) the prefix tiles
+// are the FP8 query tile and the tails the FP8 decode's VALU path, which keeps
+// no LDS ring (this workgroup's LDS holds the list's offsets).
 #include <mutex>
 
 #include "decode_wave.h"
@@ -135,17 +138,18 @@ __device__ __forceinline__ int prefix_segments(int keys) {
 
 }  // namespace
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void cascade_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_cache,
-    const uint16_t *__restrict__ v_cache, const int32_t *__restrict__ block_tables,
+    const uint16_t *__restrict__ v_cache, const float *__restrict__ k_scale,
+    const float *__restrict__ v_scale, const int32_t *__restrict__ block_tables,
     const int32_t *__restrict__ context_lens, int32_t max_blocks_per_seq, int32_t max_context_len,
     int32_t num_blocks, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
     const int32_t *__restrict__ group_starts, const int32_t *__restrict__ prefix_lens,
     int32_t num_groups, int32_t prefix_qblocks, int32_t partition_tokens, int32_t max_parts,
     float scale_log2, float *__restrict__ ws_out, float *__restrict__ ws_ml,
     int32_t *__restrict__ ws_list) {
-    using Geo = PrefillGeom<D, G>;
+    using Geo = PrefillGeom<D, G, 4, FP8>;
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Geo::BUF];
     static_assert(2 * Geo::BUF >= (kMaxPrefixSeqs + 1 + kTailWaves) * (int)sizeof(int32_t),
                   "a tail workgroup's list fits the tile's LDS");
@@ -175,10 +179,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         cross.n = v.end - v.begin;
         cross.keys = v.prefix;
         cross.bt = block_tables + (size_t)v.begin * max_blocks_per_seq;
-        prefill_unit<D, G, true, true>(q, k_cache, v_cache, block_tables, nullptr, nullptr,
-                                       max_blocks_per_seq, max_context_len, num_blocks,
-                                       num_q_heads, num_kv_heads, scale_log2, nullptr, 0, qb, kvh,
-                                       lds, split, cross);
+        prefill_unit<D, G, true, true, 4, FP8>(
+            q, k_cache, v_cache, block_tables, nullptr, nullptr, max_blocks_per_seq,
+            max_context_len, num_blocks, num_q_heads, num_kv_heads, scale_log2, nullptr, 0, qb, kvh,
+            lds, split, cross, k_scale, v_scale);
         return;
     }
 
@@ -259,10 +263,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         const int t_begin = tv.prefix + j0 * kBlockTokens;
         const int t_end = min(tv.prefix + (j0 + take) * kBlockTokens, tv.ctx);
         float acc[G][8], mg[G], lg[G];
-        wave_attend<D, G, false>(q, k_cache, v_cache, nullptr, nullptr,
-                                 block_tables + (size_t)s * max_blocks_per_seq, num_blocks,
-                                 num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
-                                 NewToken{}, Rope{}, acc, mg, lg);
+        wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale,
+                               block_tables + (size_t)s * max_blocks_per_seq, num_blocks,
+                               num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
+                               NewToken{}, Rope{}, acc, mg, lg);
         // the unit's piece: waves before this one that hold blocks of it
         const int ustart = tail_off[s] + kvh * nb;
         const int piece = w - tail_wave_of(ustart, total, nw);
@@ -385,17 +389,18 @@ int32_t compute_units() {
     return cus[dev];
 }
 
-template <int D, int G>
-static hipError_t launch_cascade_t(const CascadeArgs &a, hipStream_t stream) {
-    using Geo = PrefillGeom<D, G>;
+template <int D, int G, bool FP8>
+static hipError_t launch_cascade_f(const CascadeArgs &a, hipStream_t stream) {
+    using Geo = PrefillGeom<D, G, 4, FP8>;
     const int prefix_qblocks = cascade_prefix_qblocks(a.max_group_size, G);
     static_assert(Geo::THREADS == kTailThreads, "tail workgroups are tile-sized");
     const int64_t pf_units = (int64_t)a.num_groups * prefix_qblocks * kMaxSegments * a.num_kv_heads;
     const int64_t tail_units = a.tail_workgroups;
     const float scale_log2 = a.scale * 1.4426950408889634f;
-    hipLaunchKernelGGL((cascade_kernel<D, G>), dim3((unsigned)(pf_units + tail_units)),
+    hipLaunchKernelGGL((cascade_kernel<D, G, FP8>), dim3((unsigned)(pf_units + tail_units)),
                        dim3(Geo::THREADS), 0, stream, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.block_tables,
+                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.k_scale,
+                       a.v_scale, a.block_tables,
                        a.context_lens, a.max_blocks_per_seq, a.max_context_len, a.num_blocks,
                        a.num_seqs, a.num_q_heads, a.num_kv_heads, a.group_starts, a.prefix_lens,
                        a.num_groups, prefix_qblocks, a.partition_tokens, a.max_parts, scale_log2,
@@ -409,6 +414,11 @@ static hipError_t launch_cascade_t(const CascadeArgs &a, hipStream_t stream) {
                        prefix_qblocks * Geo::TWG, a.max_parts, a.ws_out, a.ws_ml, a.ws_list,
                        (uint16_t *)a.out);
     return hipGetLastError();
+}
+
+template <int D, int G>
+static hipError_t launch_cascade_t(const CascadeArgs &a, hipStream_t stream) {
+    return a.fp8 ? launch_cascade_f<D, G, true>(a, stream) : launch_cascade_f<D, G, false>(a, stream);
 }
 
 template <int D>

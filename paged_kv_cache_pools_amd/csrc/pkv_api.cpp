@@ -735,30 +735,13 @@ int32_t common_blocks(const int32_t *a, const int32_t *b, int32_t limit) {
     return i;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                         int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t max_context_len, int32_t partition_tokens) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_context_len < 0 || partition_tokens < 0 || partition_tokens % kBlock != 0)
-        return 0;
-    const int32_t p = partition_tokens
-                          ? partition_tokens
-                          : prefix_partition_for(num_seqs, num_kv_heads, max_context_len);
-    const int32_t parts = prefix_tail_slots(max_context_len, p);
-    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)(parts + pkv::kMaxSegments);
-    return rows * (size_t)(head_dim + 2) * sizeof(float) + prefix_list_bytes(num_seqs);
-}
-
-int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_tables,
-                           int32_t max_blocks_per_seq, const int32_t *context_lens,
-                           int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
-                           float scale, const int32_t *group_starts, const int32_t *prefix_lens,
-                           int32_t num_groups, int32_t max_group_size, void *out, void *workspace,
-                           size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream) {
+// pkv_decode_attn_prefix over either cache: argument checks, the sizing, the launch.
+int prefix_call(const void *q, const CacheDesc &cache, const int32_t *block_tables,
+                int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t num_seqs,
+                int32_t max_context_len, int32_t num_q_heads, float scale,
+                const int32_t *group_starts, const int32_t *prefix_lens, int32_t num_groups,
+                int32_t max_group_size, void *out, void *workspace, size_t workspace_bytes,
+                int32_t partition_tokens, hipStream_t stream, const char *what) {
     int rc = check_cache(cache);
     if (rc) return rc;
     if ((rc = check_heads(num_q_heads, cache.num_kv_heads))) return rc;
@@ -814,6 +797,9 @@ int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_
     a.q = q;
     a.k_cache = cache.k;
     a.v_cache = cache.v;
+    a.k_scale = cache.k_scale;
+    a.v_scale = cache.v_scale;
+    a.fp8 = cache.fp8;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.max_blocks_per_seq = max_blocks_per_seq;
@@ -837,7 +823,51 @@ int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_
     a.ws_out = ws;
     a.ws_ml = ws + rows * cache.head_dim;
     a.ws_list = reinterpret_cast<int32_t *>(a.ws_ml + rows * 2);
-    return hip_status(pkv::launch_cascade(a, stream), "pkv_decode_attn_prefix launch");
+    return hip_status(pkv::launch_cascade(a, stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || partition_tokens < 0 || partition_tokens % kBlock != 0)
+        return 0;
+    const int32_t p = partition_tokens
+                          ? partition_tokens
+                          : prefix_partition_for(num_seqs, num_kv_heads, max_context_len);
+    const int32_t parts = prefix_tail_slots(max_context_len, p);
+    const size_t rows = (size_t)num_seqs * num_q_heads * (size_t)(parts + pkv::kMaxSegments);
+    return rows * (size_t)(head_dim + 2) * sizeof(float) + prefix_list_bytes(num_seqs);
+}
+
+int pkv_decode_attn_prefix(const void *q, pkv_cache cache, const int32_t *block_tables,
+                           int32_t max_blocks_per_seq, const int32_t *context_lens,
+                           int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                           float scale, const int32_t *group_starts, const int32_t *prefix_lens,
+                           int32_t num_groups, int32_t max_group_size, void *out, void *workspace,
+                           size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream) {
+    return prefix_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, group_starts, prefix_lens,
+                       num_groups, max_group_size, out, workspace, workspace_bytes,
+                       partition_tokens, stream, "pkv_decode_attn_prefix launch");
+}
+
+int pkv_decode_attn_prefix_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_tables,
+                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                               int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                               float scale, const int32_t *group_starts,
+                               const int32_t *prefix_lens, int32_t num_groups,
+                               int32_t max_group_size, void *out, void *workspace,
+                               size_t workspace_bytes, int32_t partition_tokens,
+                               hipStream_t stream) {
+    return prefix_call(q, desc_of(cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, max_context_len, num_q_heads, scale, group_starts, prefix_lens,
+                       num_groups, max_group_size, out, workspace, workspace_bytes,
+                       partition_tokens, stream, "pkv_decode_attn_prefix_fp8 launch");
 }
 
 int pkv_prefix_groups(const int32_t *block_tables, int32_t max_blocks_per_seq,

@@ -122,6 +122,8 @@ constexpr size_t mixed_partial_bytes(int32_t head_dim) {
 struct CascadeArgs {
     const void *q;
     const void *k_cache, *v_cache;
+    const float *k_scale = nullptr, *v_scale = nullptr;  // FP8 cache
+    bool fp8 = false;
     const int32_t *block_tables;
     const int32_t *context_lens;
     int32_t max_blocks_per_seq, num_seqs, max_context_len;

@@ -52,7 +52,7 @@
 // Keys at or past the context end are zero in LDS (V) or masked by select (S),
 // so NaN bits in unused slots never reach the output.
 //
-// FP8 cache (the prefill and mixed launches): K and V arrive as OCP E4M3 codes
+// FP8 cache: K and V arrive as OCP E4M3 codes
 // with one fp32 scale per (token, KV head).  Every E4M3 value is exactly a
 // bf16 value, so the codes are converted once per workgroup while staged
 // (global -> registers -> LDS, K like V) and the matrix products run on them
@@ -249,7 +249,6 @@ __device__ __forceinline__ void prefill_unit(
     const float *__restrict__ k_scale = nullptr, const float *__restrict__ v_scale = nullptr) {
     using Geo = PrefillGeom<D, G, NW, FP8>;
     static_assert(!SPLIT || NW == 4, "split units use the 4-wave partial layout");
-    static_assert(!FP8 || !CROSS, "the shared-prefix tiles read bf16 caches only");
     constexpr int TW = Geo::TW, TWG = Geo::TWG, KC = Geo::KC, KSTEPS = Geo::KSTEPS, NT = Geo::NT;
     constexpr int MT = Geo::MT, KROW = Geo::KROW, VROW = Geo::VROW, CPR = Geo::CPR;
     constexpr int KLOADS = Geo::KLOADS, VITEMS = Geo::VITEMS, KITEMS = Geo::KITEMS;

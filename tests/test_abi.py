@@ -261,6 +261,12 @@ def test_fp8_validation(lib):
     assert mx(c=c8(ks=0)) == 1 and mx(c=c8(vs=FAKE + 4)) == 4 and mx(c=c8(d=96)) == 3
     assert mx(nd=4) == 2 and mx(mn=50) == 2 and mx(mc=80) == 2
     assert mx(q=0) == 1
+    px = lambda c=None, s=2, q=FAKE, ws=FAKE: lib.pkv_decode_attn_prefix_fp8(
+        q, c or c8(), FAKE, 3, FAKE, s, 37, 4, ctypes.c_float(0.125), FAKE, FAKE, 1, 2, FAKE, ws,
+        1 << 30, 0, None)
+    assert px(s=0) == 0                     # empty batch: nothing launched
+    assert px(c=c8(ks=0)) == 1 and px(c=c8(vs=FAKE + 4)) == 4 and px(c=c8(d=96)) == 3
+    assert px(q=0) == 1 and px(ws=0) == 5
 
 
 def test_fp8_partition_heuristic(lib):
