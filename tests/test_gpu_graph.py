@@ -1,5 +1,6 @@
-"""The decode step (bf16 and FP8 caches), the FP8 chunked prefill, the mixed
-step and the shared-prefix decode captured in a HIP graph (torch.cuda.graph) and replayed: none of their
+"""The decode step, the mixed step and the shared-prefix decode (over bf16 and
+FP8 caches) and the FP8 chunked prefill captured in a HIP graph
+(torch.cuda.graph) and replayed: none of their
 launches records a memset, so every replay must reproduce the eager result bit
 for bit, with eager work and synchronisations between the replays."""
 import numpy as np
@@ -165,3 +166,46 @@ def test_graph_shared_prefix_decode():
                                  max_context_len=wl.max_context_len, workspace=ws,
                                  partition_tokens=64)
     replay_and_check(step, [out], "shared-prefix decode")
+
+
+def test_graph_fp8_mixed_step_split():
+    """The mixed step over an FP8 cache with a split prefill chunk (mixed +
+    merge launches), the FP8 store of the step's tokens in the same graph."""
+    wl = W.mixed_tail()
+    t = W.make_tensors(wl, device="cuda", nan_fill=True)
+    pools = W.make_fp8_pools(wl, device="cuda", seed=315)
+    mnl, mcl = 64, int(wl.context_lens.max())
+    need = B.pkv_mixed_workspace_bytes(wl.num_seqs, 32, mnl, mcl, wl.num_q_heads, wl.num_kv_heads,
+                                       wl.head_dim)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    say("[gpu] graph: FP8 store + mixed step, 32 decode + one split chunk")
+
+    def step():
+        B.pkv_store_fp8(t["k_new"], t["v_new"], t["slot_mapping"], *pools)
+        B.pkv_mixed_attn_fp8(t["q"], *pools, t["block_tables"], t["cu_new_lens"], t["context_lens"],
+                             32, wl.scale, out, max_new_len=mnl, max_context_len=mcl, workspace=ws)
+    replay_and_check(step, [out], "fp8 mixed step")
+
+
+def test_graph_fp8_shared_prefix_decode():
+    """FP8 store + shared-prefix decode of a grouped batch."""
+    ctx = [320 + x for x in (1, 40, 300, 17, 64, 9, 200)]
+    wl = W.make_decode("graph_prefix8", ctx, 16, 4, 128, 316, prefix_groups=[[0, 1, 2, 3], [4, 5, 6]],
+                       prefix_tokens=320)
+    t = W.make_tensors(wl, device="cuda", nan_fill=True)
+    pools = W.make_fp8_pools(wl, device="cuda", seed=316)
+    starts, plens, mg = B.pkv_prefix_groups(wl.block_tables, wl.context_lens)
+    gs, pl = torch.from_numpy(starts).cuda(), torch.from_numpy(plens).cuda()
+    ws = torch.empty(B.pkv_decode_prefix_workspace_bytes(wl.num_seqs, 16, 4, 128, wl.max_context_len, 64),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t["q"])
+    say(f"[gpu] graph: FP8 store + shared-prefix decode, groups {starts.tolist()}")
+
+    def step():
+        B.pkv_store_fp8(t["k_new"], t["v_new"], t["slot_mapping"], *pools)
+        B.pkv_decode_attn_prefix_fp8(t["q"], *pools, t["block_tables"], t["context_lens"], wl.scale,
+                                     out, gs, pl, mg, max_context_len=wl.max_context_len,
+                                     workspace=ws, partition_tokens=64)
+    replay_and_check(step, [out], "fp8 shared-prefix decode")
