@@ -494,7 +494,10 @@ int pkv_mixed_attn_fp8(const void *q, pkv_cache_fp8 cache, const int32_t *block_
  * pkv_decode_attn_prefix_fp8 -- pkv_decode_attn_prefix over an FP8 cache
  * ([LLM4] §17.6-17.7; [NVE] §2.2): each group's shared prefix read once by the
  * FP8 query tile (MFMA on the codes, scales on the scores and weights), each
- * sequence's tail by the FP8 decode's VALU path.  Arguments, groups,
+ * sequence's tail as pkv_decode_attn_fp8 reads it: on the matrix cores when the
+ * sequence holds more than 128 keys and the batch has at most 379 sequences
+ * (123 at head_dim 64; beyond that every tail takes the fp32 VALU path, same
+ * result up to rounding).  Arguments, groups,
  * workspace (pkv_decode_prefix_workspace_bytes), preconditions and errors as
  * for pkv_decode_attn_prefix, with the cache as for pkv_decode_attn_fp8.
  */

@@ -52,10 +52,13 @@
 // engines and piles the tiles onto half of them -- measured.  Shorter runs for
 // the workgroups that start late measured slower: 219-250 against 204 us.)
 // Over an FP8 cache (codes + per-(token, KV head) scales) the prefix tiles
-// are the FP8 query tile and the tails the FP8 decode's VALU path, which keeps
-// no LDS ring (this workgroup's LDS holds the list's offsets).
+// are the FP8 query tile; a tail wave runs the FP8 decode's matrix-core path,
+// with its LDS ring, when the list's offsets fit in the LDS after the four
+// waves' rings (batches of up to a few hundred sequences) and the sequence
+// holds more than kExactDecodeKeys keys, else the FP8 decode's VALU path.
 #include <mutex>
 
+#include "decode_fp8_mfma.h"
 #include "decode_wave.h"
 #include "prefill_tile.h"
 
@@ -190,8 +193,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     // the sequences before s (each thread counts a run of sequences, then an
     // exclusive scan of the runs' totals).
     const int tw = blockIdx.x - pf_units;  // tail workgroup
-    // [num_seqs + 1] list offsets, then the 4 waves' sums (in the tile's LDS)
-    int32_t *tail_off = reinterpret_cast<int32_t *>(lds);
+    // [num_seqs + 1] list offsets, then the 4 waves' sums (in the tile's LDS).
+    // FP8: at the end of the LDS, so that when the list is short enough the
+    // waves' rings of the matrix-core decode path fit before it
+    constexpr int kLdsBytes = 2 * Geo::BUF;
+    const int list_at = FP8 ? ((kLdsBytes - (num_seqs + 1 + kTailWaves) * 4) & ~15) : 0;
+    int32_t *tail_off = reinterpret_cast<int32_t *>(lds + list_at);
+    const bool rings = FP8 && list_at >= kTailWaves * Fp8Mma<D>::WAVE_BYTES;  // uniform
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int S = num_seqs, H = num_kv_heads;
@@ -252,6 +260,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     constexpr int LPR = D / 8, TPL = 64 / LPR;
     const int row = lane / LPR;
     const int c = lane % LPR;
+    unsigned char *const ring = lds + wave_id_uniform() * Fp8Mma<D>::WAVE_BYTES;
     while (x < r1) {
         while (tail_off[s + 1] <= x) ++s;  // past sequences with no tail
         const int nb = (tail_off[s + 1] - tail_off[s]) / H;
@@ -262,14 +271,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             tail_of(context_lens, group_starts, prefix_lens, num_groups, S, ctx_cap, s);
         const int t_begin = tv.prefix + j0 * kBlockTokens;
         const int t_end = min(tv.prefix + (j0 + take) * kBlockTokens, tv.ctx);
+        // the unit's piece: waves before this one that hold blocks of it
+        const int ustart = tail_off[s] + kvh * nb;
+        const int piece = w - tail_wave_of(ustart, total, nw);
+        if constexpr (FP8) {
+            // a sequence of more than kExactDecodeKeys keys: the FP8 decode's
+            // matrix-core path, as the plain FP8 decode takes it (uniform)
+            if (rings && tv.ctx > kExactDecodeKeys) {
+                f32x4_t o[Fp8Mma<D>::MT];
+                float mr, lr;
+                wave_attend_fp8_mfma<D, G>(q + (size_t)s * num_q_heads * D,
+                                           static_cast<const uint8_t *>(static_cast<const void *>(k_cache)),
+                                           static_cast<const uint8_t *>(static_cast<const void *>(v_cache)),
+                                           k_scale, v_scale, block_tables + (size_t)s * max_blocks_per_seq,
+                                           num_blocks, num_q_heads, num_kv_heads, scale_log2, kvh, t_begin,
+                                           t_end, NewToken{}, ring, o, mr, lr);
+                const int col = lane & 15, grp = lane >> 4;  // head, dimensions 16m + 4grp ..
+                if (col < G) {
+                    const size_t r = ((size_t)s * num_q_heads + kvh * G + col) * slots + piece;
+#pragma unroll
+                    for (int m = 0; m < Fp8Mma<D>::MT; ++m)
+                        *reinterpret_cast<float4 *>(ws_out + r * D + 16 * m + 4 * grp) =
+                            make_float4(o[m][0], o[m][1], o[m][2], o[m][3]);
+                    if (grp == 0) {
+                        ws_ml[r * 2 + 0] = mr;
+                        ws_ml[r * 2 + 1] = lr;
+                    }
+                }
+                x += take;
+                continue;
+            }
+        }
         float acc[G][8], mg[G], lg[G];
         wave_attend<D, G, FP8>(q, k_cache, v_cache, k_scale, v_scale,
                                block_tables + (size_t)s * max_blocks_per_seq, num_blocks,
                                num_q_heads, num_kv_heads, scale_log2, s, kvh, t_begin, t_end,
                                NewToken{}, Rope{}, acc, mg, lg);
-        // the unit's piece: waves before this one that hold blocks of it
-        const int ustart = tail_off[s] + kvh * nb;
-        const int piece = w - tail_wave_of(ustart, total, nw);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (g % TPL == row) {

@@ -102,3 +102,26 @@ def test_prefix_fp8_cont_batch_full_size():
     out = run_prefix_fp8(c, dev, starts, plens, mg)
     ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
     compare(out, ref, "fp8 prefix decode cont_batch", plus_floor=True)
+
+
+@pytest.mark.parametrize("d,nseq", [(64, 130), (128, 400)])
+def test_prefix_fp8_large_batch(d, nseq):
+    """A batch whose list of tail offsets leaves no room in LDS for the
+    matrix-core tails (more than 123 sequences at d 64, 379 at d 128): every
+    tail runs the VALU path.  Groups of 16 share 64 tokens; tails of 1 to 150
+    tokens; a few sequences stand alone."""
+    rng = np.random.default_rng(1400 + d)
+    tails = [int(x) for x in rng.integers(1, 151, size=nseq)]
+    ngroups = (nseq - 4) // 16
+    groups = [list(range(16 * k, 16 * k + 16)) for k in range(ngroups)]
+    ctx = [64 + t if i < 16 * ngroups else t for i, t in enumerate(tails)]
+    wl = W.make_decode(f"prefix8_big_d{d}", ctx, 8, 2, d, 1400 + d, prefix_groups=groups,
+                       prefix_tokens=64, spare_blocks=2)
+    c = Case(wl)
+    say(f"[gpu] fp8 prefix decode, {nseq} sequences, d={d}")
+    host, dev = stored_quantized(c)
+    starts, plens, mg = B.pkv_prefix_groups(wl.block_tables, wl.context_lens)
+    assert len(starts) >= ngroups
+    out = run_prefix_fp8(c, dev, starts, plens, mg)
+    ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
+    compare(out, ref, f"fp8 prefix decode {nseq} seqs d{d}")
