@@ -280,12 +280,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
             if (rings && tv.ctx > kExactDecodeKeys) {
                 f32x4_t o[Fp8Mma<D>::MT];
                 float mr, lr;
-                wave_attend_fp8_mfma<D, G>(q + (size_t)s * num_q_heads * D,
-                                           static_cast<const uint8_t *>(static_cast<const void *>(k_cache)),
-                                           static_cast<const uint8_t *>(static_cast<const void *>(v_cache)),
-                                           k_scale, v_scale, block_tables + (size_t)s * max_blocks_per_seq,
-                                           num_blocks, num_q_heads, num_kv_heads, scale_log2, kvh, t_begin,
-                                           t_end, NewToken{}, ring, o, mr, lr);
+                wave_attend_fp8_mfma<D, G>(
+                    q + (size_t)s * num_q_heads * D, reinterpret_cast<const uint8_t *>(k_cache),
+                    reinterpret_cast<const uint8_t *>(v_cache), k_scale, v_scale,
+                    block_tables + (size_t)s * max_blocks_per_seq, num_blocks, num_q_heads,
+                    num_kv_heads, scale_log2, kvh, t_begin, t_end, NewToken{}, ring, o, mr, lr);
                 const int col = lane & 15, grp = lane >> 4;  // head, dimensions 16m + 4grp ..
                 if (col < G) {
                     const size_t r = ((size_t)s * num_q_heads + kvh * G + col) * slots + piece;
