@@ -205,9 +205,11 @@ __global__ __launch_bounds__(512) void decode_fused_kernel(
     extern __shared__ float smem[];
     int kvh = blockIdx.x;
     int s = blockIdx.y;
-    if constexpr (FP8)
-        pair_kv_heads(blockIdx.y * num_kv_heads + blockIdx.x, num_kv_heads * (int)gridDim.y,
-                      num_kv_heads, s, kvh);
+    // KV heads 2k and 2k + 1 of a sequence back to back on one XCD: FP8 scale
+    // rows of the two share 128-byte lines; bf16 or FP8, their tiles of a block
+    // are adjacent in the pool (measured 0.3-0.6% faster for bf16 too)
+    pair_kv_heads(blockIdx.y * num_kv_heads + blockIdx.x, num_kv_heads * (int)gridDim.y,
+                  num_kv_heads, s, kvh);
     const int ctx = clamp_context(context_lens[s], max_context_len, max_blocks_per_seq,
                                   kvh == 0 && threadIdx.x == 0, s);
     const int32_t *bt_row = block_tables + (size_t)s * max_blocks_per_seq;
