@@ -147,3 +147,34 @@ def test_mixed_fp8_step_full_size():
     host, dev = random_code_pools(wl)
     out = run_mixed_fp8(c, dev, nd)
     compare(out, oracle(c, host), "fp8 mixed full size", plus_floor=True)
+
+
+@pytest.mark.parametrize("which", ["all_decode", "all_prefill"])
+def test_mixed_fp8_one_kind_only(which):
+    """Every sequence one kind: all decode (one past 128 keys, so both decode
+    paths run) or all prefill."""
+    if which == "all_decode":
+        wl = W.make_prefill("mixed8_all_decode", [3, 64, 500], [1, 1, 1], 16, 4, 128, 1720)
+        nd = 3
+    else:
+        wl = W.make_prefill("mixed8_all_prefill", [0, 31, 200], [9, 33, 64], 16, 4, 64, 1721)
+        nd = 0
+    c = Case(wl)
+    say(f"[gpu] fp8 mixed step, {which}")
+    host, dev = quantized_pools_after_store(c)
+    out = run_mixed_fp8(c, dev, nd)
+    compare(out, oracle(c, host), f"fp8 mixed {which}")
+
+
+def test_mixed_fp8_decode_range_irregular():
+    """In the decode range a sequence with 3 new tokens is still computed in
+    full and one with none writes nothing; a prefill chunk of one token is
+    computed as prefill."""
+    cached = [40, 20, 33, 0, 7]
+    new = [1, 3, 0, 1, 1]
+    wl = W.make_prefill("mixed8_irregular", cached + [50, 12], new + [1, 70], 8, 2, 128, 1710)
+    c = Case(wl)
+    say("[gpu] fp8 mixed step, irregular decode range")
+    host, dev = quantized_pools_after_store(c)
+    out = run_mixed_fp8(c, dev, len(cached))
+    compare(out, oracle(c, host), "fp8 mixed irregular")
