@@ -125,3 +125,60 @@ def test_prefix_fp8_large_batch(d, nseq):
     out = run_prefix_fp8(c, dev, starts, plens, mg)
     ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
     compare(out, ref, f"fp8 prefix decode {nseq} seqs d{d}")
+
+
+def test_prefix_fp8_whole_context_and_no_groups():
+    """A member whose context is exactly the prefix (no tail), and the same
+    batch with no groups at all (every sequence split-KV only)."""
+    wl, starts = grouped_case(128, 4, 1360)
+    wl.context_lens[3] = 320  # member 3 of group 0 keeps only the shared tokens
+    wl.slot_mapping[3] = -1   # and stores nothing
+    c = Case(wl)
+    say("[gpu] fp8 prefix decode: a member with no tail; then without groups")
+    host, dev = stored_quantized(c)
+    out = run_prefix_fp8(c, dev, starts, [320, 320, 320], 36)
+    plain = run_prefix_fp8(c, dev, [0], [], 0)
+    ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
+    compare(out, ref, "fp8 prefix decode, empty tail")
+    compare(plain, ref, "fp8 prefix decode, no groups")
+
+
+def test_prefix_fp8_workspace_reuse_deterministic():
+    wl, starts = grouped_case(128, 8, 1370)
+    c = Case(wl)
+    host, dev = stored_quantized(c)
+    need = B.pkv_decode_prefix_workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads,
+                                               wl.head_dim, int(wl.context_lens.max()), 32)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    say(f"[gpu] fp8 prefix decode twice on one workspace of {need} B")
+    d = c.dev
+
+    def call():
+        out = torch.full_like(d["q"], float("nan"))
+        B.pkv_decode_attn_prefix_fp8(d["q"], *dev, d["block_tables"], d["context_lens"], wl.scale,
+                                     out, torch.tensor(starts, dtype=torch.int32, device="cuda"),
+                                     torch.tensor([320, 320, 320], dtype=torch.int32, device="cuda"),
+                                     36, max_context_len=int(wl.context_lens.max()), workspace=ws,
+                                     partition_tokens=32)
+        torch.cuda.synchronize()
+        return out
+    a, b = call(), call()
+    assert np.array_equal(a.cpu().view(torch.int16).numpy(), b.cpu().view(torch.int16).numpy())
+
+
+def test_prefix_fp8_precondition_rows_are_nan():
+    """A declared prefix longer than a member's context, and a group larger
+    than max_group_size, give NaN for exactly the rows concerned."""
+    wl, starts = grouped_case(128, 4, 1380)
+    c = Case(wl)
+    say("[gpu] fp8 prefix decode with broken preconditions (NaN rows expected)")
+    host, dev = stored_quantized(c)
+    # group 2's members have contexts 384 and 323: a 336-token prefix exceeds the second
+    out = run_prefix_fp8(c, dev, starts, [320, 320, 336], 32, partition_tokens=64)
+    ref = orc().decode_fp8(c.h["q"], *host, wl.block_tables, wl.context_lens, wl.scale)
+    got = out.float().cpu().numpy()
+    assert np.all(np.isnan(got[42])), "prefix beyond the context must give NaN"
+    # max_group_size 32 with G = 4 covers 32 members of group 1 (5 .. 36)
+    assert np.all(np.isnan(got[37:41])), "members past max_group_size must give NaN"
+    valid = [s for s in range(wl.num_seqs) if not (37 <= s <= 40 or s == 42)]
+    compare(out[valid], ref[valid], "fp8 prefix decode, valid rows")
