@@ -123,3 +123,70 @@ def test_copy_pair_outside_the_pool(dbg):
     B.pkv_copy_blocks([pool], copies)
     assert B.pkv_debug_status()[:3] == (COPY, 99, 1)
     assert int(pool[5].min()) == 7 and int(pool[2].max()) == 0
+
+
+@pytest.mark.parametrize("part", [0, 32])
+def test_fp8_block_id_out_of_range(dbg, part):
+    """FP8 decode: an out-of-range id met by the matrix-core path (a sequence
+    past 128 keys), single pass and split-KV."""
+    wl = W.make_decode("dbg_bid8", [40, 300, 20], 8, 2, 128, 1206, store=False)
+    c = Case(wl, nan_fill=False)
+    pools = W.make_fp8_pools(wl, device="cuda", seed=1206)
+    bt = wl.block_tables.copy()
+    bt[1, 3] = wl.num_blocks + 5
+    d = c.dev
+    out = torch.empty_like(d["q"])
+    say(f"[gpu] debug build: FP8 decode, block id {bt[1, 3]} in a pool of {wl.num_blocks}, P={part}")
+    B.pkv_decode_attn_fp8(d["q"], *pools, torch.from_numpy(bt).cuda(), d["context_lens"], wl.scale,
+                          out, max_context_len=wl.max_context_len, partition_tokens=part)
+    kind, value, where, _ = B.pkv_debug_status()
+    assert (kind, value, where) == (BLOCK_ID, wl.num_blocks + 5, 3)
+
+
+def test_fp8_negative_block_id_in_prefill(dbg):
+    wl = W.make_prefill("dbg_pf8", [30, 0], [40, 20], 8, 2, 128, 1207, spare_blocks=1)
+    c = Case(wl, nan_fill=False)
+    pools = W.make_fp8_pools(wl, device="cuda", seed=1207)
+    bt = wl.block_tables.copy()
+    bt[0, 2] = -7
+    d = c.dev
+    out = torch.empty_like(d["q"])
+    say("[gpu] debug build: block id -7 in FP8 chunked prefill")
+    B.pkv_prefill_attn_fp8(d["q"], *pools, torch.from_numpy(bt).cuda(), d["cu_new_lens"],
+                           d["context_lens"], wl.scale, out, max_new_len=wl.max_new_len,
+                           max_context_len=wl.max_context_len)
+    kind, value, where, _ = B.pkv_debug_status()
+    assert (kind, value, where) == (BLOCK_ID, -7, 2)
+
+
+def test_fp8_slot_past_the_pool(dbg):
+    wl = W.make_decode("dbg_slot8", [20, 33, 7], 4, 2, 64, 1208, spare_blocks=1)
+    c = Case(wl)
+    pools = W.make_fp8_pools(wl, device="cuda", seed=1208)
+    slots = wl.slot_mapping.copy()
+    slots[2] = wl.num_blocks * 16 + 3
+    d = c.dev
+    say("[gpu] debug build: a slot past the pool in the FP8 store")
+    B.pkv_store_fp8(d["k_new"], d["v_new"], torch.from_numpy(slots).cuda(), *pools)
+    assert B.pkv_debug_status()[:3] == (SLOT, wl.num_blocks * 16 + 3, 2)
+
+
+def test_fp8_prefix_tail_block_id(dbg):
+    """FP8 shared-prefix decode: an out-of-range id in a grouped sequence's
+    tail, met by a tail wave on the matrix-core path."""
+    ctx = [320 + t for t in (200, 150, 40)]
+    wl = W.make_decode("dbg_px8", ctx, 8, 2, 128, 1209, prefix_groups=[[0, 1, 2]],
+                       prefix_tokens=320, store=False)
+    c = Case(wl, nan_fill=False)
+    pools = W.make_fp8_pools(wl, device="cuda", seed=1209)
+    bt = wl.block_tables.copy()
+    bt[1, 22] = wl.num_blocks + 9          # block 22: tokens 352..367, in sequence 1's tail
+    d = c.dev
+    out = torch.empty_like(d["q"])
+    say("[gpu] debug build: FP8 shared-prefix decode, a tail block id past the pool")
+    B.pkv_decode_attn_prefix_fp8(d["q"], *pools, torch.from_numpy(bt).cuda(), d["context_lens"],
+                                 wl.scale, out, torch.tensor([0, 3], dtype=torch.int32, device="cuda"),
+                                 torch.tensor([320], dtype=torch.int32, device="cuda"), 3,
+                                 max_context_len=wl.max_context_len)
+    kind, value, where, _ = B.pkv_debug_status()
+    assert (kind, value, where) == (BLOCK_ID, wl.num_blocks + 9, 22)
