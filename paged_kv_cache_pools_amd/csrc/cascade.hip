@@ -45,9 +45,12 @@
 //
 // Dispatch order: all prefix tiles first, then the tail workgroups, two per
 // compute unit (as many as can be resident).  The dispatcher hands an XCD's
-// workgroups to its compute units breadth first, so as long as there are at
-// most 256 tiles no compute unit runs two of them, and the tail workgroups
-// that find no slot start as the tiles finish.  (Alternating the kinds in
+// workgroups to its compute units breadth first, so as long as at most 256
+// tiles have keys to read (they lead the grid) no compute unit runs two of
+// them, and the tail workgroups that find no slot start as the tiles finish.
+// (With the key segment innermost instead, a 2048-token prefix's four live
+// segments of eight put two busy tiles on half the compute units and none on
+// the others -- a per-wave timeline showed it.)  (Alternating the kinds in
 // short runs instead aliases with the dispatcher's walk over the shader
 // engines and piles the tiles onto half of them -- measured.  Shorter runs for
 // the workgroups that start late measured slower: 219-250 against 204 us.)
@@ -161,21 +164,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
     const int pf_units = num_groups * prefix_qblocks * kMaxSegments * num_kv_heads;
 
     if ((int)blockIdx.x < pf_units) {
-        // a prefix tile: idx = ((g * prefix_qblocks + qb) * kMaxSegments + seg) * H_kv + kvh
+        // a prefix tile: idx = ((seg * num_groups + g) * prefix_qblocks + qb) * H_kv + kvh.
+        // The key segment is outermost: a prefix has fewer segments than
+        // kMaxSegments unless it is long, and the tiles past its last return at
+        // once, so the tiles with keys to read come first in the grid and the
+        // dispatcher spreads them over distinct compute units.
         int idx = blockIdx.x;
         const int kvh = idx % num_kv_heads;
         idx /= num_kv_heads;
+        const int qb = idx % prefix_qblocks;
+        idx /= prefix_qblocks;
+        const int g = idx % num_groups;
         SplitSlot split;
-        split.seg = idx % kMaxSegments;
+        split.seg = idx / num_groups;
         split.slots = kMaxSegments;
         split.min_chunks = kPrefixSegmentChunks;
         split.ws_out = ws_out;
         split.ws_ml = ws_ml;
         split.ws_slots = slots;
         split.slot0 = max_parts;
-        idx /= kMaxSegments;
-        const int qb = idx % prefix_qblocks;
-        const int g = idx / prefix_qblocks;
         const GroupView v = group_view(group_starts, prefix_lens, g, num_seqs, ctx_cap);
         CrossGeom cross;
         cross.row0 = v.begin;
@@ -267,8 +274,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void c
         const int rel = x - tail_off[s];
         const int kvh = rel / nb, j0 = rel - kvh * nb;
         const int take = min(nb - j0, r1 - x);
-        const TailView tv =
-            tail_of(context_lens, group_starts, prefix_lens, num_groups, S, ctx_cap, s);
+        // the tail is the last nb blocks of the context: one load, no group lookup
+        TailView tv;
+        tv.ctx = min(context_lens[s], ctx_cap);
+        tv.blocks = nb;
+        tv.prefix = ((tv.ctx + kBlockTokens - 1) / kBlockTokens - nb) * kBlockTokens;
         const int t_begin = tv.prefix + j0 * kBlockTokens;
         const int t_end = min(tv.prefix + (j0 + take) * kBlockTokens, tv.ctx);
         // the unit's piece: waves before this one that hold blocks of it
