@@ -782,12 +782,18 @@ int prefix_call(const void *q, const CacheDesc &cache, const int32_t *block_tabl
     if (!workspace || workspace_bytes < need)
         return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
-    // the grid: tail workgroups (two per compute unit, as many as can be
-    // resident: 4 tail waves per compute unit stream the list 13% slower on
-    // 256 sequences in 8 shared-prefix groups) plus prefix tiles (a tile holds
-    // at least 16 sequences, group size 8); 256 threads per workgroup
+    // the grid: tail workgroups plus prefix tiles (a tile holds at least 16
+    // sequences, group size 8); 256 threads per workgroup.  Over an FP8 cache
+    // two tail workgroups per compute unit, as many as can be resident (4 tail
+    // waves per compute unit stream the list 13% slower on 256 sequences in 8
+    // shared-prefix groups; 4 or 6 workgroups with shorter runs, 5-6% slower).
+    // Over a bf16 cache six, so that three rounds of shorter runs pass through
+    // each compute unit: equal runs do not take equal times (compute units
+    // finished them between 100 and 170 us in a per-wave timeline), and the
+    // dispatcher hands the later rounds to the compute units that finish
+    // first (2% faster on the same batch).
     const int64_t qblocks = ((int64_t)max_group_size + 15) / 16;
-    const int32_t tail_wgs = 2 * pkv::compute_units();
+    const int32_t tail_wgs = (cache.fp8 ? 2 : 6) * pkv::compute_units();
     const int64_t wgs = tail_wgs +
                         (int64_t)num_groups * qblocks * pkv::kMaxSegments * cache.num_kv_heads;
     if (wgs >= (int64_t)1 << 24 || (int64_t)num_seqs * num_q_heads >= (int64_t)1 << 26)

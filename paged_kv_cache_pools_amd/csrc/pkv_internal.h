@@ -132,7 +132,7 @@ struct CascadeArgs {
     const int32_t *prefix_lens;   // device [num_groups]
     int32_t num_groups, max_group_size;
     int32_t partition_tokens, max_parts;  // max_parts: tail slots per row
-    int32_t tail_workgroups;              // one per compute unit
+    int32_t tail_workgroups;              // 2 (FP8) or 6 (bf16) per compute unit
     float scale;
     void *out;
     float *ws_out;     // [num_seqs][num_q_heads][max_parts + kMaxSegments][head_dim]
