@@ -50,7 +50,7 @@
 // them, and the tail workgroups that find no slot start as the tiles finish.
 // (With the key segment innermost instead, a 2048-token prefix's four live
 // segments of eight put two busy tiles on half the compute units and none on
-// the others -- a per-wave timeline showed it.)  (Alternating the kinds in
+// the others; the step was 1-3% slower.)  (Alternating the kinds in
 // short runs instead aliases with the dispatcher's walk over the shader
 // engines and piles the tiles onto half of them -- measured.  Shorter runs for
 // the workgroups that start late measured slower: 219-250 against 204 us.)
