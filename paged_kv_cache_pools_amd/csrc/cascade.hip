@@ -43,8 +43,9 @@
 // up to kMaxSegments ranges of at least 512 keys).  After the rows: the list's
 // wave count NW, then the offsets, for the merge.
 //
-// Dispatch order: all prefix tiles first, then the tail workgroups, two per
-// compute unit (as many as can be resident).  The dispatcher hands an XCD's
+// Dispatch order: all prefix tiles first, then the tail workgroups (the host
+// sizes their number: two per compute unit, as many as can be resident, or
+// several rounds of shorter runs).  The dispatcher hands an XCD's
 // workgroups to its compute units breadth first, so as long as at most 256
 // tiles have keys to read (they lead the grid) no compute unit runs two of
 // them, and the tail workgroups that find no slot start as the tiles finish.
